@@ -1,0 +1,210 @@
+/*
+ * pka.h -- paged KV attention for one batch on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpka.so.  An attention backend, as the pages define it, builds
+ * per-batch metadata (page tables and index buffers), and runs forward_extend
+ * for prefill and forward_decode for decode over the paged KV cache of one
+ * batch ("sglang-101 s4.2 --attention-backend", section "What an attention
+ * backend is").  This library exposes those steps as plain C calls:
+ *
+ *   pka_init_metadata  seq_lens + page table -> kv_indptr / kv_indices / ...
+ *   pka_save_kv        scatter new K/V rows into the page pool
+ *   pka_attn_decode    one query token per request (split-K flash decoding)
+ *   pka_attn_extend    a causal block of new tokens against prefix + itself
+ *   pka_forward        ForwardMode-keyed dispatch between the two paths
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All device buffers are owned by the caller and passed as plain device
+ *   pointers; the library never allocates, frees or synchronises on these
+ *   paths.  Work is enqueued on the caller's HIP stream (a hipStream_t passed
+ *   as void*; NULL is the default stream).
+ * - Layouts are row-major and contiguous:
+ *     q, out            [num_q_tokens, num_q_heads, head_dim]   (q dtype)
+ *     k_new, v_new      [num_q_tokens, num_kv_heads, head_dim]  (q dtype)
+ *     k_pool, v_pool    [num_pages * page_size, num_kv_heads, head_dim]
+ *                       (kv dtype; separate K and V pools, token-major)
+ *     lse               [num_q_tokens, num_q_heads] fp32, natural log
+ *   Page p holds slots p*page_size .. p*page_size + page_size - 1.  Query
+ *   head h reads KV head h / (num_q_heads / num_kv_heads).
+ * - seq_lens[b] (L_b) counts every token request b attends to, including its
+ *   new tokens; the new tokens sit at positions L_b - n_b .. L_b - 1 and new
+ *   token i attends to positions 0 .. L_b - n_b + i (bottom-right causal).
+ *   Decode has n_b = 1 for every request.
+ * - Every call validates its host-visible arguments first and returns a
+ *   pka_status; on any error nothing is launched, and pka_last_error()
+ *   returns a description (thread-local).  No C++ exception crosses the ABI.
+ *   Device-side data (lengths, page ids) is checked by the kernels: out of
+ *   range values are clamped so no access leaves its buffer, and a sticky
+ *   flag is set that pka_read_status reports.
+ */
+#ifndef PKA_H
+#define PKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Forward modes of a batch, after the pages' ForwardMode ("[SGLang] Hybrid
+ * Attention", section on _select_backend: decode_or_idle, target_verify,
+ * draft_extend, and prefill/extend). */
+typedef enum {
+    PKA_MODE_EXTEND = 0,
+    PKA_MODE_DECODE = 1,
+    PKA_MODE_IDLE = 2,
+    PKA_MODE_TARGET_VERIFY = 3,
+    PKA_MODE_DRAFT_EXTEND = 4
+} pka_forward_mode;
+
+/* Which path runs the speculative verify pass; the pages give "prefill" as
+ * the default ("sglang-101 s4.2", section "Two backends in one server"). */
+typedef enum { PKA_SPEC_PREFILL = 0, PKA_SPEC_DECODE = 1 } pka_spec_attn_mode;
+
+typedef enum { PKA_F32 = 0, PKA_BF16 = 1, PKA_FP8_E4M3FN = 2 } pka_dtype;
+
+typedef enum {
+    PKA_OK = 0,
+    PKA_ERR_INVALID_ARG = -1,
+    PKA_ERR_UNSUPPORTED = -2,
+    PKA_ERR_WORKSPACE = -3,
+    PKA_ERR_HIP = -4
+} pka_status;
+
+typedef enum { PKA_PATH_NONE = 0, PKA_PATH_DECODE = 1, PKA_PATH_EXTEND = 2 } pka_path;
+
+/* Per-layer attention parameters (the analogue of one attention layer's
+ * handle).  Supported:
+ *   head_dim in {64, 128}; page_size in {1, 2, 4, ..., 256} (a power of two);
+ *   num_q_heads a positive multiple of num_kv_heads;
+ *   (q, kv) dtypes: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN);
+ *   extend runs for (BF16, BF16) and (F32, F32).
+ * scale multiplies q.k; k_scale / v_scale are the per-tensor fp8 scales (the
+ * cached code c stands for c * scale); they must be 1 for non-fp8 caches. */
+typedef struct {
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t num_pages; /* pool capacity in pages */
+    pka_dtype q_dtype;
+    pka_dtype kv_dtype;
+    float scale;
+    float k_scale;
+    float v_scale;
+} pka_config;
+
+typedef struct pka_ctx pka_ctx;
+
+/* Caller-owned device int32 arrays describing one batch, sized by
+ * pka_batch_sizes.  pka_init_metadata fills them; the attention calls read
+ * them.  mode records which kind of batch they were built for. */
+typedef struct {
+    pka_forward_mode mode;
+    int32_t batch;            /* B */
+    int32_t num_q_tokens;     /* N = sum of n_b (decode: B) */
+    int64_t max_kv_pages;     /* capacity of kv_indices */
+    int32_t* kv_indptr;       /* [B+1]  page offsets per request */
+    int32_t* kv_indices;      /* [max_kv_pages] page ids, request-major */
+    int32_t* kv_last_page_len;/* [B]    tokens in each request's last page */
+    int32_t* qo_indptr;       /* [B+1]  query-token offsets per request */
+    int32_t* out_cache_loc;   /* [N]    pool slot of each new token */
+    int32_t* plan;            /* [plan elems] work partition + status word */
+} pka_batch;
+
+/* Element counts of the pka_batch arrays and workspace bytes for a batch. */
+typedef struct {
+    int64_t kv_indptr;
+    int64_t kv_indices;
+    int64_t kv_last_page_len;
+    int64_t qo_indptr;
+    int64_t out_cache_loc;
+    int64_t plan;
+    int64_t workspace_bytes;
+} pka_sizes;
+
+/* Validate a configuration and create a host-only context (no device memory,
+ * no device calls).  Refuses unsupported combinations with
+ * PKA_ERR_UNSUPPORTED, after the pages' rule that a backend refuses to start
+ * on what it cannot run ("sglang-101 s4.2", section "The obvious fix, and why
+ * it fails").  *out must be released with pka_destroy. */
+pka_status pka_create(const pka_config* cfg, pka_ctx** out);
+void pka_destroy(pka_ctx* ctx);
+
+/* Sizes for a batch of `batch` requests, `num_q_tokens` new tokens and at
+ * most `max_kv_pages` pages in total (sum of ceil(L_b / page_size)). */
+pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t batch,
+                           int32_t num_q_tokens, int64_t max_kv_pages, pka_sizes* out);
+
+/* Build the per-batch index buffers on the device ("What an attention backend
+ * is": per-batch metadata such as page tables and index buffers):
+ *   kv_indptr[b+1] = kv_indptr[b] + ceil(L_b / P); kv_indices = the first
+ *   ceil(L_b / P) ids of page-table row b; kv_last_page_len[b] =
+ *   L_b - (ceil(L_b/P) - 1) * P; qo_indptr = prefix sum of n_b;
+ *   out_cache_loc = slot (page * P + offset) of each new token;
+ *   plan = the work partition for the attention kernels.
+ * seq_lens [B] and extend_lens [B] (n_b; NULL for decode) are device int32;
+ * page_table is device int32 [B, page_table_stride] whose first
+ * page_table_cols entries per row may be read.  md->mode, batch,
+ * num_q_tokens, max_kv_pages and the array pointers must be set by the
+ * caller.  One kernel launch. */
+pka_status pka_init_metadata(const pka_ctx* ctx, const int32_t* seq_lens,
+                             const int32_t* extend_lens, const int32_t* page_table,
+                             int32_t page_table_stride, int32_t page_table_cols, pka_batch* md,
+                             void* stream);
+
+/* Write the new tokens' K and V rows into the pools at out_cache_loc (the
+ * backend's save_kv_cache=True step, "[SGLang] Hybrid Attention", forward
+ * delegation).  Same dtype: copy.  bf16 -> fp8 e4m3fn: y = x * fp32(1/scale),
+ * saturated at +-448 and rounded to nearest even. */
+pka_status pka_save_kv(const pka_ctx* ctx, const pka_batch* md, const void* k_new,
+                       const void* v_new, void* k_pool, void* v_pool, void* stream);
+
+/* forward_decode: one query per request against its whole cache, split-K
+ * flash decoding (split partials + log-sum-exp merge).  workspace: device
+ * bytes >= pka_sizes.workspace_bytes.  lse may be NULL. */
+pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* q,
+                           const void* k_pool, const void* v_pool, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* forward_extend: each new token attends causally to its request's prefix and
+ * to the new tokens up to itself.  Same buffers as decode. */
+pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* q,
+                           const void* k_pool, const void* v_pool, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* The pages' backend selection by ForwardMode ("[SGLang] Hybrid Attention",
+ * section on _select_backend): decode/idle -> decode; target_verify and
+ * draft_extend -> decode if the speculative attention mode is decode, else
+ * prefill; everything else -> prefill (extend).  IDLE maps to PKA_PATH_NONE
+ * (nothing to compute).  Pure host function. */
+pka_path pka_select_path(pka_forward_mode mode, pka_spec_attn_mode spec_mode);
+
+/* One attention layer's forward: optional save_kv, then the path chosen by
+ * pka_select_path.  The decode path takes one query per request, so a verify
+ * batch routed to it must have num_q_tokens == batch (else UNSUPPORTED). */
+pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
+                       const pka_batch* md, const void* q, const void* k_new, const void* v_new,
+                       int save_kv, void* k_pool, void* v_pool, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronise `stream` and read the sticky device status word of a batch:
+ * 0 = clean, else a bitwise OR of PKA_DEV_* flags. */
+pka_status pka_read_status(const pka_batch* md, int32_t* status, void* stream);
+#define PKA_DEV_BAD_LENGTH 1    /* L_b < 1, n_b < 0 or n_b > L_b (clamped) */
+#define PKA_DEV_BAD_PAGE 2      /* page id outside [0, num_pages) (clamped) */
+#define PKA_DEV_TABLE_SHORT 4   /* ceil(L_b/P) > page_table_cols (clamped) */
+#define PKA_DEV_CAPACITY 8      /* pages or tokens beyond the batch capacities */
+
+const char* pka_status_string(pka_status s);
+const char* pka_last_error(void);
+
+/* Build identification, e.g. "pka 0.1 gfx950". */
+const char* pka_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKA_H */

@@ -1,0 +1,377 @@
+// C ABI of libpka: validation, the ForwardMode dispatch and kernel launches.
+//
+// Every entry point checks what the host can see before anything is
+// enqueued and returns a pka_status; on error nothing is launched, after the
+// pages' rule that a backend refuses to start on what it cannot run
+// ("sglang-101 s4.2 --attention-backend", section "The obvious fix, and why it
+// fails").  The library holds no device memory: buffers come from the caller.
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "pka_internal.h"
+
+struct pka_ctx {
+    pka_config cfg;
+    int32_t G;
+    int32_t qgroups;     // ceil(G / 16): decode waves per KV head
+    int32_t page_shift;
+    int32_t wpb;         // decode waves per workgroup
+    int32_t ext_tq;      // extend query tokens per work item
+    std::atomic<int32_t> nwg{0};  // decode workgroups (from the device's CU count)
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pka_status fail(pka_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+pka_status fail(pka_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+pka_status hip_fail(hipError_t e, const char* what) {
+    return fail(PKA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_bytes(pka_dtype t) { return t == PKA_F32 ? 4 : t == PKA_BF16 ? 2 : 1; }
+
+// Decode workgroups: a few per compute unit (waves per CU ~ 16), capped by
+// the plan's capacity.  Queried once per context on first use.
+pka_status decode_wgs(const pka_ctx* ctx, int32_t* out) {
+    int32_t v = ctx->nwg.load(std::memory_order_relaxed);
+    if (v <= 0) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "querying the device");
+        const int per_cu = std::max(1, 16 / ctx->wpb);
+        v = std::min<int32_t>(pka::DEC_MAX_WG, std::max(1, cus * per_cu));
+        const_cast<pka_ctx*>(ctx)->nwg.store(v, std::memory_order_relaxed);
+    }
+    *out = v;
+    return PKA_OK;
+}
+
+int64_t decode_ws_bytes(const pka_ctx* ctx, int32_t B, int32_t nwg) {
+    return ((int64_t)B + nwg) * ctx->cfg.num_q_heads * (ctx->cfg.head_dim + 1) * 4;
+}
+
+bool is_extend_like(pka_forward_mode m) {
+    return m == PKA_MODE_EXTEND || m == PKA_MODE_TARGET_VERIFY || m == PKA_MODE_DRAFT_EXTEND;
+}
+
+pka_status check_batch(const pka_ctx* ctx, const pka_batch* md) {
+    if (!ctx || !md) return fail(PKA_ERR_INVALID_ARG, "null context or batch");
+    if (md->batch < 0 || md->num_q_tokens < 0 || md->max_kv_pages < 0)
+        return fail(PKA_ERR_INVALID_ARG, "negative batch sizes");
+    if (md->mode < PKA_MODE_EXTEND || md->mode > PKA_MODE_DRAFT_EXTEND)
+        return fail(PKA_ERR_INVALID_ARG, "unknown forward mode %d", (int)md->mode);
+    if (md->mode == PKA_MODE_DECODE && md->num_q_tokens != md->batch)
+        return fail(PKA_ERR_INVALID_ARG, "decode batch needs num_q_tokens == batch (%d vs %d)",
+                    md->num_q_tokens, md->batch);
+    if (md->batch > 0 && (!md->kv_indptr || !md->kv_indices || !md->kv_last_page_len ||
+                          !md->qo_indptr || !md->plan))
+        return fail(PKA_ERR_INVALID_ARG, "null metadata array");
+    if (md->batch > 0 && md->max_kv_pages < 1)
+        return fail(PKA_ERR_INVALID_ARG, "max_kv_pages must be positive");
+    if (md->num_q_tokens > 0 && !md->out_cache_loc)
+        return fail(PKA_ERR_INVALID_ARG, "null out_cache_loc");
+    return PKA_OK;
+}
+
+pka::AttnArgs attn_args(const pka_ctx* ctx, const pka_batch* md, const void* q, const void* kp,
+                        const void* vp, void* out, float* lse) {
+    pka::AttnArgs a{};
+    const pka_config& c = ctx->cfg;
+    a.q = q;
+    a.k_pool = kp;
+    a.v_pool = vp;
+    a.out = out;
+    a.lse = lse;
+    a.kv_indptr = md->kv_indptr;
+    a.kv_indices = md->kv_indices;
+    a.kv_last_page_len = md->kv_last_page_len;
+    a.qo_indptr = md->qo_indptr;
+    a.plan = md->plan;
+    a.kv_cap = md->max_kv_pages;
+    a.B = md->batch;
+    a.N = md->num_q_tokens;
+    a.Hq = c.num_q_heads;
+    a.Hkv = c.num_kv_heads;
+    a.G = ctx->G;
+    a.qgroups = ctx->qgroups;
+    a.page_shift = ctx->page_shift;
+    a.num_pages = c.num_pages;
+    const float k_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f;
+    a.scale_log2 = c.scale * 1.4426950408889634f * k_scale;
+    a.v_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f;
+    return a;
+}
+
+pka_status check_attn(const pka_ctx* ctx, const pka_batch* md, const void* q, const void* kp,
+                      const void* vp, void* out) {
+    pka_status s = check_batch(ctx, md);
+    if (s != PKA_OK) return s;
+    if (md->num_q_tokens > 0 && (!q || !kp || !vp || !out))
+        return fail(PKA_ERR_INVALID_ARG, "null q, pool or output pointer");
+    if (!aligned16(q) || !aligned16(kp) || !aligned16(vp) || !aligned16(out))
+        return fail(PKA_ERR_INVALID_ARG, "q, pools and output must be 16-byte aligned");
+    return PKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pka_status_string(pka_status s) {
+    switch (s) {
+    case PKA_OK: return "ok";
+    case PKA_ERR_INVALID_ARG: return "invalid argument";
+    case PKA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKA_ERR_WORKSPACE: return "workspace too small";
+    case PKA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* pka_last_error(void) { return g_last_error.c_str(); }
+
+const char* pka_version(void) { return "pka 0.1 gfx950"; }
+
+pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
+    if (!cfg || !out) return fail(PKA_ERR_INVALID_ARG, "null config or output handle");
+    *out = nullptr;
+    const pka_config& c = *cfg;
+    if (c.num_q_heads < 1 || c.num_kv_heads < 1 || c.num_q_heads % c.num_kv_heads != 0)
+        return fail(PKA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    c.num_q_heads, c.num_kv_heads);
+    if (c.head_dim != 64 && c.head_dim != 128)
+        return fail(PKA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c.head_dim);
+    if (c.page_size < 1 || c.page_size > 256 || (c.page_size & (c.page_size - 1)))
+        return fail(PKA_ERR_UNSUPPORTED, "page_size %d (supported: powers of two up to 256)", c.page_size);
+    if (c.num_pages < 1 || (int64_t)c.num_pages * c.page_size > INT32_MAX)
+        return fail(PKA_ERR_INVALID_ARG, "num_pages %d: pool slots must fit in int32", c.num_pages);
+    const bool pair_ok = (c.q_dtype == PKA_F32 && c.kv_dtype == PKA_F32) ||
+                         (c.q_dtype == PKA_BF16 && c.kv_dtype == PKA_BF16) ||
+                         (c.q_dtype == PKA_BF16 && c.kv_dtype == PKA_FP8_E4M3FN);
+    if (!pair_ok)
+        return fail(PKA_ERR_UNSUPPORTED, "dtype pair q=%d kv=%d (supported: f32/f32, bf16/bf16, bf16/fp8)",
+                    (int)c.q_dtype, (int)c.kv_dtype);
+    if (!std::isfinite(c.scale)) return fail(PKA_ERR_INVALID_ARG, "scale must be finite");
+    if (c.kv_dtype == PKA_FP8_E4M3FN) {
+        if (!(c.k_scale > 0.f) || !(c.v_scale > 0.f) || !std::isfinite(c.k_scale) ||
+            !std::isfinite(c.v_scale) || !std::isfinite(1.0f / c.k_scale) || !std::isfinite(1.0f / c.v_scale))
+            return fail(PKA_ERR_INVALID_ARG, "fp8 k_scale / v_scale must be positive and finite");
+    } else if (c.k_scale != 1.f || c.v_scale != 1.f) {
+        return fail(PKA_ERR_INVALID_ARG, "k_scale / v_scale apply to fp8 caches only (must be 1)");
+    }
+    pka_ctx* ctx = new (std::nothrow) pka_ctx;
+    if (!ctx) return fail(PKA_ERR_INVALID_ARG, "out of host memory");
+    ctx->cfg = c;
+    ctx->G = c.num_q_heads / c.num_kv_heads;
+    ctx->qgroups = (ctx->G + 15) / 16;
+    int shift = 0;
+    while ((1 << shift) < c.page_size) ++shift;
+    ctx->page_shift = shift;
+    const int units = c.num_kv_heads * ctx->qgroups;
+    int wpb = 8;
+    while (units % wpb) wpb >>= 1;
+    ctx->wpb = wpb;
+    ctx->ext_tq = pka::extend_tq(c.q_dtype, c.kv_dtype, c.head_dim, ctx->G);
+    *out = ctx;
+    return PKA_OK;
+}
+
+void pka_destroy(pka_ctx* ctx) { delete ctx; }
+
+pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t batch,
+                           int32_t num_q_tokens, int64_t max_kv_pages, pka_sizes* out) {
+    if (!ctx || !out) return fail(PKA_ERR_INVALID_ARG, "null context or output");
+    if (batch < 0 || num_q_tokens < 0 || max_kv_pages < 0)
+        return fail(PKA_ERR_INVALID_ARG, "negative sizes");
+    if (mode < PKA_MODE_EXTEND || mode > PKA_MODE_DRAFT_EXTEND)
+        return fail(PKA_ERR_INVALID_ARG, "unknown forward mode %d", (int)mode);
+    if (mode == PKA_MODE_DECODE && num_q_tokens != batch)
+        return fail(PKA_ERR_INVALID_ARG, "decode batch needs num_q_tokens == batch");
+    out->kv_indptr = (int64_t)batch + 1;
+    out->kv_indices = std::max<int64_t>(max_kv_pages, 1);
+    out->kv_last_page_len = std::max<int32_t>(batch, 1);
+    out->qo_indptr = (int64_t)batch + 1;
+    out->out_cache_loc = std::max<int32_t>(num_q_tokens, 1);
+    out->plan = pka::plan_elems(batch, num_q_tokens, ctx->ext_tq);
+    // split partials: only the decode path uses the workspace (an extend batch
+    // may still be routed to it by the speculative-attention dispatch)
+    out->workspace_bytes = mode == PKA_MODE_EXTEND || mode == PKA_MODE_IDLE
+                               ? 0
+                               : decode_ws_bytes(ctx, batch, pka::DEC_MAX_WG);
+    return PKA_OK;
+}
+
+pka_status pka_init_metadata(const pka_ctx* ctx, const int32_t* seq_lens,
+                             const int32_t* extend_lens, const int32_t* page_table,
+                             int32_t page_table_stride, int32_t page_table_cols, pka_batch* md,
+                             void* stream) {
+    pka_status s = check_batch(ctx, md);
+    if (s != PKA_OK) return s;
+    if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
+    if (!seq_lens || !page_table) return fail(PKA_ERR_INVALID_ARG, "null seq_lens or page_table");
+    if (md->mode != PKA_MODE_DECODE && !extend_lens)
+        return fail(PKA_ERR_INVALID_ARG, "extend-like batches need extend_lens");
+    if (page_table_cols < 1 || page_table_stride < page_table_cols)
+        return fail(PKA_ERR_INVALID_ARG, "page table stride %d / cols %d", page_table_stride, page_table_cols);
+    pka::MetaArgs a{};
+    a.seq_lens = seq_lens;
+    a.extend_lens = md->mode == PKA_MODE_DECODE ? nullptr : extend_lens;
+    a.page_table = page_table;
+    a.pt_stride = page_table_stride;
+    a.pt_cols = page_table_cols;
+    a.B = md->batch;
+    a.N = md->num_q_tokens;
+    a.max_kv_pages = md->max_kv_pages;
+    a.page_shift = ctx->page_shift;
+    a.num_pages = ctx->cfg.num_pages;
+    int32_t nwg = 0;
+    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+    a.nwg = nwg;
+    a.ext_tq = ctx->ext_tq;
+    a.is_decode = md->mode == PKA_MODE_DECODE;
+    a.kv_indptr = md->kv_indptr;
+    a.kv_indices = md->kv_indices;
+    a.kv_last_page_len = md->kv_last_page_len;
+    a.qo_indptr = md->qo_indptr;
+    a.out_cache_loc = md->out_cache_loc;
+    a.plan = md->plan;
+    hipError_t e = pka::launch_metadata(a, (hipStream_t)stream);
+    return e == hipSuccess ? PKA_OK : hip_fail(e, "metadata launch");
+}
+
+pka_status pka_save_kv(const pka_ctx* ctx, const pka_batch* md, const void* k_new,
+                       const void* v_new, void* k_pool, void* v_pool, void* stream) {
+    pka_status s = check_batch(ctx, md);
+    if (s != PKA_OK) return s;
+    if (md->mode == PKA_MODE_IDLE || md->num_q_tokens == 0) return PKA_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool)
+        return fail(PKA_ERR_INVALID_ARG, "null K/V or pool pointer");
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return fail(PKA_ERR_INVALID_ARG, "K/V rows and pools must be 16-byte aligned");
+    const pka_config& c = ctx->cfg;
+    pka::SaveArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.out_cache_loc = md->out_cache_loc;
+    a.plan = md->plan;
+    a.N = md->num_q_tokens;
+    a.row_elems = c.num_kv_heads * c.head_dim;
+    a.pool_slots = (int64_t)c.num_pages * c.page_size;
+    a.k_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f);
+    a.v_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f);
+    hipError_t e = pka::launch_save_kv(c.q_dtype, c.kv_dtype, c.head_dim, a, (hipStream_t)stream);
+    return e == hipSuccess ? PKA_OK : hip_fail(e, "save_kv launch");
+}
+
+pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* q,
+                           const void* k_pool, const void* v_pool, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
+    if (s != PKA_OK) return s;
+    if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
+    if (md->num_q_tokens != md->batch)
+        return fail(PKA_ERR_UNSUPPORTED, "the decode path takes one query per request (%d tokens, %d requests)",
+                    md->num_q_tokens, md->batch);
+    int32_t nwg = 0;
+    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+    const int64_t need = decode_ws_bytes(ctx, md->batch, nwg);
+    if (!workspace || (int64_t)workspace_bytes < need || !aligned16(workspace))
+        return fail(PKA_ERR_WORKSPACE, "decode needs %lld workspace bytes (16-byte aligned), got %zu",
+                    (long long)need, workspace_bytes);
+    pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
+    a.nwg = nwg;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * ctx->cfg.num_q_heads * ctx->cfg.head_dim;
+    hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->cfg.head_dim, a,
+                                      ctx->wpb, (hipStream_t)stream);
+    return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
+}
+
+pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* q,
+                           const void* k_pool, const void* v_pool, void* out, float* lse,
+                           void* /*workspace*/, size_t /*workspace_bytes*/, void* stream) {
+    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
+    if (s != PKA_OK) return s;
+    if (md->mode == PKA_MODE_IDLE || md->batch == 0 || md->num_q_tokens == 0) return PKA_OK;
+    if (!is_extend_like(md->mode))
+        return fail(PKA_ERR_INVALID_ARG, "metadata was built for a decode batch; extend needs extend metadata");
+    if (ctx->cfg.kv_dtype == PKA_FP8_E4M3FN)
+        return fail(PKA_ERR_UNSUPPORTED, "extend over an fp8 cache is not supported");
+    pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
+    hipError_t e = pka::launch_extend(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->cfg.head_dim, a,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? PKA_OK : hip_fail(e, "extend launch");
+}
+
+pka_path pka_select_path(pka_forward_mode mode, pka_spec_attn_mode spec_mode) {
+    switch (mode) {
+    case PKA_MODE_IDLE: return PKA_PATH_NONE;
+    case PKA_MODE_DECODE: return PKA_PATH_DECODE;
+    case PKA_MODE_TARGET_VERIFY:
+    case PKA_MODE_DRAFT_EXTEND:
+        return spec_mode == PKA_SPEC_DECODE ? PKA_PATH_DECODE : PKA_PATH_EXTEND;
+    default: return PKA_PATH_EXTEND;
+    }
+}
+
+pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
+                       const pka_batch* md, const void* q, const void* k_new, const void* v_new,
+                       int save_kv, void* k_pool, void* v_pool, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (mode < PKA_MODE_EXTEND || mode > PKA_MODE_DRAFT_EXTEND)
+        return fail(PKA_ERR_INVALID_ARG, "unknown forward mode %d", (int)mode);
+    if (spec_mode != PKA_SPEC_PREFILL && spec_mode != PKA_SPEC_DECODE)
+        return fail(PKA_ERR_INVALID_ARG, "unknown speculative attention mode %d", (int)spec_mode);
+    const pka_path path = pka_select_path(mode, spec_mode);
+    if (path == PKA_PATH_NONE) return PKA_OK;
+    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
+    if (s != PKA_OK) return s;
+    if (md->mode != mode)
+        return fail(PKA_ERR_INVALID_ARG, "metadata was built for mode %d, forward called with %d",
+                    (int)md->mode, (int)mode);
+    if (path == PKA_PATH_DECODE && md->num_q_tokens != md->batch)
+        return fail(PKA_ERR_UNSUPPORTED, "speculative decode-mode verify needs one query per request");
+    if (path == PKA_PATH_EXTEND && ctx->cfg.kv_dtype == PKA_FP8_E4M3FN)
+        return fail(PKA_ERR_UNSUPPORTED, "extend over an fp8 cache is not supported");
+    if (path == PKA_PATH_DECODE) {  // check the workspace before anything is enqueued
+        int32_t nwg = 0;
+        if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+        if (!workspace || (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg))
+            return fail(PKA_ERR_WORKSPACE, "decode workspace too small");
+    }
+    if (save_kv && (s = pka_save_kv(ctx, md, k_new, v_new, k_pool, v_pool, stream)) != PKA_OK)
+        return s;
+    if (path == PKA_PATH_DECODE)
+        return pka_attn_decode(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, stream);
+    return pka_attn_extend(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, stream);
+}
+
+pka_status pka_read_status(const pka_batch* md, int32_t* status, void* stream) {
+    if (!md || !status || !md->plan) return fail(PKA_ERR_INVALID_ARG, "null batch or status");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e == hipSuccess) e = hipMemcpy(status, md->plan + pka::PLAN_STATUS, sizeof(int32_t), hipMemcpyDeviceToHost);
+    return e == hipSuccess ? PKA_OK : hip_fail(e, "reading the status word");
+}
+
+}  // extern "C"

@@ -1,0 +1,465 @@
+// forward_decode: one query token per request against its paged cache.
+//
+// Decode reads one query against a long cache and is memory-bound
+// ("sglang-101 s4.2 --attention-backend", section "Two backends in one
+// server"; "[SGLang] Hybrid Attention", introduction).  The kernel is split-K
+// flash decoding: the batch's tokens, laid end to end, are cut into one equal
+// share per workgroup; each wave of a workgroup serves one KV head (16 query
+// heads of its group at most) over that share with an online softmax, and a
+// share that covers only part of a request leaves an fp32 partial (output and
+// log-sum-exp) that a merge kernel combines.
+//
+// gfx950 mapping of the MFMA variant (bf16 or fp8 e4m3fn cache):
+//   S^T[token, head]  = K[token, :] . Q^T        v_mfma_f32_16x16x32_bf16
+//   O^T[d, head]     += V^T[d, token] . P^T      v_mfma_f32_16x16x32_bf16
+// K rows are loaded straight into the A operand (16 bytes per lane, every
+// lane group of 16 covering whole 64-byte row segments); the scores come out
+// with one head per lane column, so the softmax row statistics stay in the
+// lane and P^T feeds the second MFMA without a shuffle.  V rows are loaded
+// as whole 256-byte (bf16) rows per 16 lanes and transposed in registers with
+// v_perm_b32 (fp8: byte gather + v_cvt_scalef32_pk_bf16_fp8).  The token order
+// inside a tile is a permutation chosen so every operand lines up.
+#include "pka_internal.h"
+
+namespace pka {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float LN2 = 0.69314718055994531f;
+
+__device__ inline uint32_t bits(bf16x2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};  // round to nearest even
+    return bits(v);
+}
+
+__device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// two fp8 e4m3fn codes (bytes 0,1 or, with HI, bytes 2,3 of w) -> two bf16
+// (exact: every e4m3fn value has a bf16 representation)
+template <bool HI>
+__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Pool slot of token position `pos` of a request whose pages start at
+// kv_indices[page_base]; indices and page ids are clamped into their buffers.
+__device__ inline int32_t slot_of(const AttnArgs& a, int32_t page_base, int32_t pos) {
+    int64_t idx = (int64_t)page_base + (pos >> a.page_shift);
+    idx = idx < a.kv_cap ? idx : a.kv_cap - 1;
+    int32_t pg = a.kv_indices[idx];
+    pg = min(max(pg, 0), a.num_pages - 1);
+    return (pg << a.page_shift) | (pos & ((1 << a.page_shift) - 1));
+}
+
+__device__ inline float wave_max_xor_16_32(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ inline float wave_sum_xor_16_32(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+// Write a finished (or partial) result of one wave: lane (n, j) owns head n
+// and the D/4 consecutive dims starting at j * D/4, stored as O[c][r] with
+// d = CPL * (4 j + r) + c.
+template <int D, typename Emit>
+__device__ inline void emit_rows(const f32x4_t (&O)[D / 16], float inv, int j, Emit emit) {
+    constexpr int CPL = D / 16;
+    float v[4 * CPL];
+    #pragma unroll
+    for (int r = 0; r < 4; ++r)
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) v[r * CPL + c] = O[c][r] * inv;
+    emit(v, 4 * CPL * j);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
+    constexpr int ESZ = FP8 ? 1 : 2;       // cache bytes per element
+    constexpr int KE = 16 / ESZ;           // elements per 16-byte K load
+    constexpr int NKL = D * ESZ / 64;      // 16-byte K loads per lane per 16 tokens
+    constexpr int KSTEPS = D / 32;         // MFMA k-steps of q.k
+    constexpr int SPL = KE / 8;            // k-steps per K load
+    constexpr int CPL = D / 16;            // V dims per lane per token = PV MFMAs
+    static_assert(NKL * SPL == KSTEPS, "k-step bookkeeping");
+
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, j = lane >> 4;
+    const int wpb = blockDim.x >> 6;
+    const int unit = blockIdx.y * wpb + (threadIdx.x >> 6);
+    const int g = unit / a.qgroups;
+    const int h0 = g * a.G + (unit % a.qgroups) * 16;
+    const int nh = min(16, a.G - (unit % a.qgroups) * 16);
+    if (g >= a.Hkv) return;
+
+    const int32_t* plan = a.plan;
+    const int32_t w = blockIdx.x;
+    const int32_t nwg = plan[PLAN_NWG];
+    if (w >= nwg) return;
+    const int64_t share = plan[PLAN_SHARE];
+    const int64_t W = plan[PLAN_TOTAL];
+    const int64_t start = (int64_t)w * share;
+    if (start >= W) return;
+    const int64_t end = min(start + share, W);
+    const int32_t* F = plan + plan_seg_prefix(a.B);
+    int32_t seg = plan[plan_wg_seg(a.B) + w];
+
+    const int64_t row_bytes = (int64_t)a.Hkv * D * ESZ;  // one pool slot, all KV heads
+    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * D * ESZ;
+    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * D * ESZ;
+    const int tok = lane & 31;  // tile token whose slot this lane looks up
+
+    for (; seg < a.B; ++seg) {
+        const int32_t f0 = F[seg], f1 = F[seg + 1];
+        if (f0 >= end) break;
+        const int32_t lo = (int32_t)(max(start, (int64_t)f0) - f0);
+        const int32_t hi = (int32_t)(min(end, (int64_t)f1) - f0);
+        const int32_t L = f1 - f0;
+        const int32_t b = seg;
+        const int32_t page_base = a.kv_indptr[b];
+        const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);  // the request's query row
+
+        // Q^T operand: lane (n, j) holds head h0+n at the dims its K lanes load.
+        bf16x8_t qop[KSTEPS];
+        {
+            const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + h0 + n) * D;
+            #pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const int d0 = (ks / SPL) * 4 * KE + j * KE + (ks % SPL) * 8;
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (n < nh) v = *(const u32x4_t*)(qrow + d0);
+                qop[ks] = as_bf16x8(v);
+            }
+        }
+
+        f32x4_t O[CPL];
+        #pragma unroll
+        for (int c = 0; c < CPL; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float m2 = -INFINITY, lsum = 0.f;
+
+        int32_t slot_cur = slot_of(a, page_base, lo + tok < hi ? lo + tok : lo);
+        for (int32_t t0 = lo; t0 < hi; t0 += DEC_TILE) {
+            // next tile's slot: issued now, used next iteration
+            const int32_t pn = t0 + DEC_TILE + tok;
+            const int32_t slot_next = slot_of(a, page_base, pn < hi ? pn : lo);
+
+            // K rows: row block sb holds tile tokens 16*sb + n
+            const int32_t slot_x = __shfl_xor(slot_cur, 16);
+            const int32_t ks0 = (j & 1) ? slot_x : slot_cur;
+            const int32_t ks1 = (j & 1) ? slot_cur : slot_x;
+            u32x4_t kr[2][NKL];
+            #pragma unroll
+            for (int s = 0; s < NKL; ++s) {
+                kr[0][s] = *(const u32x4_t*)(kbase + ks0 * row_bytes + s * 64 + j * 16);
+                kr[1][s] = *(const u32x4_t*)(kbase + ks1 * row_bytes + s * 64 + j * 16);
+            }
+            // V rows: k-slot q of lane group j is tile token 16*(q/4) + 4*j + q%4
+            typedef typename std::conditional<CPL * ESZ == 16, u32x4_t,
+                    typename std::conditional<CPL * ESZ == 8, u32x2_t, uint32_t>::type>::type vrow_t;
+            vrow_t vr[8];
+            #pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int32_t vs = __shfl(slot_cur, 16 * (q >> 2) + 4 * j + (q & 3));
+                vr[q] = *(const vrow_t*)(vbase + vs * row_bytes + n * (CPL * ESZ));
+            }
+
+            // S^T = K . Q^T, two 16-token row blocks
+            f32x4_t S[2];
+            #pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                S[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                #pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    u32x4_t kw;
+                    if constexpr (FP8) {
+                        const u32x4_t raw = kr[sb][ks / SPL];
+                        const uint32_t w0 = (ks % SPL) ? raw.z : raw.x;
+                        const uint32_t w1 = (ks % SPL) ? raw.w : raw.y;
+                        kw = u32x4_t{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                                     fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
+                    } else {
+                        kw = kr[sb][ks];
+                    }
+                    S[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[ks], S[sb],
+                                                                    0, 0, 0);
+                }
+            }
+
+            // online softmax (log2 domain); lane (n, j) holds head n, tokens
+            // 16*sb + 4*j + r of this tile
+            float s[8];
+            float mx = -INFINITY;
+            #pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+                #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool valid = t0 + 16 * sb + 4 * j + r < hi;
+                    const float v = valid ? S[sb][r] * a.scale_log2 : -INFINITY;
+                    s[sb * 4 + r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            mx = wave_max_xor_16_32(mx);
+            const float mnew = fmaxf(m2, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+            m2 = mnew;
+            float psum = 0.f;
+            #pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                s[i] = __builtin_amdgcn_exp2f(s[i] - mnew);
+                psum += s[i];
+            }
+            lsum = lsum * alpha + psum;
+            #pragma unroll
+            for (int c = 0; c < CPL; ++c) O[c] *= alpha;
+            const u32x4_t pw = {pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3]),
+                                pack_bf16(s[4], s[5]), pack_bf16(s[6], s[7])};
+            const bf16x8_t pop = as_bf16x8(pw);
+
+            // O^T += V^T . P^T, one MFMA per d-row block c (d = CPL*m + c)
+            if constexpr (!FP8) {
+                #pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+                    u32x4_t av;
+                    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        uint32_t lo_w, hi_w;
+                        if constexpr (CPL == 8) {
+                            lo_w = vr[2 * u][c >> 1];
+                            hi_w = vr[2 * u + 1][c >> 1];
+                        } else {
+                            lo_w = vr[2 * u][c >> 1];
+                            hi_w = vr[2 * u + 1][c >> 1];
+                        }
+                        av[u] = __builtin_amdgcn_perm(hi_w, lo_w, sel);
+                    }
+                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
+                }
+            } else {
+                #pragma unroll
+                for (int c = 0; c < CPL; c += 2) {
+                    const uint32_t sel = ((c & 3) == 0) ? 0x05010400u : 0x07030602u;
+                    u32x4_t a0, a1;
+                    #pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        uint32_t lo_w, hi_w;
+                        if constexpr (CPL == 8) {
+                            lo_w = vr[2 * u][c >> 2];
+                            hi_w = vr[2 * u + 1][c >> 2];
+                        } else {
+                            lo_w = vr[2 * u];
+                            hi_w = vr[2 * u + 1];
+                        }
+                        const uint32_t x = __builtin_amdgcn_perm(hi_w, lo_w, sel);
+                        a0[u] = fp8x2_to_bf16x2<false>(x);
+                        a1[u] = fp8x2_to_bf16x2<true>(x);
+                    }
+                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), pop, O[c], 0, 0, 0);
+                    O[c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), pop, O[c + 1],
+                                                                       0, 0, 0);
+                }
+            }
+            slot_cur = slot_next;
+        }
+
+        // finish: denominator over the four lane groups of each head
+        const float ltot = wave_sum_xor_16_32(lsum);
+        const float inv = 1.0f / ltot;
+        const float lse_nat = (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
+        if (n < nh) {
+            const int32_t h = h0 + n;
+            if (lo == 0 && hi == L) {
+                __bf16* orow = (__bf16*)a.out + ((int64_t)qr * a.Hq + h) * D;
+                emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+                    #pragma unroll
+                    for (int i = 0; i < 4 * CPL; i += 8) {
+                        const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
+                                            pack_bf16(v[i + 4], v[i + 5]),
+                                            pack_bf16(v[i + 6], v[i + 7])};
+                        *(u32x4_t*)(orow + d0 + i) = pk;
+                    }
+                });
+                if (a.lse && j == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
+            } else {
+                const int64_t ps = (int64_t)b + w;  // partial slot of (request, workgroup)
+                float* prow = a.ws_o + (ps * a.Hq + h) * D;
+                emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+                    #pragma unroll
+                    for (int i = 0; i < 4 * CPL; i += 4)
+                        *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
+                });
+                if (j == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
+            }
+        }
+    }
+}
+
+// fp32 cache: a plain VALU variant with the same work partition (lanes over
+// head_dim, one token at a time).  Used for fp32 workloads.
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
+    constexpr int EPL = D / 64;  // dims per lane
+    const int lane = threadIdx.x & 63;
+    const int wpb = blockDim.x >> 6;
+    const int unit = blockIdx.y * wpb + (threadIdx.x >> 6);
+    const int g = unit / a.qgroups;
+    const int h0 = g * a.G + (unit % a.qgroups) * 16;
+    const int nh = min(16, a.G - (unit % a.qgroups) * 16);
+    if (g >= a.Hkv) return;
+    const int32_t* plan = a.plan;
+    const int32_t w = blockIdx.x;
+    if (w >= plan[PLAN_NWG]) return;
+    const int64_t share = plan[PLAN_SHARE], W = plan[PLAN_TOTAL];
+    const int64_t start = (int64_t)w * share;
+    if (start >= W) return;
+    const int64_t end = min(start + share, W);
+    const int32_t* F = plan + plan_seg_prefix(a.B);
+    const float scale2 = a.scale_log2;
+    for (int32_t seg = plan[plan_wg_seg(a.B) + w]; seg < a.B; ++seg) {
+        const int32_t f0 = F[seg], f1 = F[seg + 1];
+        if (f0 >= end) break;
+        const int32_t lo = (int32_t)(max(start, (int64_t)f0) - f0);
+        const int32_t hi = (int32_t)(min(end, (int64_t)f1) - f0);
+        const int32_t b = seg, page_base = a.kv_indptr[b];
+        const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
+        float q[16][EPL], o[16][EPL], m[16], l[16];
+        #pragma unroll
+        for (int hh = 0; hh < 16; ++hh) {
+            m[hh] = -INFINITY;
+            l[hh] = 0.f;
+            #pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                q[hh][e] = hh < nh ? ((const float*)a.q)[((int64_t)qr * a.Hq + h0 + hh) * D + e * 64 + lane] : 0.f;
+                o[hh][e] = 0.f;
+            }
+        }
+        for (int32_t t = lo; t < hi; ++t) {
+            const int64_t base = ((int64_t)slot_of(a, page_base, t) * a.Hkv + g) * D;
+            float k[EPL], v[EPL];
+            #pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                k[e] = ((const float*)a.k_pool)[base + e * 64 + lane];
+                v[e] = ((const float*)a.v_pool)[base + e * 64 + lane];
+            }
+            #pragma unroll
+            for (int hh = 0; hh < 16; ++hh) {
+                if (hh >= nh) continue;
+                float dot = 0.f;
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) dot += q[hh][e] * k[e];
+                #pragma unroll
+                for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+                const float s = dot * scale2;
+                const float mn = fmaxf(m[hh], s);
+                const float al = __builtin_amdgcn_exp2f(m[hh] - mn);
+                const float p = __builtin_amdgcn_exp2f(s - mn);
+                m[hh] = mn;
+                l[hh] = l[hh] * al + p;
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) o[hh][e] = o[hh][e] * al + p * v[e];
+            }
+        }
+        const bool full = lo == 0 && hi == f1 - f0;
+        #pragma unroll
+        for (int hh = 0; hh < 16; ++hh) {
+            if (hh >= nh) continue;
+            const int32_t h = h0 + hh;
+            const float inv = 1.0f / l[hh];
+            const float lse_nat = (m[hh] + __builtin_amdgcn_logf(l[hh])) * LN2;
+            if (full) {
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    ((float*)a.out)[((int64_t)qr * a.Hq + h) * D + e * 64 + lane] = o[hh][e] * inv;
+                if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
+            } else {
+                const int64_t ps = (int64_t)b + w;
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    a.ws_o[(ps * a.Hq + h) * D + e * 64 + lane] = o[hh][e] * inv;
+                if (lane == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
+            }
+        }
+    }
+}
+
+// Log-sum-exp merge of the partials of requests that were split across
+// workgroups: out = sum_c e^(lse_c - M) o_c / sum_c e^(lse_c - M) and
+// lse = M + ln(sum_c e^(lse_c - M)).  One wave per (request, head).
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
+    constexpr int EPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int32_t b = blockIdx.x;
+    const int32_t h = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (h >= a.Hq) return;
+    const int32_t* plan = a.plan;
+    const int64_t share = plan[PLAN_SHARE];
+    const int32_t* F = plan + plan_seg_prefix(a.B);
+    const int64_t f0 = F[b], f1 = F[b + 1];
+    if (f1 <= f0) return;
+    const int64_t w0 = f0 / share, w1 = (f1 - 1) / share;
+    if (w0 == w1) return;  // written directly by its only workgroup
+    float M = -INFINITY;
+    for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, a.ws_lse[(b + w) * a.Hq + h]);
+    float den = 0.f, acc[EPL];
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    for (int64_t w = w0; w <= w1; ++w) {
+        const float wt = expf(a.ws_lse[(b + w) * a.Hq + h] - M);
+        den += wt;
+        const float* prow = a.ws_o + ((b + w) * a.Hq + h) * D;
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += wt * prow[e * 64 + lane];
+    }
+    const float inv = 1.0f / den;
+    const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+        const int64_t o = ((int64_t)qr * a.Hq + h) * D + e * 64 + lane;
+        if constexpr (OUT_BF16)
+            ((__bf16*)a.out)[o] = (__bf16)(acc[e] * inv);
+        else
+            ((float*)a.out)[o] = acc[e] * inv;
+    }
+    if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = M + logf(den);
+}
+
+template <int D>
+hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb, hipStream_t s) {
+    const int units = a.Hkv * a.qgroups;
+    const dim3 grid(a.nwg, units / wpb);
+    const dim3 block(64 * wpb);
+    if (kv == PKA_BF16)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, false>), grid, block, 0, s, a);
+    else if (kv == PKA_FP8_E4M3FN)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_f32_kernel<D>), grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 mgrid(a.B, (a.Hq + 3) / 4);
+    if (q == PKA_BF16)
+        hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_merge_kernel<D, false>), mgrid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, int wpb,
+                         hipStream_t s) {
+    if (D == 128) return launch_decode_d<128>(q, kv, a, wpb, s);
+    if (D == 64) return launch_decode_d<64>(q, kv, a, wpb, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pka

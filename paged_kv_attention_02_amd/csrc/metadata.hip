@@ -1,0 +1,261 @@
+// Per-batch metadata: page-table rows -> CSR index buffers and the work plan.
+//
+// The pages define an attention backend as building per-batch metadata such
+// as page tables and index buffers before running forward_extend or
+// forward_decode ("sglang-101 s4.2 --attention-backend", section "What an
+// attention backend is").  Two launches:
+//   md_scan   one workgroup: clamps lengths, prefix sums (kv_indptr,
+//             qo_indptr, flattened token prefix), kv_last_page_len, and the
+//             decode / extend work partitions;
+//   md_gather a grid over requests: kv_indices (page ids, clamped into the
+//             pool) and out_cache_loc (slot of every new token).
+#include <algorithm>
+
+#include "pka_internal.h"
+
+namespace pka {
+namespace {
+
+constexpr int SCAN_THREADS = 1024;
+
+// Inclusive block scan of three int64 values (Hillis-Steele in LDS).
+__device__ inline void block_scan3(int64_t& x0, int64_t& x1, int64_t& x2, int64_t* sh) {
+    const int t = threadIdx.x;
+    sh[t] = x0;
+    sh[SCAN_THREADS + t] = x1;
+    sh[2 * SCAN_THREADS + t] = x2;
+    __syncthreads();
+    for (int off = 1; off < SCAN_THREADS; off <<= 1) {
+        int64_t a0 = 0, a1 = 0, a2 = 0;
+        if (t >= off) {
+            a0 = sh[t - off];
+            a1 = sh[SCAN_THREADS + t - off];
+            a2 = sh[2 * SCAN_THREADS + t - off];
+        }
+        __syncthreads();
+        sh[t] += a0;
+        sh[SCAN_THREADS + t] += a1;
+        sh[2 * SCAN_THREADS + t] += a2;
+        __syncthreads();
+    }
+    x0 = sh[t];
+    x1 = sh[SCAN_THREADS + t];
+    x2 = sh[2 * SCAN_THREADS + t];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
+    __shared__ int64_t sh[3 * SCAN_THREADS];
+    __shared__ int64_t carry[3];
+    __shared__ int32_t s_status;
+    const int t = threadIdx.x;
+    const int32_t P = 1 << a.page_shift;
+    int32_t* F = a.plan + plan_seg_prefix(a.B);
+    if (t == 0) {
+        carry[0] = carry[1] = carry[2] = 0;
+        s_status = 0;
+        a.kv_indptr[0] = 0;
+        a.qo_indptr[0] = 0;
+        F[0] = 0;
+    }
+    __syncthreads();
+    int32_t flags = 0;
+    for (int32_t base = 0; base < a.B; base += SCAN_THREADS) {
+        const int32_t b = base + t;
+        int64_t L = 0, n = 0, pages = 0;
+        if (b < a.B) {
+            L = a.seq_lens[b];
+            n = a.is_decode ? 1 : a.extend_lens[b];
+            if (L < 1) { flags |= PKA_DEV_BAD_LENGTH; L = 1; }
+            if (n < 0) { flags |= PKA_DEV_BAD_LENGTH; n = 0; }
+            if (n > L) { flags |= PKA_DEV_BAD_LENGTH; n = L; }
+            pages = (L + P - 1) >> a.page_shift;
+            if (pages > a.pt_cols) {
+                flags |= PKA_DEV_TABLE_SHORT;
+                pages = a.pt_cols;
+                L = (int64_t)a.pt_cols << a.page_shift;
+                if (n > L) n = L;
+            }
+        }
+        int64_t ip = pages, iq = n, iL = L;
+        block_scan3(ip, iq, iL, sh);
+        if (b < a.B) {
+            const int64_t cp = carry[0] + ip, cq = carry[1] + iq, cL = carry[2] + iL;
+            if (cp > a.max_kv_pages || cq > a.N || cL > INT32_MAX) flags |= PKA_DEV_CAPACITY;
+            a.kv_indptr[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
+            a.qo_indptr[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
+            F[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
+            a.kv_last_page_len[b] = (int32_t)(L - ((pages - 1) << a.page_shift));
+        }
+        __syncthreads();
+        if (t == SCAN_THREADS - 1) {
+            carry[0] += ip;
+            carry[1] += iq;
+            carry[2] += iL;
+        }
+        __syncthreads();
+    }
+    if (flags) atomicOr(&s_status, flags);
+    __syncthreads();
+    __threadfence_block();
+
+    const int64_t W = min(carry[2], (int64_t)INT32_MAX);
+    {
+        // Decode partition (built for every batch, so a verify batch can take
+        // either path): the flattened token range [0, W) is cut into nwg equal
+        // shares, rounded up to whole tiles; workgroup w starts in the request
+        // that holds token w * share.
+        int64_t share = (W + a.nwg - 1) / a.nwg;
+        share = (share + DEC_TILE - 1) / DEC_TILE * DEC_TILE;
+        if (share < DEC_MIN_SHARE) share = DEC_MIN_SHARE;
+        int32_t* wg_seg = a.plan + plan_wg_seg(a.B);
+        for (int32_t w = t; w < a.nwg; w += SCAN_THREADS) {
+            const int64_t pos = (int64_t)w * share;
+            int32_t seg = a.B;
+            if (pos < W) {
+                int32_t lo = 0, hi = a.B - 1;  // largest b with F[b] <= pos
+                while (lo < hi) {
+                    const int32_t mid = (lo + hi + 1) >> 1;
+                    if (F[mid] <= pos) lo = mid; else hi = mid - 1;
+                }
+                seg = lo;
+            }
+            wg_seg[w] = seg;
+        }
+        if (t == 0) {
+            a.plan[PLAN_SHARE] = (int32_t)share;
+            a.plan[PLAN_TOTAL] = (int32_t)W;
+            a.plan[PLAN_NWG] = a.nwg;
+            a.plan[PLAN_EXT_COUNT] = 0;
+            a.plan[PLAN_EXT_TQ] = a.ext_tq;
+        }
+    }
+    if (!a.is_decode) {
+        // Extend items (request, query tile), heaviest first: a tile's cost
+        // grows with the last key position it attends to.
+        const int32_t tq = a.ext_tq;
+        const int64_t cap = plan_ext_capacity(a.B, a.N, tq);
+        int32_t* items = a.plan + plan_ext_items(a.B);
+        __shared__ int32_t s_count;
+        if (t == 0) s_count = 0;
+        __syncthreads();
+        // pass 1: count (serial over requests in chunks, tiles in parallel)
+        for (int32_t b = 0; b < a.B; ++b) {
+            const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
+            const int32_t tiles = (q1 - q0 + tq - 1) / tq;
+            for (int32_t i = t; i < tiles; i += SCAN_THREADS) {
+                const int32_t slot = s_count + i;
+                if (slot < cap) {
+                    items[2 * slot] = b;
+                    items[2 * slot + 1] = i;
+                }
+            }
+            __syncthreads();
+            if (t == 0) s_count += tiles;
+            __syncthreads();
+        }
+        int32_t count = s_count;
+        if (count > cap) { flags |= PKA_DEV_CAPACITY; count = (int32_t)cap; }
+        // sort by weight (descending) with a bitonic sort in LDS when small
+        constexpr int SORT_MAX = 2048;
+        __shared__ uint32_t keys[SORT_MAX];
+        if (count <= SORT_MAX && count > 1) {
+            int n2 = 1;
+            while (n2 < count) n2 <<= 1;
+            for (int i = t; i < n2; i += SCAN_THREADS) {
+                uint32_t key = 0;  // padding sorts last
+                if (i < count) {
+                    const int32_t b = items[2 * i], ti = items[2 * i + 1];
+                    const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
+                    const int32_t L = F[b + 1] - F[b];
+                    const int32_t n = q1 - q0;
+                    const int32_t last = L - n + min((ti + 1) * tq, n);  // keys of the tile's last row
+                    const uint32_t wgt = (uint32_t)min(last, (1 << 20) - 1);
+                    key = (wgt << 11) | (uint32_t)(SORT_MAX - 1 - i);  // ties: lower index first
+                    key = key + 1;  // keep 0 for padding
+                }
+                keys[i] = key;
+            }
+            __syncthreads();
+            for (int k = 2; k <= n2; k <<= 1) {
+                for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                    for (int i = t; i < n2; i += SCAN_THREADS) {
+                        const int ixj = i ^ jj;
+                        if (ixj > i) {
+                            const uint32_t x = keys[i], y = keys[ixj];
+                            const bool desc = (i & k) == 0;
+                            if (desc ? (x < y) : (x > y)) {
+                                keys[i] = y;
+                                keys[ixj] = x;
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            // rebuild the item list in sorted order
+            for (int i = t; i < count; i += SCAN_THREADS) {
+                const uint32_t key = keys[i] - 1;
+                const int32_t src = SORT_MAX - 1 - (int32_t)(key & (SORT_MAX - 1));
+                sh[i] = ((int64_t)items[2 * src] << 32) | (uint32_t)items[2 * src + 1];
+            }
+            __syncthreads();
+            for (int i = t; i < count; i += SCAN_THREADS) {
+                items[2 * i] = (int32_t)(sh[i] >> 32);
+                items[2 * i + 1] = (int32_t)(sh[i] & 0xffffffff);
+            }
+        }
+        if (t == 0) a.plan[PLAN_EXT_COUNT] = count;
+    }
+    if (flags) atomicOr(&s_status, flags);
+    __syncthreads();
+    if (t == 0) a.plan[PLAN_STATUS] = s_status;
+}
+
+// kv_indices and out_cache_loc.  Grid (x, B); page ids outside the pool are
+// clamped (and flagged) so that no later kernel reads outside the pools.
+__global__ __launch_bounds__(256) void md_gather_kernel(MetaArgs a) {
+    const int32_t b = blockIdx.y;
+    const int32_t P = 1 << a.page_shift;
+    const int32_t p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
+    const int32_t L = (p1 - p0 - 1) * P + a.kv_last_page_len[b];
+    const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
+    const int32_t n = q1 - q0;
+    const int32_t* row = a.page_table + (int64_t)b * a.pt_stride;
+    int32_t flags = 0;
+    const int32_t step = gridDim.x * blockDim.x;
+    for (int32_t k = blockIdx.x * blockDim.x + threadIdx.x; k < p1 - p0; k += step) {
+        int32_t pg = row[k];
+        if (pg < 0 || pg >= a.num_pages) {
+            flags |= PKA_DEV_BAD_PAGE;
+            pg = min(max(pg, 0), a.num_pages - 1);
+        }
+        if (p0 + k < a.max_kv_pages) a.kv_indices[p0 + k] = pg;
+    }
+    for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += step) {
+        const int32_t pos = L - n + i;
+        int32_t pg = row[pos >> a.page_shift];
+        if (pg < 0 || pg >= a.num_pages) {
+            flags |= PKA_DEV_BAD_PAGE;
+            pg = min(max(pg, 0), a.num_pages - 1);
+        }
+        if (q0 + i < a.N) a.out_cache_loc[q0 + i] = (pg << a.page_shift) | (pos & (P - 1));
+    }
+    if (flags) atomicOr(a.plan + PLAN_STATUS, flags);
+}
+
+}  // namespace
+
+hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(md_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.B == 0) return e;
+    // enough blocks per request to cover its pages in one or two strides
+    int64_t per_req = (a.max_kv_pages / a.B + 255) / 256;
+    if (!a.is_decode) per_req = std::max<int64_t>(per_req, ((int64_t)a.N / a.B + 255) / 256);
+    const int gx = (int)std::min<int64_t>(std::max<int64_t>(per_req, 1), 64);
+    hipLaunchKernelGGL(md_gather_kernel, dim3(gx, a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace pka

@@ -1,0 +1,117 @@
+// Internal declarations shared by the libpka translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pka.h"
+
+namespace pka {
+
+// ----------------------------------------------------------------- plan --
+// Layout of the int32 `plan` array of a pka_batch.
+enum : int32_t {
+    PLAN_STATUS = 0,     // sticky PKA_DEV_* flags (device writes, host reads)
+    PLAN_SHARE = 1,      // decode: tokens of the flattened batch per workgroup
+    PLAN_TOTAL = 2,      // decode: sum of L_b
+    PLAN_NWG = 3,        // decode: workgroups the partition was made for
+    PLAN_EXT_COUNT = 4,  // extend: number of (request, query tile) items
+    PLAN_EXT_TQ = 5,     // extend: query tokens per item
+    PLAN_HDR = 16,
+};
+
+// Tokens per decode tile (two MFMA row blocks of 16 tokens).
+constexpr int DEC_TILE = 32;
+// Smallest share of the flattened token range given to one workgroup.
+constexpr int DEC_MIN_SHARE = 64;
+// Upper bound of decode workgroups (persistent grid).
+constexpr int DEC_MAX_WG = 2048;
+
+// plan offsets that depend on the batch size
+__host__ __device__ inline int64_t plan_seg_prefix(int32_t /*B*/) { return PLAN_HDR; }
+__host__ __device__ inline int64_t plan_wg_seg(int32_t B) { return PLAN_HDR + (int64_t)B + 1; }
+__host__ __device__ inline int64_t plan_ext_items(int32_t B) {
+    return plan_wg_seg(B) + DEC_MAX_WG;
+}
+// extend items (request, query tile of tq tokens): at most ceil(N / tq) + B
+__host__ __device__ inline int64_t plan_ext_capacity(int32_t B, int32_t N, int32_t tq) {
+    return ((int64_t)N + tq - 1) / tq + B;
+}
+__host__ __device__ inline int64_t plan_elems(int32_t B, int32_t N, int32_t tq) {
+    return plan_ext_items(B) + 2 * plan_ext_capacity(B, N, tq);
+}
+
+// --------------------------------------------------------------- launch --
+struct MetaArgs {
+    const int32_t* seq_lens;
+    const int32_t* extend_lens;  // null: decode (n_b = 1)
+    const int32_t* page_table;
+    int64_t pt_stride;
+    int32_t pt_cols;
+    int32_t B;
+    int32_t N;
+    int64_t max_kv_pages;
+    int32_t page_shift;
+    int32_t num_pages;
+    int32_t nwg;       // decode workgroups
+    int32_t ext_tq;    // extend query tokens per item
+    int32_t is_decode;
+    int32_t* kv_indptr;
+    int32_t* kv_indices;
+    int32_t* kv_last_page_len;
+    int32_t* qo_indptr;
+    int32_t* out_cache_loc;
+    int32_t* plan;
+};
+
+struct SaveArgs {
+    const void* k_new;
+    const void* v_new;
+    void* k_pool;
+    void* v_pool;
+    const int32_t* out_cache_loc;
+    int32_t* plan;
+    int32_t N;
+    int32_t row_elems;  // Hkv * D
+    int64_t pool_slots;
+    float k_inv;  // fp32(1 / k_scale)
+    float v_inv;
+};
+
+struct AttnArgs {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    void* out;
+    float* lse;
+    float* ws_o;    // split partials [(B + nwg), Hq, D] fp32
+    float* ws_lse;  // [(B + nwg), Hq]
+    const int32_t* kv_indptr;
+    const int32_t* kv_indices;
+    const int32_t* kv_last_page_len;
+    const int32_t* qo_indptr;
+    const int32_t* plan;
+    int64_t kv_cap;  // capacity of kv_indices (reads are clamped below it)
+    int32_t B;
+    int32_t N;
+    int32_t Hq;
+    int32_t Hkv;
+    int32_t G;
+    int32_t qgroups;  // ceil(G / 16): waves per KV head
+    int32_t page_shift;
+    int32_t num_pages;
+    int32_t nwg;
+    float scale_log2;  // scale * log2(e) * k_scale
+    float v_scale;
+};
+
+hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
+hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, int D, const SaveArgs& a, hipStream_t s);
+hipError_t launch_decode(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, int waves_per_wg,
+                         hipStream_t s);
+hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hipStream_t s);
+
+// Query tokens per extend item for a dtype pair.
+int extend_tq(pka_dtype q, pka_dtype kv, int D, int G);
+
+}  // namespace pka

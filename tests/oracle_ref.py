@@ -61,12 +61,13 @@ def oracle_full(layout: workloads.Layout, values: workloads.Values, threads: int
 
 
 def oracle_requests(layout: workloads.Layout, values: workloads.Values, requests, heads=None,
-                    threads: int = 0):
+                    tokens=None, threads: int = 0):
     """Oracle output for a few requests of a large batch.
 
     Each selected request is re-packed into a compact single-request problem
     (its own tokens, contiguous pages); attention of a request does not depend
-    on where its pages sit in the pool.  Returns {b: (out [n_b, H, D], lse)}.
+    on where its pages sit in the pool.  ``tokens(n_b)`` may pick a subset of
+    the request's new tokens.  Returns {b: (token_idx, out [t, H, D], lse [t, H])}.
     """
     spec = layout.spec
     offs = workloads.request_token_offsets(layout)
@@ -85,11 +86,13 @@ def oracle_requests(layout: workloads.Layout, values: workloads.Values, requests
         ext = None if spec.mode == "decode" else sub.extend_lens
         Hq = spec.num_q_heads
         hs = list(range(Hq)) if heads is None else list(heads)
-        sel = np.array([t * Hq + h for t in range(n) for h in hs], dtype=np.int64)
+        ts = list(range(n)) if tokens is None else list(tokens(n))
+        sel = np.array([t * Hq + h for t in ts for h in hs], dtype=np.int64)
         out, lse = oracle.attention(sub.seq_lens, ext, sub.page_table, P, pages, q, spec.q_dtype,
                                     kp, vp, spec.kv_dtype, spec.softmax_scale, values.k_scale,
                                     values.v_scale, sel=sel, threads=threads)
-        res[b] = (out.reshape(n, len(hs), spec.head_dim), lse.reshape(n, len(hs)))
+        res[b] = (np.asarray(ts, dtype=np.int64), out.reshape(len(ts), len(hs), spec.head_dim),
+                  lse.reshape(len(ts), len(hs)))
     return res
 
 
