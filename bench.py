@@ -1,0 +1,258 @@
+"""Benchmark of the paged KV attention path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+A step is one pass of the whole hot path over one batch: per-batch metadata
+(init_metadata), the cache write of the new tokens (save_kv) and attention
+(attn_decode, split kernel + merge), on the Llama-3-8B-shaped decode workload
+(batch 64, 32/8 heads, head_dim 128, bf16, page size 16, seq_lens uniform in
+[512, 4096]).  Inputs are resident in HBM before timing starts.  The JSON line
+reports KV bytes read per step / step time, the dominant kernel against the
+HBM roofline (HIP events on the stream the kernels run on), the oracle timed
+on the host cores, and the extend and the other decode workloads as extras.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published
+METRIC = "paged decode KV-read GB/s (% HBM peak); extend TFLOP/s (% MFMA peak)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kv_bytes(layout) -> int:
+    spec = layout.spec
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}[spec.kv_dtype]
+    return int(layout.total_tokens) * spec.num_kv_heads * spec.head_dim * 2 * eb
+
+
+def decode_algorithmic_bytes(layout) -> int:
+    """KV read + Q read + O write + index buffers (kv_indices, indptr, last_page_len)."""
+    spec = layout.spec
+    qb = {"f32": 4, "bf16": 2}[spec.q_dtype]
+    qo = layout.batch * spec.num_q_heads * spec.head_dim * qb * 2
+    idx = 4 * (layout.kv_pages + 2 * layout.batch + 1)
+    return kv_bytes(layout) + qo + idx
+
+
+def extend_flops(layout) -> float:
+    """4 * D * Hq * (causally valid query/key pairs): q.k and p.v, 2 flops per MAC."""
+    spec = layout.spec
+    pairs = 0
+    for L, n in zip(layout.seq_lens.tolist(), layout.extend_lens.tolist()):
+        p = L - n
+        pairs += n * p + n * (n + 1) // 2
+    return 4.0 * spec.head_dim * spec.num_q_heads * pairs
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_attention_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key: str, src_hash: str):
+    """Counter-derived HBM bytes per launch, if measured on the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_events(fn, iters: int, warm: int = 2):
+    """Average ms per call of fn() from HIP events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(iters):
+        fn(i)
+    stop.record()
+    stop.synchronize()
+    return start.elapsed_time(stop) / iters
+
+
+def cpu_baseline(layout, values, budget_s: float = 20.0):
+    """The oracle (fp64, OpenMP) on whole requests of the same workload until
+    about budget_s of work; reported in the same unit as the GPU value."""
+    import numpy as np
+    from tests.oracle_ref import oracle_requests
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    order = list(range(layout.batch))
+    done, kv, t_total = [], 0, 0.0
+    spec = layout.spec
+    eb = {"f32": 4, "bf16": 2, "fp8": 1}[spec.kv_dtype]
+    for b in order:
+        t0 = time.perf_counter()
+        oracle_requests(layout, values, [b], threads=threads)
+        t_total += time.perf_counter() - t0
+        done.append(b)
+        kv += int(layout.seq_lens[b]) * spec.num_kv_heads * spec.head_dim * 2 * eb
+        if t_total >= budget_s:
+            break
+    return {"value": round(kv / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(done)} of {layout.batch} requests ({sum(int(layout.seq_lens[b]) for b in done)} "
+                      f"cached tokens), all {spec.num_q_heads} heads, fp64 C oracle, "
+                      f"{oracle.max_threads()} OpenMP threads, wall {t_total:.2f} s incl. "
+                      f"per-request cache repacking"}
+
+
+def bench_decode_kernel(cfg_id: int, iters: int):
+    """Kernel-level decode figure for one workload (attn_decode alone)."""
+    import torch
+    import workloads
+    from tests.gpu_problem import GpuProblem
+    layout = workloads.make_layout(workloads.CONFIGS[cfg_id])
+    prob = GpuProblem(layout)
+    prob.attention_step(save=True)
+    torch.cuda.synchronize()
+    ms = time_events(lambda i: prob.attention_step(save=False, lse=False), iters)
+    nbytes = decode_algorithmic_bytes(layout)
+    out = {"workload": layout.spec.name, "kv_tokens": layout.total_tokens,
+           "ms": round(ms, 4), "kv_read_GBps": round(kv_bytes(layout) / ms / 1e6, 1),
+           "algorithmic_GBps": round(nbytes / ms / 1e6, 1),
+           "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del prob
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_extend(iters: int):
+    import torch
+    import workloads
+    from tests.gpu_problem import GpuProblem
+    layout = workloads.make_layout(workloads.CONFIGS[4])
+    prob = GpuProblem(layout)
+    prob.attention_step(save=True)
+    torch.cuda.synchronize()
+    ms = time_events(lambda i: prob.attention_step(save=False, lse=False), iters)
+    fl = extend_flops(layout)
+    tf = fl / ms / 1e9
+    out = {"workload": layout.spec.name, "q_tokens": layout.num_q_tokens,
+           "kv_tokens": layout.total_tokens, "gflop": round(fl / 1e9, 2), "ms": round(ms, 4),
+           "TFLOPs": round(tf, 1), "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
+           "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+    del prob
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the extend / other decode figures")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path here is "
+              "a single-GPU kernel library and no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import paged_kv_attention_02_amd as pka
+    from tests.gpu_problem import GpuProblem
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pka.lib()  # fail loudly if the library is missing
+
+    spec = workloads.CONFIGS[2]
+    layout = workloads.make_layout(spec)
+    log(f"workload {spec.name}: B={layout.batch} tokens={layout.total_tokens} pages={layout.kv_pages}")
+    values = workloads.make_values(layout, device="cuda")
+    # two copies of the pools and metadata, used alternately, so the 256 MB
+    # Infinity Cache cannot serve one step's KV from the previous step
+    probs = [GpuProblem(layout, values), GpuProblem(layout, values)]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        probs[i % 2].step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        probs[i % 2].step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    kvb = kv_bytes(layout)
+    value = kvb / (ms_step * 1e-3) / 1e9
+    for p in probs:
+        assert p.md.status() == 0, "device status flags set"
+    log(f"step {ms_step:.4f} ms -> {value:.1f} GB/s KV read")
+
+    # dominant kernel: the decode call (split kernel + merge) alone, HIP events
+    ms_attn = time_events(lambda i: probs[i % 2].attention_step(save=False, lse=False), args.steps)
+    ms_meta = time_events(lambda i: probs[i % 2].metadata_step(), args.steps)
+    nbytes = decode_algorithmic_bytes(layout)
+    achieved = nbytes / (ms_attn * 1e-3) / 1e9
+    src = source_hash("decode.hip")
+    roof = {"bound": "hbm", "kernel": "decode_mfma_kernel + decode_merge_kernel (one attn_decode call)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles("decode_llama3_8b", src),
+            "bytes_per_launch": nbytes, "ms_per_launch": round(ms_attn, 4),
+            "source_hash": src}
+    log(f"attn_decode {ms_attn:.4f} ms -> {achieved:.1f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); "
+        f"metadata {ms_meta:.4f} ms")
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "batch": layout.batch, "num_q_heads": spec.num_q_heads,
+                   "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+                   "page_size": spec.page_size, "kv_tokens": layout.total_tokens,
+                   "kv_bytes_per_step": kvb, "seed": spec.seed,
+                   "step": "init_metadata + save_kv + attn_decode",
+                   "metadata_ms": round(ms_meta, 4)},
+        "roofline": roof,
+    }
+    del probs
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        result["extend"] = bench_extend(args.steps)
+        log(f"extend: {result['extend']}")
+        result["decode_configs"] = {}
+        for cid in (3, 5):
+            result["decode_configs"][str(cid)] = bench_decode_kernel(cid, args.steps)
+            log(f"decode config {cid}: {result['decode_configs'][str(cid)]}")
+
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host cores ...")
+        result["cpu_baseline"] = cpu_baseline(layout, values, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
