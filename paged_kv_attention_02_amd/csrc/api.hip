@@ -48,8 +48,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t elem_bytes(pka_dtype t) { return t == PKA_F32 ? 4 : t == PKA_BF16 ? 2 : 1; }
 
-// Decode workgroups: a few per compute unit (waves per CU ~ 16), capped by
-// the plan's capacity.  Queried once per context on first use.
+// Decode workgroups: exactly one resident round (every workgroup on the
+// device at once, so the equal token shares finish together), from the
+// device's CU count and the kernel's occupancy.  Queried once per context.
 pka_status decode_wgs(const pka_ctx* ctx, int32_t* out) {
     int32_t v = ctx->nwg.load(std::memory_order_relaxed);
     if (v <= 0) {
@@ -57,7 +58,8 @@ pka_status decode_wgs(const pka_ctx* ctx, int32_t* out) {
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_fail(e, "querying the device");
-        const int per_cu = std::max(1, 16 / ctx->wpb);
+        int per_cu = pka::decode_blocks_per_cu(ctx->cfg.kv_dtype, ctx->cfg.head_dim, ctx->wpb);
+        if (per_cu < 1) per_cu = 1;
         v = std::min<int32_t>(pka::DEC_MAX_WG, std::max(1, cus * per_cu));
         const_cast<pka_ctx*>(ctx)->nwg.store(v, std::memory_order_relaxed);
     }
@@ -248,6 +250,8 @@ pka_status pka_init_metadata(const pka_ctx* ctx, const int32_t* seq_lens,
     a.nwg = nwg;
     a.ext_tq = ctx->ext_tq;
     a.is_decode = md->mode == PKA_MODE_DECODE;
+    a.fuse_gather = md->batch <= pka::FUSE_MAX_B && md->max_kv_pages <= pka::FUSE_MAX_ITEMS &&
+                    md->num_q_tokens <= pka::FUSE_MAX_ITEMS;
     a.kv_indptr = md->kv_indptr;
     a.kv_indices = md->kv_indices;
     a.kv_last_page_len = md->kv_last_page_len;

@@ -82,15 +82,148 @@ __device__ inline void emit_rows(const f32x4_t (&O)[D / 16], float inv, int j, E
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
-    constexpr int ESZ = FP8 ? 1 : 2;       // cache bytes per element
-    constexpr int KE = 16 / ESZ;           // elements per 16-byte K load
-    constexpr int NKL = D * ESZ / 64;      // 16-byte K loads per lane per 16 tokens
-    constexpr int KSTEPS = D / 32;         // MFMA k-steps of q.k
-    constexpr int SPL = KE / 8;            // k-steps per K load
-    constexpr int CPL = D / 16;            // V dims per lane per token = PV MFMAs
+struct DecodeShape {
+    static constexpr int ESZ = FP8 ? 1 : 2;   // cache bytes per element
+    static constexpr int KE = 16 / ESZ;       // elements per 16-byte K load
+    static constexpr int NKL = D * ESZ / 64;  // 16-byte K loads per lane per 16 tokens
+    static constexpr int KSTEPS = D / 32;     // MFMA k-steps of q.k
+    static constexpr int SPL = KE / 8;        // k-steps per K load
+    static constexpr int CPL = D / 16;        // V dims per lane per token = PV MFMAs
     static_assert(NKL * SPL == KSTEPS, "k-step bookkeeping");
+    using vrow_t = typename std::conditional<
+        CPL * ESZ == 16, u32x4_t,
+        typename std::conditional<CPL * ESZ == 8, u32x2_t, uint32_t>::type>::type;
+};
 
+// One 32-token tile of K and V in registers.  Row block sb of K holds tile
+// tokens 16*sb + n (lane n = lane & 15); V k-slot q of lane group j holds
+// tile token 16*(q/4) + 4*j + q%4, the order in which the scores come out of
+// the first MFMA, so P^T needs no shuffle.
+template <int D, bool FP8>
+struct KVTile {
+    using S = DecodeShape<D, FP8>;
+    u32x4_t kr[2][S::NKL];
+    typename S::vrow_t vr[8];
+};
+
+// Issue the loads of one tile.  `slot` is the pool slot of tile token
+// (lane & 31); lanes exchange slots with cross-lane moves.  The cache is
+// read once per call, so the loads carry the non-temporal hint.
+template <int D, bool FP8>
+__device__ inline void load_tile(KVTile<D, FP8>& T, int32_t slot, const uint8_t* kbase,
+                                 const uint8_t* vbase, int64_t row_bytes, int n, int j) {
+    using S = DecodeShape<D, FP8>;
+    const int32_t slot_x = __shfl_xor(slot, 16);
+    const int32_t ks0 = (j & 1) ? slot_x : slot;
+    const int32_t ks1 = (j & 1) ? slot : slot_x;
+    #pragma unroll
+    for (int s = 0; s < S::NKL; ++s) {
+        T.kr[0][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks0 * row_bytes + s * 64 + j * 16));
+        T.kr[1][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks1 * row_bytes + s * 64 + j * 16));
+    }
+    #pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int32_t vs = __shfl(slot, 16 * (q >> 2) + 4 * j + (q & 3));
+        T.vr[q] = __builtin_nontemporal_load(
+            (const typename S::vrow_t*)(vbase + vs * row_bytes + n * (S::CPL * S::ESZ)));
+    }
+}
+
+// Scores, online-softmax update and P.V for one tile whose first `valid`
+// tokens are real (the rest are masked out).
+template <int D, bool FP8>
+__device__ inline void compute_tile(const KVTile<D, FP8>& T, const bf16x8_t* qop,
+                                    f32x4_t* O, float& m2, float& lsum, int valid,
+                                    float scale_log2, int j) {
+    using S = DecodeShape<D, FP8>;
+    // S^T = K . Q^T, two 16-token row blocks
+    f32x4_t st[2];
+    #pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int ks = 0; ks < S::KSTEPS; ++ks) {
+            u32x4_t kw;
+            if constexpr (FP8) {
+                const u32x4_t raw = T.kr[sb][ks / S::SPL];
+                const uint32_t w0 = (ks % S::SPL) ? raw.z : raw.x;
+                const uint32_t w1 = (ks % S::SPL) ? raw.w : raw.y;
+                kw = u32x4_t{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+                             fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
+            } else {
+                kw = T.kr[sb][ks];
+            }
+            st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[ks], st[sb], 0, 0, 0);
+        }
+    }
+    // online softmax (log2 domain); lane (n, j) holds head n, tile tokens
+    // 16*sb + 4*j + r
+    float p[8];
+    float mx = -INFINITY;
+    #pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+        #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = 16 * sb + 4 * j + r < valid ? st[sb][r] * scale_log2 : -INFINITY;
+            p[sb * 4 + r] = v;
+            mx = fmaxf(mx, v);
+        }
+    mx = wave_max_xor_16_32(mx);
+    const float mnew = fmaxf(m2, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+    m2 = mnew;
+    float psum = 0.f;
+    #pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(p[i] - mnew);
+        psum += p[i];
+    }
+    lsum = lsum * alpha + psum;
+    #pragma unroll
+    for (int c = 0; c < S::CPL; ++c) O[c] *= alpha;
+    const u32x4_t pw = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                        pack_bf16(p[6], p[7])};
+    const bf16x8_t pop = as_bf16x8(pw);
+
+    // O^T += V^T . P^T, one MFMA per d-row block c (d = CPL*m + c)
+    if constexpr (!FP8) {
+        #pragma unroll
+        for (int c = 0; c < S::CPL; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t av;
+            #pragma unroll
+            for (int u = 0; u < 4; ++u)
+                av[u] = __builtin_amdgcn_perm(T.vr[2 * u + 1][c >> 1], T.vr[2 * u][c >> 1], sel);
+            O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
+        }
+    } else {
+        #pragma unroll
+        for (int c = 0; c < S::CPL; c += 2) {
+            const uint32_t sel = ((c & 3) == 0) ? 0x05010400u : 0x07030602u;
+            u32x4_t a0, a1;
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t lo_w, hi_w;
+                if constexpr (S::CPL == 8) {
+                    lo_w = T.vr[2 * u][c >> 2];
+                    hi_w = T.vr[2 * u + 1][c >> 2];
+                } else {
+                    lo_w = T.vr[2 * u];
+                    hi_w = T.vr[2 * u + 1];
+                }
+                const uint32_t x = __builtin_amdgcn_perm(hi_w, lo_w, sel);
+                a0[u] = fp8x2_to_bf16x2<false>(x);
+                a1[u] = fp8x2_to_bf16x2<true>(x);
+            }
+            O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), pop, O[c], 0, 0, 0);
+            O[c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), pop, O[c + 1], 0, 0, 0);
+        }
+    }
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
+    using S = DecodeShape<D, FP8>;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, j = lane >> 4;
     const int wpb = blockDim.x >> 6;
@@ -112,9 +245,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const int32_t* F = plan + plan_seg_prefix(a.B);
     int32_t seg = plan[plan_wg_seg(a.B) + w];
 
-    const int64_t row_bytes = (int64_t)a.Hkv * D * ESZ;  // one pool slot, all KV heads
-    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * D * ESZ;
-    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * D * ESZ;
+    const int64_t row_bytes = (int64_t)a.Hkv * D * S::ESZ;  // one pool slot, all KV heads
+    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * D * S::ESZ;
+    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * D * S::ESZ;
     const int tok = lane & 31;  // tile token whose slot this lane looks up
 
     for (; seg < a.B; ++seg) {
@@ -126,148 +259,49 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
         const int32_t b = seg;
         const int32_t page_base = a.kv_indptr[b];
         const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);  // the request's query row
+        // slot of tile token `tok` of the tile starting at position t0; positions
+        // past the piece repeat its last token (cached, never counted)
+        auto slot_at = [&](int32_t t0) {
+            const int32_t pos = t0 + tok;
+            return slot_of(a, page_base, pos < hi ? pos : hi - 1);
+        };
+
+        KVTile<D, FP8> A, Bt;
+        int32_t slot_a = slot_at(lo);
+        int32_t slot_b = slot_at(lo + DEC_TILE);
+        load_tile(A, slot_a, kbase, vbase, row_bytes, n, j);
 
         // Q^T operand: lane (n, j) holds head h0+n at the dims its K lanes load.
-        bf16x8_t qop[KSTEPS];
+        bf16x8_t qop[S::KSTEPS];
         {
             const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + h0 + n) * D;
             #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const int d0 = (ks / SPL) * 4 * KE + j * KE + (ks % SPL) * 8;
+            for (int ks = 0; ks < S::KSTEPS; ++ks) {
+                const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
                 u32x4_t v = {0u, 0u, 0u, 0u};
                 if (n < nh) v = *(const u32x4_t*)(qrow + d0);
                 qop[ks] = as_bf16x8(v);
             }
         }
 
-        f32x4_t O[CPL];
+        f32x4_t O[S::CPL];
         #pragma unroll
-        for (int c = 0; c < CPL; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < S::CPL; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         float m2 = -INFINITY, lsum = 0.f;
 
-        int32_t slot_cur = slot_of(a, page_base, lo + tok < hi ? lo + tok : lo);
-        for (int32_t t0 = lo; t0 < hi; t0 += DEC_TILE) {
-            // next tile's slot: issued now, used next iteration
-            const int32_t pn = t0 + DEC_TILE + tok;
-            const int32_t slot_next = slot_of(a, page_base, pn < hi ? pn : lo);
-
-            // K rows: row block sb holds tile tokens 16*sb + n
-            const int32_t slot_x = __shfl_xor(slot_cur, 16);
-            const int32_t ks0 = (j & 1) ? slot_x : slot_cur;
-            const int32_t ks1 = (j & 1) ? slot_cur : slot_x;
-            u32x4_t kr[2][NKL];
-            #pragma unroll
-            for (int s = 0; s < NKL; ++s) {
-                kr[0][s] = *(const u32x4_t*)(kbase + ks0 * row_bytes + s * 64 + j * 16);
-                kr[1][s] = *(const u32x4_t*)(kbase + ks1 * row_bytes + s * 64 + j * 16);
-            }
-            // V rows: k-slot q of lane group j is tile token 16*(q/4) + 4*j + q%4
-            typedef typename std::conditional<CPL * ESZ == 16, u32x4_t,
-                    typename std::conditional<CPL * ESZ == 8, u32x2_t, uint32_t>::type>::type vrow_t;
-            vrow_t vr[8];
-            #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int32_t vs = __shfl(slot_cur, 16 * (q >> 2) + 4 * j + (q & 3));
-                vr[q] = *(const vrow_t*)(vbase + vs * row_bytes + n * (CPL * ESZ));
-            }
-
-            // S^T = K . Q^T, two 16-token row blocks
-            f32x4_t S[2];
-            #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                S[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                #pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    u32x4_t kw;
-                    if constexpr (FP8) {
-                        const u32x4_t raw = kr[sb][ks / SPL];
-                        const uint32_t w0 = (ks % SPL) ? raw.z : raw.x;
-                        const uint32_t w1 = (ks % SPL) ? raw.w : raw.y;
-                        kw = u32x4_t{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
-                                     fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
-                    } else {
-                        kw = kr[sb][ks];
-                    }
-                    S[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[ks], S[sb],
-                                                                    0, 0, 0);
-                }
-            }
-
-            // online softmax (log2 domain); lane (n, j) holds head n, tokens
-            // 16*sb + 4*j + r of this tile
-            float s[8];
-            float mx = -INFINITY;
-            #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-                #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool valid = t0 + 16 * sb + 4 * j + r < hi;
-                    const float v = valid ? S[sb][r] * a.scale_log2 : -INFINITY;
-                    s[sb * 4 + r] = v;
-                    mx = fmaxf(mx, v);
-                }
-            mx = wave_max_xor_16_32(mx);
-            const float mnew = fmaxf(m2, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-            m2 = mnew;
-            float psum = 0.f;
-            #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                s[i] = __builtin_amdgcn_exp2f(s[i] - mnew);
-                psum += s[i];
-            }
-            lsum = lsum * alpha + psum;
-            #pragma unroll
-            for (int c = 0; c < CPL; ++c) O[c] *= alpha;
-            const u32x4_t pw = {pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3]),
-                                pack_bf16(s[4], s[5]), pack_bf16(s[6], s[7])};
-            const bf16x8_t pop = as_bf16x8(pw);
-
-            // O^T += V^T . P^T, one MFMA per d-row block c (d = CPL*m + c)
-            if constexpr (!FP8) {
-                #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-                    u32x4_t av;
-                    #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        uint32_t lo_w, hi_w;
-                        if constexpr (CPL == 8) {
-                            lo_w = vr[2 * u][c >> 1];
-                            hi_w = vr[2 * u + 1][c >> 1];
-                        } else {
-                            lo_w = vr[2 * u][c >> 1];
-                            hi_w = vr[2 * u + 1][c >> 1];
-                        }
-                        av[u] = __builtin_amdgcn_perm(hi_w, lo_w, sel);
-                    }
-                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
-                }
-            } else {
-                #pragma unroll
-                for (int c = 0; c < CPL; c += 2) {
-                    const uint32_t sel = ((c & 3) == 0) ? 0x05010400u : 0x07030602u;
-                    u32x4_t a0, a1;
-                    #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        uint32_t lo_w, hi_w;
-                        if constexpr (CPL == 8) {
-                            lo_w = vr[2 * u][c >> 2];
-                            hi_w = vr[2 * u + 1][c >> 2];
-                        } else {
-                            lo_w = vr[2 * u];
-                            hi_w = vr[2 * u + 1];
-                        }
-                        const uint32_t x = __builtin_amdgcn_perm(hi_w, lo_w, sel);
-                        a0[u] = fp8x2_to_bf16x2<false>(x);
-                        a1[u] = fp8x2_to_bf16x2<true>(x);
-                    }
-                    O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), pop, O[c], 0, 0, 0);
-                    O[c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), pop, O[c + 1],
-                                                                       0, 0, 0);
-                }
-            }
-            slot_cur = slot_next;
+        // Two tiles in flight: while one tile is consumed the next one's
+        // loads are outstanding.  Loads are issued unconditionally (past the
+        // end they re-read the piece's last row) so the wait counts are the
+        // same on every iteration.
+        for (int32_t t0 = lo;; t0 += 2 * DEC_TILE) {
+            load_tile(Bt, slot_b, kbase, vbase, row_bytes, n, j);
+            slot_a = slot_at(t0 + 2 * DEC_TILE);
+            compute_tile<D, FP8>(A, qop, O, m2, lsum, hi - t0, a.scale_log2, j);
+            if (t0 + DEC_TILE >= hi) break;
+            load_tile(A, slot_a, kbase, vbase, row_bytes, n, j);
+            slot_b = slot_at(t0 + 3 * DEC_TILE);
+            compute_tile<D, FP8>(Bt, qop, O, m2, lsum, hi - t0 - DEC_TILE, a.scale_log2, j);
+            if (t0 + 2 * DEC_TILE >= hi) break;
         }
 
         // finish: denominator over the four lane groups of each head
@@ -280,7 +314,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
                 __bf16* orow = (__bf16*)a.out + ((int64_t)qr * a.Hq + h) * D;
                 emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
                     #pragma unroll
-                    for (int i = 0; i < 4 * CPL; i += 8) {
+                    for (int i = 0; i < 4 * S::CPL; i += 8) {
                         const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
                                             pack_bf16(v[i + 4], v[i + 5]),
                                             pack_bf16(v[i + 6], v[i + 7])};
@@ -293,7 +327,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
                 float* prow = a.ws_o + (ps * a.Hq + h) * D;
                 emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
                     #pragma unroll
-                    for (int i = 0; i < 4 * CPL; i += 4)
+                    for (int i = 0; i < 4 * S::CPL; i += 4)
                         *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
                 });
                 if (j == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
@@ -392,10 +426,13 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
 
 // Log-sum-exp merge of the partials of requests that were split across
 // workgroups: out = sum_c e^(lse_c - M) o_c / sum_c e^(lse_c - M) and
-// lse = M + ln(sum_c e^(lse_c - M)).  One wave per (request, head).
+// lse = M + ln(sum_c e^(lse_c - M)).  One wave per (request, head): lanes
+// first take one partial each (max and normaliser by wave reductions), then
+// lanes take head dims and sweep the partials with several loads in flight.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     constexpr int EPL = D / 64;
+    constexpr int UNROLL = 8;
     const int lane = threadIdx.x & 63;
     const int32_t b = blockIdx.x;
     const int32_t h = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -407,18 +444,40 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     if (f1 <= f0) return;
     const int64_t w0 = f0 / share, w1 = (f1 - 1) / share;
     if (w0 == w1) return;  // written directly by its only workgroup
+    const int32_t np = (int32_t)(w1 - w0 + 1);
+    const float* lse_col = a.ws_lse + (b + w0) * a.Hq + h;  // stride Hq per partial
+    const float* o_col = a.ws_o + ((b + w0) * a.Hq + h) * D;  // stride Hq*D per partial
+    const int64_t ostride = (int64_t)a.Hq * D;
+
     float M = -INFINITY;
-    for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, a.ws_lse[(b + w) * a.Hq + h]);
+    for (int32_t k = lane; k < np; k += 64) M = fmaxf(M, lse_col[(int64_t)k * a.Hq]);
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float den = 0.f, acc[EPL];
     #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    for (int64_t w = w0; w <= w1; ++w) {
-        const float wt = expf(a.ws_lse[(b + w) * a.Hq + h] - M);
-        den += wt;
-        const float* prow = a.ws_o + ((b + w) * a.Hq + h) * D;
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += wt * prow[e * 64 + lane];
+    for (int32_t k0 = 0; k0 < np; k0 += 64) {
+        const int32_t k = k0 + lane;
+        const float wk = k < np ? expf(lse_col[(int64_t)k * a.Hq] - M) : 0.f;
+        den += wk;
+        const int32_t cnt = min(64, np - k0);
+        for (int32_t i = 0; i < cnt; i += UNROLL) {
+            float v[UNROLL][EPL], wt[UNROLL];
+            #pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int32_t kk = min(i + u, cnt - 1);
+                wt[u] = i + u < cnt ? __shfl(wk, kk) : 0.f;
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)(k0 + kk) * ostride + e * 64 + lane];
+            }
+            #pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[e] += wt[u] * v[u][e];
+        }
     }
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
     const float inv = 1.0f / den;
     const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
     #pragma unroll
@@ -453,7 +512,26 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
     return hipGetLastError();
 }
 
+template <int D>
+int blocks_per_cu_d(pka_dtype kv, int wpb) {
+    int n = 0;
+    hipError_t e;
+    if (kv == PKA_BF16)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, false>, 64 * wpb, 0);
+    else if (kv == PKA_FP8_E4M3FN)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, true>, 64 * wpb, 0);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<D>, 64 * wpb, 0);
+    return e == hipSuccess ? n : 0;
+}
+
 }  // namespace
+
+int decode_blocks_per_cu(pka_dtype kv, int D, int wpb) {
+    if (D == 128) return blocks_per_cu_d<128>(kv, wpb);
+    if (D == 64) return blocks_per_cu_d<64>(kv, wpb);
+    return 0;
+}
 
 hipError_t launch_decode(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, int wpb,
                          hipStream_t s) {

@@ -31,7 +31,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float LN2 = 0.69314718055994531f;
 constexpr int EXT_COLS = 128;  // query columns per workgroup (4 waves x 32)
-constexpr int KT = 32;         // keys per tile
+constexpr int KT = 32;         // keys per tile (one 32-key MFMA block; keeps two waves per SIMD)
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
     bf16x2_t v = {(__bf16)lo, (__bf16)hi};
@@ -50,7 +50,13 @@ __device__ inline int32_t slot_of(const AttnArgs& a, int32_t page_base, int32_t 
 // row of the 32x32 MFMA accumulator held by register r of lane half hh
 __device__ constexpr int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-template <int D>
+// Online-softmax state of one query column (two lanes per column).  The
+// running max is raised lazily: only when a tile's max exceeds it by more
+// than LAZY (log2 units) are O and the normaliser rescaled, so most tiles
+// skip the rescale; p = 2^(s*c - m) then stays below 2^LAZY.
+constexpr float LAZY = 8.0f;
+
+template <int D, bool POS>
 __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
     constexpr int ROWB = D * 2;              // bytes of one K/V row of one head
     constexpr int STRIDE = ROWB + 16;        // LDS row stride (padding against bank conflicts)
@@ -59,6 +65,7 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
     constexpr int PASSES = KT / RPP;         // passes per tile and tensor
     constexpr int KSTEPS = D / 16;           // k-steps of q.k (32x32x16)
     constexpr int VC = D / 32;               // d-row blocks of O^T (d = VC*m + c)
+    constexpr int SUB = KT / 32;             // 32-key sub-tiles per tile
     __shared__ __attribute__((aligned(16))) uint8_t sK[2][KT * STRIDE];
     __shared__ __attribute__((aligned(16))) uint8_t sV[2][KT * STRIDE];
 
@@ -87,6 +94,7 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
     const int32_t qtok = col_ok ? ctok : tok_lo;  // invalid columns mirror a valid one
     const int32_t head = g * a.G + col % a.G;
     const int32_t qpos = pb + qtok;
+    const int32_t qpos_min = pb + tok_lo;  // tiles wholly at or below it need no mask
 
     // Q^T operand: k-step s covers dims 16 s + 8 hh .. + 8
     bf16x8_t qop[KSTEPS];
@@ -130,6 +138,9 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
         #pragma unroll
         for (int r = 0; r < 16; ++r) O[c][r] = 0.f;
     float m2 = -INFINITY, lsum = 0.f;
+    // POS: scores are scaled by c > 0 inside one FMA, so the max is taken on
+    // raw scores; otherwise the scaled scores are formed first.
+    const float c2 = a.scale_log2;
 
     load_tile(0);
     store_tile(0);
@@ -139,49 +150,67 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
         const int32_t kt0 = t * KT;
         if (t + 1 < ntiles) load_tile(kt0 + KT);
 
-        // S^T = K . Q^T
-        f32x16_t S;
+        // S^T = K . Q^T for each 32-key sub-tile
+        f32x16_t S[SUB];
         #pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = 0.f;
-        const uint8_t* krow = &sK[buf][n * STRIDE + 16 * hh];
-        #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-            const u32x4_t kw = *(const u32x4_t*)(krow + 32 * s);
-            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), qop[s], S, 0, 0, 0);
+        for (int u = 0; u < SUB; ++u) {
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) S[u][r] = 0.f;
+            const uint8_t* krow = &sK[buf][(32 * u + n) * STRIDE + 16 * hh];
+            #pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const u32x4_t kw = *(const u32x4_t*)(krow + 32 * s);
+                S[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), qop[s], S[u], 0, 0, 0);
+            }
         }
 
-        // causal mask and online softmax for column n (log2 domain)
+        // causal mask only where the tile crosses the diagonal of some column
+        if (kt0 + KT - 1 > qpos_min) {
+            #pragma unroll
+            for (int u = 0; u < SUB; ++u)
+                #pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kt0 + 32 * u + acc_row(r, hh) > qpos) S[u][r] = -INFINITY;
+        }
+        if constexpr (!POS) {
+            #pragma unroll
+            for (int u = 0; u < SUB; ++u)
+                #pragma unroll
+                for (int r = 0; r < 16; ++r) S[u][r] = S[u][r] == -INFINITY ? -INFINITY : S[u][r] * c2;
+        }
         float mx = -INFINITY;
         #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int32_t kp = kt0 + acc_row(r, hh);
-            const float v = kp <= qpos ? S[r] * a.scale_log2 : -INFINITY;
-            S[r] = v;
-            mx = fmaxf(mx, v);
-        }
+        for (int u = 0; u < SUB; ++u)
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[u][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m2, mx);
-        // a column can have no valid key in this tile only after it had some
-        // before (tiles start at key 0), so mnew is finite
-        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-        m2 = mnew;
-        float psum = 0.f;
-        #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            S[r] = __builtin_amdgcn_exp2f(S[r] - mnew);
-            psum += S[r];
+        const float mc = POS ? mx * c2 : mx;  // candidate max, log2 units
+        if (__any(mc > m2 + LAZY)) {
+            const float mnew = fmaxf(m2, mc);
+            const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+            m2 = mnew;
+            lsum *= alpha;
+            #pragma unroll
+            for (int c = 0; c < VC; ++c) O[c] *= alpha;
         }
-        lsum = lsum * alpha + psum;
+        // a column has a valid key in every tile up to its own position, and
+        // tiles start at key 0, so m2 is finite from the first tile on
         #pragma unroll
-        for (int c = 0; c < VC; ++c) O[c] *= alpha;
+        for (int u = 0; u < SUB; ++u)
+            #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = POS ? __builtin_fmaf(S[u][r], c2, -m2) : S[u][r] - m2;
+                S[u][r] = __builtin_amdgcn_exp2f(e);
+                lsum += S[u][r];
+            }
 
-        // O^T += V^T . P^T in two k-steps of 16 keys
+        // O^T += V^T . P^T in k-steps of 16 keys
         #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const u32x4_t pw = {pack_bf16(S[8 * ks + 0], S[8 * ks + 1]),
-                                pack_bf16(S[8 * ks + 2], S[8 * ks + 3]),
-                                pack_bf16(S[8 * ks + 4], S[8 * ks + 5]),
-                                pack_bf16(S[8 * ks + 6], S[8 * ks + 7])};
+        for (int ks = 0; ks < 2 * SUB; ++ks) {
+            const f32x16_t& P = S[ks >> 1];
+            const int r0 = 8 * (ks & 1);
+            const u32x4_t pw = {pack_bf16(P[r0 + 0], P[r0 + 1]), pack_bf16(P[r0 + 2], P[r0 + 3]),
+                                pack_bf16(P[r0 + 4], P[r0 + 5]), pack_bf16(P[r0 + 6], P[r0 + 7])};
             const bf16x8_t pop = as_bf16x8(pw);
             // key of B-operand slot e (lane half hh): 16 ks + 8 (e/4) + 4 hh + e%4
             typedef typename std::conditional<VC == 4, u32x2_t, uint32_t>::type vrow_t;
@@ -196,16 +225,16 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
                 const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 u32x4_t av;
                 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int w = 0; w < 4; ++w) {
                     uint32_t lo_w, hi_w;
                     if constexpr (VC == 4) {
-                        lo_w = R[2 * u][c >> 1];
-                        hi_w = R[2 * u + 1][c >> 1];
+                        lo_w = R[2 * w][c >> 1];
+                        hi_w = R[2 * w + 1][c >> 1];
                     } else {
-                        lo_w = R[2 * u];
-                        hi_w = R[2 * u + 1];
+                        lo_w = R[2 * w];
+                        hi_w = R[2 * w + 1];
                     }
-                    av[u] = __builtin_amdgcn_perm(hi_w, lo_w, sel);
+                    av[w] = __builtin_amdgcn_perm(hi_w, lo_w, sel);
                 }
                 O[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
             }
@@ -308,8 +337,14 @@ hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hi
         else hipLaunchKernelGGL((extend_f32_kernel<64>), grid, dim3(256), 0, s, a);
     } else {
         const dim3 grid((unsigned)items, a.Hkv);
-        if (D == 128) hipLaunchKernelGGL((extend_mfma_kernel<128>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((extend_mfma_kernel<64>), grid, dim3(256), 0, s, a);
+        const bool pos = a.scale_log2 > 0.f;
+        if (D == 128) {
+            if (pos) hipLaunchKernelGGL((extend_mfma_kernel<128, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((extend_mfma_kernel<128, false>), grid, dim3(256), 0, s, a);
+        } else {
+            if (pos) hipLaunchKernelGGL((extend_mfma_kernel<64, true>), grid, dim3(256), 0, s, a);
+            else hipLaunchKernelGGL((extend_mfma_kernel<64, false>), grid, dim3(256), 0, s, a);
+        }
     }
     return hipGetLastError();
 }

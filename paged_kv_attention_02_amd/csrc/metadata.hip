@@ -18,42 +18,54 @@ namespace {
 
 constexpr int SCAN_THREADS = 1024;
 
-// Inclusive block scan of three int64 values (Hillis-Steele in LDS).
+// Inclusive block scan of three int64 values: a shuffle scan inside each
+// wave, then the wave totals (two barriers in all).
 __device__ inline void block_scan3(int64_t& x0, int64_t& x1, int64_t& x2, int64_t* sh) {
-    const int t = threadIdx.x;
-    sh[t] = x0;
-    sh[SCAN_THREADS + t] = x1;
-    sh[2 * SCAN_THREADS + t] = x2;
-    __syncthreads();
-    for (int off = 1; off < SCAN_THREADS; off <<= 1) {
-        int64_t a0 = 0, a1 = 0, a2 = 0;
-        if (t >= off) {
-            a0 = sh[t - off];
-            a1 = sh[SCAN_THREADS + t - off];
-            a2 = sh[2 * SCAN_THREADS + t - off];
+    constexpr int NW = SCAN_THREADS / 64;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    #pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y0 = __shfl_up(x0, off), y1 = __shfl_up(x1, off), y2 = __shfl_up(x2, off);
+        if (lane >= off) {
+            x0 += y0;
+            x1 += y1;
+            x2 += y2;
         }
-        __syncthreads();
-        sh[t] += a0;
-        sh[SCAN_THREADS + t] += a1;
-        sh[2 * SCAN_THREADS + t] += a2;
-        __syncthreads();
     }
-    x0 = sh[t];
-    x1 = sh[SCAN_THREADS + t];
-    x2 = sh[2 * SCAN_THREADS + t];
+    if (lane == 63) {
+        sh[wv] = x0;
+        sh[NW + wv] = x1;
+        sh[2 * NW + wv] = x2;
+    }
+    __syncthreads();
+    int64_t p0 = 0, p1 = 0, p2 = 0;
+    for (int k = 0; k < wv; ++k) {
+        p0 += sh[k];
+        p1 += sh[NW + k];
+        p2 += sh[2 * NW + k];
+    }
+    x0 += p0;
+    x1 += p1;
+    x2 += p2;
     __syncthreads();
 }
 
 __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
-    __shared__ int64_t sh[3 * SCAN_THREADS];
+    __shared__ int64_t sh[3 * SCAN_THREADS];  // scan scratch, then sorted extend items
     __shared__ int64_t carry[3];
     __shared__ int32_t s_status;
+    // per-request prefixes kept in LDS when the gather is fused (B <= FUSE_MAX_B)
+    __shared__ int32_t sP[FUSE_MAX_B + 1], sQ[FUSE_MAX_B + 1], sF[FUSE_MAX_B + 1],
+        sLen[FUSE_MAX_B];
     const int t = threadIdx.x;
     const int32_t P = 1 << a.page_shift;
     int32_t* F = a.plan + plan_seg_prefix(a.B);
     if (t == 0) {
         carry[0] = carry[1] = carry[2] = 0;
         s_status = 0;
+        sP[0] = 0;
+        sQ[0] = 0;
+        sF[0] = 0;
         a.kv_indptr[0] = 0;
         a.qo_indptr[0] = 0;
         F[0] = 0;
@@ -86,6 +98,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             a.qo_indptr[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
             F[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
             a.kv_last_page_len[b] = (int32_t)(L - ((pages - 1) << a.page_shift));
+            if (a.B <= FUSE_MAX_B) {
+                sP[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
+                sQ[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
+                sF[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
+                sLen[b] = (int32_t)L;
+            }
         }
         __syncthreads();
         if (t == SCAN_THREADS - 1) {
@@ -94,6 +112,68 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             carry[2] += iL;
         }
         __syncthreads();
+    }
+    __syncthreads();
+    if (a.fuse_gather) {
+        // kv_indices[i] and out_cache_loc[j]: find the request by binary search
+        // over the LDS prefixes (largest b with prefix[b] <= i).
+        auto find = [&](const int32_t* pre, int32_t i) {
+            int32_t lo = 0, hi = a.B - 1;
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) >> 1;
+                if (pre[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            return lo;
+        };
+        // FUSE_MAX_ITEMS / SCAN_THREADS independent lookups per thread, all in flight
+        constexpr int U = (int)(FUSE_MAX_ITEMS / SCAN_THREADS);
+        const int32_t npages = (int32_t)min((int64_t)sP[a.B], a.max_kv_pages);
+        for (int32_t i0 = t; i0 < npages; i0 += U * SCAN_THREADS) {
+            int32_t pg[U];
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t i = i0 + u * SCAN_THREADS;
+                if (i < npages) {
+                    const int32_t b = find(sP, i);
+                    pg[u] = a.page_table[(int64_t)b * a.pt_stride + (i - sP[b])];
+                }
+            }
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t i = i0 + u * SCAN_THREADS;
+                if (i < npages) {
+                    if (pg[u] < 0 || pg[u] >= a.num_pages) {
+                        flags |= PKA_DEV_BAD_PAGE;
+                        pg[u] = min(max(pg[u], 0), a.num_pages - 1);
+                    }
+                    a.kv_indices[i] = pg[u];
+                }
+            }
+        }
+        const int32_t nnew = min(sQ[a.B], a.N);
+        for (int32_t i0 = t; i0 < nnew; i0 += U * SCAN_THREADS) {
+            int32_t pg[U], pos[U];
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t i = i0 + u * SCAN_THREADS;
+                if (i < nnew) {
+                    const int32_t b = find(sQ, i);
+                    pos[u] = sLen[b] - (sQ[b + 1] - sQ[b]) + (i - sQ[b]);
+                    pg[u] = a.page_table[(int64_t)b * a.pt_stride + (pos[u] >> a.page_shift)];
+                }
+            }
+            #pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int32_t i = i0 + u * SCAN_THREADS;
+                if (i < nnew) {
+                    if (pg[u] < 0 || pg[u] >= a.num_pages) {
+                        flags |= PKA_DEV_BAD_PAGE;
+                        pg[u] = min(max(pg[u], 0), a.num_pages - 1);
+                    }
+                    a.out_cache_loc[i] = (pg[u] << a.page_shift) | (pos[u] & (P - 1));
+                }
+            }
+        }
     }
     if (flags) atomicOr(&s_status, flags);
     __syncthreads();
@@ -113,10 +193,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             const int64_t pos = (int64_t)w * share;
             int32_t seg = a.B;
             if (pos < W) {
+                const int32_t* Fs = a.B <= FUSE_MAX_B ? sF : F;
                 int32_t lo = 0, hi = a.B - 1;  // largest b with F[b] <= pos
                 while (lo < hi) {
                     const int32_t mid = (lo + hi + 1) >> 1;
-                    if (F[mid] <= pos) lo = mid; else hi = mid - 1;
+                    if (Fs[mid] <= pos) lo = mid; else hi = mid - 1;
                 }
                 seg = lo;
             }
@@ -249,7 +330,7 @@ __global__ __launch_bounds__(256) void md_gather_kernel(MetaArgs a) {
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(md_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.B == 0) return e;
+    if (e != hipSuccess || a.B == 0 || a.fuse_gather) return e;
     // enough blocks per request to cover its pages in one or two strides
     int64_t per_req = (a.max_kv_pages / a.B + 255) / 256;
     if (!a.is_decode) per_req = std::max<int64_t>(per_req, ((int64_t)a.N / a.B + 255) / 256);

@@ -20,6 +20,11 @@ enum : int32_t {
     PLAN_HDR = 16,
 };
 
+// Batches up to this size (and page / token counts below FUSE_MAX_ITEMS)
+// build all metadata in one launch.
+constexpr int FUSE_MAX_B = 1024;
+constexpr int64_t FUSE_MAX_ITEMS = 16384;
+
 // Tokens per decode tile (two MFMA row blocks of 16 tokens).
 constexpr int DEC_TILE = 32;
 // Smallest share of the flattened token range given to one workgroup.
@@ -56,6 +61,7 @@ struct MetaArgs {
     int32_t nwg;       // decode workgroups
     int32_t ext_tq;    // extend query tokens per item
     int32_t is_decode;
+    int32_t fuse_gather;  // B <= FUSE_MAX_B: md_scan also writes kv_indices / out_cache_loc
     int32_t* kv_indptr;
     int32_t* kv_indices;
     int32_t* kv_last_page_len;
@@ -110,6 +116,9 @@ hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, int D, const SaveArgs& a,
 hipError_t launch_decode(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, int waves_per_wg,
                          hipStream_t s);
 hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hipStream_t s);
+
+// Decode workgroups of `wpb` waves that fit on one compute unit at once.
+int decode_blocks_per_cu(pka_dtype kv, int D, int wpb);
 
 // Query tokens per extend item for a dtype pair.
 int extend_tq(pka_dtype q, pka_dtype kv, int D, int G);
