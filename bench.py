@@ -58,7 +58,9 @@ def extend_flops(layout) -> float:
 
 
 def source_hash(*names) -> str:
-    h = hashlib.sha256()
+    """Hash of kernel sources plus the build flags (what decides the code)."""
+    from paged_kv_attention_02_amd import build as pkb
+    h = hashlib.sha256(" ".join(pkb.HIPCC_FLAGS).encode())
     for n in names:
         with open(os.path.join(ROOT, "paged_kv_attention_02_amd", "csrc", n), "rb") as f:
             h.update(f.read())
@@ -160,6 +162,17 @@ def bench_extend(iters: int):
     return out
 
 
+def bench_copy(iters: int, nbytes: int = 1 << 30):
+    """A plain device copy of known size: the reference for scaling HBM
+    traffic counters (FETCH_SIZE / WRITE_SIZE) into bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    ms = time_events(lambda i: dst.copy_(src), iters)
+    return {"workload": "device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+            "ms": round(ms, 4), "GBps_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +181,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the extend / other decode figures")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--only", choices=["extend", "decode3", "decode5", "copy"], default=None,
+                    help="run one extra leg alone (for profiling) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the attention path here is "
@@ -182,6 +197,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pka.lib()  # fail loudly if the library is missing
+    if args.only:
+        if args.only == "copy":
+            res = bench_copy(args.steps)
+        elif args.only == "extend":
+            res = bench_extend(args.steps)
+        else:
+            res = bench_decode_kernel(int(args.only[-1]), args.steps)
+        print(json.dumps(res), flush=True)
+        return
 
     spec = workloads.CONFIGS[2]
     layout = workloads.make_layout(spec)
@@ -212,7 +236,7 @@ def main():
     ms_meta = time_events(lambda i: probs[i % 2].metadata_step(), args.steps)
     nbytes = decode_algorithmic_bytes(layout)
     achieved = nbytes / (ms_attn * 1e-3) / 1e9
-    src = source_hash("decode.hip")
+    src = source_hash("decode.hip", "pka_internal.h")
     roof = {"bound": "hbm", "kernel": "decode_mfma_kernel + decode_merge_kernel (one attn_decode call)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),

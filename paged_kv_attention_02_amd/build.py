@@ -23,6 +23,9 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no copies between the AGPR and
+    # VGPR files around the softmax (gfx950 reads both as MFMA operands)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-warning-option",
 ]
 
