@@ -373,9 +373,14 @@ pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_
 
 pka_status pka_read_status(const pka_batch* md, int32_t* status, void* stream) {
     if (!md || !status || !md->plan) return fail(PKA_ERR_INVALID_ARG, "null batch or status");
+    int32_t words[pka::PLAN_MDST + pka::MD_SLOTS];
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
-    if (e == hipSuccess) e = hipMemcpy(status, md->plan + pka::PLAN_STATUS, sizeof(int32_t), hipMemcpyDeviceToHost);
-    return e == hipSuccess ? PKA_OK : hip_fail(e, "reading the status word");
+    if (e == hipSuccess) e = hipMemcpy(words, md->plan, sizeof words, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "reading the status words");
+    int32_t v = words[pka::PLAN_STATUS];
+    for (int i = 0; i < pka::MD_SLOTS; ++i) v |= words[pka::PLAN_MDST + i];
+    *status = v;
+    return PKA_OK;
 }
 
 }  // extern "C"

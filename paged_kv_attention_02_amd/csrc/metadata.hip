@@ -58,6 +58,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
     __shared__ int32_t sP[FUSE_MAX_B + 1], sQ[FUSE_MAX_B + 1], sF[FUSE_MAX_B + 1],
         sLen[FUSE_MAX_B];
     const int t = threadIdx.x;
+    const int blk = blockIdx.x;  // > 0 only when the gather is fused: slices of it
+    const bool lead = blk == 0;  // the one workgroup that writes the CSR arrays and plan
     const int32_t P = 1 << a.page_shift;
     int32_t* F = a.plan + plan_seg_prefix(a.B);
     if (t == 0) {
@@ -66,9 +68,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         sP[0] = 0;
         sQ[0] = 0;
         sF[0] = 0;
-        a.kv_indptr[0] = 0;
-        a.qo_indptr[0] = 0;
-        F[0] = 0;
+        if (lead) {
+            a.kv_indptr[0] = 0;
+            a.qo_indptr[0] = 0;
+            F[0] = 0;
+        }
     }
     __syncthreads();
     int32_t flags = 0;
@@ -94,10 +98,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         if (b < a.B) {
             const int64_t cp = carry[0] + ip, cq = carry[1] + iq, cL = carry[2] + iL;
             if (cp > a.max_kv_pages || cq > a.N || cL > INT32_MAX) flags |= PKA_DEV_CAPACITY;
-            a.kv_indptr[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
-            a.qo_indptr[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
-            F[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
-            a.kv_last_page_len[b] = (int32_t)(L - ((pages - 1) << a.page_shift));
+            if (lead) {
+                a.kv_indptr[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
+                a.qo_indptr[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
+                F[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
+                a.kv_last_page_len[b] = (int32_t)(L - ((pages - 1) << a.page_shift));
+            }
             if (a.B <= FUSE_MAX_B) {
                 sP[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
                 sQ[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
@@ -125,15 +131,19 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             }
             return lo;
         };
-        // FUSE_MAX_ITEMS / SCAN_THREADS independent lookups per thread, all in flight
-        constexpr int U = (int)(FUSE_MAX_ITEMS / SCAN_THREADS);
+        // this workgroup's slice of the pages and of the new tokens, with
+        // FUSE_PER_THREAD independent lookups per thread in flight
+        constexpr int U = FUSE_PER_THREAD;
+        const int32_t nblk = gridDim.x;
         const int32_t npages = (int32_t)min((int64_t)sP[a.B], a.max_kv_pages);
-        for (int32_t i0 = t; i0 < npages; i0 += U * SCAN_THREADS) {
+        const int32_t pchunk = (npages + nblk - 1) / nblk;
+        const int32_t p_lo = blk * pchunk, p_hi = min(npages, p_lo + pchunk);
+        for (int32_t i0 = p_lo + t; i0 < p_hi; i0 += U * SCAN_THREADS) {
             int32_t pg[U];
             #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < npages) {
+                if (i < p_hi) {
                     const int32_t b = find(sP, i);
                     pg[u] = a.page_table[(int64_t)b * a.pt_stride + (i - sP[b])];
                 }
@@ -141,7 +151,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < npages) {
+                if (i < p_hi) {
                     if (pg[u] < 0 || pg[u] >= a.num_pages) {
                         flags |= PKA_DEV_BAD_PAGE;
                         pg[u] = min(max(pg[u], 0), a.num_pages - 1);
@@ -151,12 +161,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             }
         }
         const int32_t nnew = min(sQ[a.B], a.N);
-        for (int32_t i0 = t; i0 < nnew; i0 += U * SCAN_THREADS) {
+        const int32_t qchunk = (nnew + nblk - 1) / nblk;
+        const int32_t q_lo = blk * qchunk, q_hi = min(nnew, q_lo + qchunk);
+        for (int32_t i0 = q_lo + t; i0 < q_hi; i0 += U * SCAN_THREADS) {
             int32_t pg[U], pos[U];
             #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < nnew) {
+                if (i < q_hi) {
                     const int32_t b = find(sQ, i);
                     pos[u] = sLen[b] - (sQ[b + 1] - sQ[b]) + (i - sQ[b]);
                     pg[u] = a.page_table[(int64_t)b * a.pt_stride + (pos[u] >> a.page_shift)];
@@ -165,7 +177,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < nnew) {
+                if (i < q_hi) {
                     if (pg[u] < 0 || pg[u] >= a.num_pages) {
                         flags |= PKA_DEV_BAD_PAGE;
                         pg[u] = min(max(pg[u], 0), a.num_pages - 1);
@@ -179,6 +191,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
     __syncthreads();
     __threadfence_block();
 
+    if (!lead) {  // a gather slice: report its flags in its own status slot
+        if (flags) atomicOr(&s_status, flags);
+        __syncthreads();
+        if (t == 0) a.plan[PLAN_MDST + blk] = s_status;
+        return;
+    }
     const int64_t W = min(carry[2], (int64_t)INT32_MAX);
     {
         // Decode partition (built for every batch, so a verify batch can take
@@ -290,7 +308,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
     }
     if (flags) atomicOr(&s_status, flags);
     __syncthreads();
-    if (t == 0) a.plan[PLAN_STATUS] = s_status;
+    if (t == 0) {
+        a.plan[PLAN_MDST] = s_status;
+        a.plan[PLAN_STATUS] = 0;  // later kernels OR their flags into it
+    }
+    for (int i = (int)gridDim.x + t; i < MD_SLOTS; i += SCAN_THREADS) a.plan[PLAN_MDST + i] = 0;
 }
 
 // kv_indices and out_cache_loc.  Grid (x, B); page ids outside the pool are
@@ -328,7 +350,15 @@ __global__ __launch_bounds__(256) void md_gather_kernel(MetaArgs a) {
 }  // namespace
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(md_scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a);
+    // fused: enough workgroups that each thread has at most FUSE_PER_THREAD
+    // lookups of each kind
+    int nblk = 1;
+    if (a.fuse_gather) {
+        const int64_t items = std::max<int64_t>(a.max_kv_pages, a.N);
+        nblk = (int)std::min<int64_t>(MD_SLOTS, std::max<int64_t>(1, (items + SCAN_THREADS * FUSE_PER_THREAD - 1) /
+                                                                      (SCAN_THREADS * FUSE_PER_THREAD)));
+    }
+    hipLaunchKernelGGL(md_scan_kernel, dim3(nblk), dim3(SCAN_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.B == 0 || a.fuse_gather) return e;
     // enough blocks per request to cover its pages in one or two strides

@@ -11,19 +11,23 @@ namespace pka {
 // ----------------------------------------------------------------- plan --
 // Layout of the int32 `plan` array of a pka_batch.
 enum : int32_t {
-    PLAN_STATUS = 0,     // sticky PKA_DEV_* flags (device writes, host reads)
+    PLAN_STATUS = 0,     // sticky PKA_DEV_* flags of save_kv / attention (atomic OR)
     PLAN_SHARE = 1,      // decode: tokens of the flattened batch per workgroup
     PLAN_TOTAL = 2,      // decode: sum of L_b
     PLAN_NWG = 3,        // decode: workgroups the partition was made for
     PLAN_EXT_COUNT = 4,  // extend: number of (request, query tile) items
     PLAN_EXT_TQ = 5,     // extend: query tokens per item
-    PLAN_HDR = 16,
+    PLAN_MDST = 16,      // PKA_DEV_* flags of each metadata workgroup (MD_SLOTS words)
+    PLAN_HDR = 80,
 };
+constexpr int MD_SLOTS = 64;  // most metadata workgroups per launch
 
-// Batches up to this size (and page / token counts below FUSE_MAX_ITEMS)
-// build all metadata in one launch.
+// Batches up to this size (and page plus new-token counts up to
+// FUSE_MAX_ITEMS) build all metadata in one launch: every workgroup scans
+// the batch itself and gathers its slice of kv_indices / out_cache_loc.
 constexpr int FUSE_MAX_B = 1024;
-constexpr int64_t FUSE_MAX_ITEMS = 16384;
+constexpr int FUSE_PER_THREAD = 4;  // lookups in flight per thread
+constexpr int64_t FUSE_MAX_ITEMS = (int64_t)MD_SLOTS * 1024 * FUSE_PER_THREAD;
 
 // Tokens per decode tile (two MFMA row blocks of 16 tokens).
 constexpr int DEC_TILE = 32;
