@@ -134,6 +134,46 @@ pka_status check_attn(const pka_ctx* ctx, const pka_batch* md, const void* q, co
     return PKA_OK;
 }
 
+
+// Decode launch; with write_new the new tokens k_new / v_new are written by
+// the decode kernel itself (bf16 and fp8 caches).
+pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, const void* k_pool,
+                       const void* v_pool, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream, bool write_new, const void* k_new,
+                       const void* v_new) {
+    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
+    if (s != PKA_OK) return s;
+    if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
+    if (write_new && (!k_new || !v_new)) return fail(PKA_ERR_INVALID_ARG, "null K/V pointer");
+    if (write_new && (!aligned16(k_new) || !aligned16(v_new)))
+        return fail(PKA_ERR_INVALID_ARG, "K/V rows must be 16-byte aligned");
+    if (md->num_q_tokens != md->batch)
+        return fail(PKA_ERR_UNSUPPORTED, "the decode path takes one query per request (%d tokens, %d requests)",
+                    md->num_q_tokens, md->batch);
+    int32_t nwg = 0;
+    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+    const int64_t need = decode_ws_bytes(ctx, md->batch, nwg);
+    if (!workspace || (int64_t)workspace_bytes < need || !aligned16(workspace))
+        return fail(PKA_ERR_WORKSPACE, "decode needs %lld workspace bytes (16-byte aligned), got %zu",
+                    (long long)need, workspace_bytes);
+    pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
+    a.nwg = nwg;
+    a.ws_o = (float*)workspace;
+    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * ctx->cfg.num_q_heads * ctx->cfg.head_dim;
+    if (write_new) {
+        const pka_config& c = ctx->cfg;
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.out_cache_loc = md->out_cache_loc;
+        a.pool_slots = (int64_t)c.num_pages * c.page_size;
+        a.k_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f);
+        a.v_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f);
+    }
+    hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->cfg.head_dim, a,
+                                      ctx->wpb, (hipStream_t)stream);
+    return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,25 +331,8 @@ pka_status pka_save_kv(const pka_ctx* ctx, const pka_batch* md, const void* k_ne
 pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* q,
                            const void* k_pool, const void* v_pool, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
-    if (s != PKA_OK) return s;
-    if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
-    if (md->num_q_tokens != md->batch)
-        return fail(PKA_ERR_UNSUPPORTED, "the decode path takes one query per request (%d tokens, %d requests)",
-                    md->num_q_tokens, md->batch);
-    int32_t nwg = 0;
-    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
-    const int64_t need = decode_ws_bytes(ctx, md->batch, nwg);
-    if (!workspace || (int64_t)workspace_bytes < need || !aligned16(workspace))
-        return fail(PKA_ERR_WORKSPACE, "decode needs %lld workspace bytes (16-byte aligned), got %zu",
-                    (long long)need, workspace_bytes);
-    pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
-    a.nwg = nwg;
-    a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * ctx->cfg.num_q_heads * ctx->cfg.head_dim;
-    hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->cfg.head_dim, a,
-                                      ctx->wpb, (hipStream_t)stream);
-    return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
+    return decode_call(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, stream,
+                       false, nullptr, nullptr);
 }
 
 pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* q,
@@ -364,8 +387,14 @@ pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_
         if (!workspace || (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg))
             return fail(PKA_ERR_WORKSPACE, "decode workspace too small");
     }
-    if (save_kv && (s = pka_save_kv(ctx, md, k_new, v_new, k_pool, v_pool, stream)) != PKA_OK)
+    // bf16 / fp8 decode writes the new tokens inside the decode kernel (one
+    // launch less); other paths write them first with the save_kv kernel
+    const bool fused = path == PKA_PATH_DECODE && save_kv && ctx->cfg.kv_dtype != PKA_F32;
+    if (save_kv && !fused && (s = pka_save_kv(ctx, md, k_new, v_new, k_pool, v_pool, stream)) != PKA_OK)
         return s;
+    if (fused)
+        return decode_call(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, stream,
+                           true, k_new, v_new);
     if (path == PKA_PATH_DECODE)
         return pka_attn_decode(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, stream);
     return pka_attn_extend(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, stream);

@@ -19,6 +19,7 @@
 // as whole 256-byte (bf16) rows per 16 lanes and transposed in registers with
 // v_perm_b32 (fp8: byte gather + v_cvt_scalef32_pk_bf16_fp8).  The token order
 // inside a tile is a permutation chosen so every operand lines up.
+#include "fp8_encode.h"
 #include "pka_internal.h"
 
 namespace pka {
@@ -79,6 +80,34 @@ __device__ inline void emit_rows(const f32x4_t (&O)[D / 16], float inv, int j, E
         #pragma unroll
         for (int c = 0; c < CPL; ++c) v[r * CPL + c] = O[c][r] * inv;
     emit(v, 4 * CPL * j);
+}
+
+// Cache write of one request's new token for KV head g, fused into decode:
+// K on lanes 0..31, V on lanes 32..63, 8 elements per lane (bf16 copy or
+// bf16 -> fp8 quantisation).  The store is waited for before the wave reads
+// the pool, so the wave's own later load of that slot sees it.
+template <int D, bool FP8>
+__device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int g, int lane) {
+    const int32_t slot = a.out_cache_loc[qr];
+    if (slot < 0 || slot >= a.pool_slots) {
+        if (lane == 0) atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_PAGE);
+        return;
+    }
+    const bool is_v = lane >= 32;
+    const int e = (lane & 31) * 8;  // first element of this lane
+    if (e < D) {
+        const int64_t src = ((int64_t)qr * a.Hkv + g) * D + e;
+        const int64_t dst = ((int64_t)slot * a.Hkv + g) * D + e;
+        const u32x4_t w = *(const u32x4_t*)((const __bf16*)(is_v ? a.v_new : a.k_new) + src);
+        if constexpr (FP8) {
+            const float inv = is_v ? a.v_inv : a.k_inv;
+            *(u32x2_t*)((uint8_t*)(is_v ? a.v_pool : a.k_pool) + dst) =
+                u32x2_t{quant4(w.x, w.y, inv), quant4(w.z, w.w, inv)};
+        } else {
+            *(u32x4_t*)((__bf16*)(is_v ? a.v_pool : a.k_pool) + dst) = w;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stores have completed
 }
 
 template <int D, bool FP8>
@@ -259,6 +288,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
         const int32_t b = seg;
         const int32_t page_base = a.kv_indptr[b];
         const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);  // the request's query row
+        // the piece holding the request's last position writes the new token
+        if (a.k_new && hi == L) write_new_token<D, FP8>(a, qr, g, lane);
         // slot of tile token `tok` of the tile starting at position t0; positions
         // past the piece repeat its last token (cached, never counted)
         auto slot_at = [&](int32_t t0) {

@@ -113,6 +113,14 @@ struct AttnArgs {
     int32_t nwg;
     float scale_log2;  // scale * log2(e) * k_scale
     float v_scale;
+    // cache write fused into decode (null k_new: none): the new token's K/V
+    // row of each request is written by the wave that later reads it
+    const void* k_new;
+    const void* v_new;
+    const int32_t* out_cache_loc;
+    int64_t pool_slots;
+    float k_inv;  // fp32(1 / k_scale) for an fp8 cache, else 1
+    float v_inv;
 };
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);

@@ -21,7 +21,7 @@ def sentinel_pool_gpu(shape, kv_dtype: str, device="cuda"):
 
 class GpuProblem:
     def __init__(self, layout: workloads.Layout, values: workloads.Values = None, device="cuda",
-                 fill: bool = True):
+                 fill: bool = True, prefix_only: bool = False):
         spec = layout.spec
         self.layout, self.spec = layout, spec
         if values is None:
@@ -39,7 +39,7 @@ class GpuProblem:
         self.page_table = torch.tensor(layout.page_table, **i32)
         B, kvp = layout.batch, layout.kv_pages
         if fill:
-            self.fill_pools()
+            self.fill_pools(prefix_only)
         self.mode = spec.mode
         self.md = pka.Batch(self.ctx, self.mode, B, layout.num_q_tokens, kvp, device=device)
         self.md.init(self.seq_lens, None if self.mode == "decode" else self.extend_lens,
@@ -52,8 +52,11 @@ class GpuProblem:
         self.lse = torch.empty((layout.num_q_tokens, spec.num_q_heads), dtype=torch.float32,
                                device=device)
 
-    def fill_pools(self):
-        """Write every cached token (prefix and new) with the library's save_kv."""
+    def fill_pools(self, prefix_only: bool = False):
+        """Write every cached token (prefix and new) with the library's save_kv.
+
+        prefix_only: afterwards put the sentinel back into the new tokens'
+        slots, so only a forward pass with save_kv_cache=True fills them."""
         layout = self.layout
         B = layout.batch
         fill = pka.Batch(self.ctx, "extend", B, layout.total_tokens, layout.kv_pages,
@@ -63,6 +66,12 @@ class GpuProblem:
         torch.cuda.synchronize()
         status = fill.status()
         assert status == 0, f"device status {status} while filling the pools"
+        if prefix_only:
+            rows = torch.from_numpy(workloads.new_token_rows(layout)).to(self.seq_lens.device)
+            self.new_slots = fill.out_cache_loc.index_select(0, rows).long()
+            for pool in (self.k_pool, self.v_pool):
+                pool[self.new_slots] = sentinel_pool_gpu((1,) + tuple(pool.shape[1:]),
+                                                         self.spec.kv_dtype, pool.device)
 
     def metadata_step(self):
         self.md.init(self.seq_lens, None if self.mode == "decode" else self.extend_lens,

@@ -206,6 +206,7 @@ def test_idle_and_empty_batches_launch_nothing():
     spec = BASE_DEC.replace(batch=2, seq_len_kind="uniform", seq_len_args=(5, 50))
     layout = workloads.make_layout(spec)
     prob = GpuProblem(layout)
+    prob.out.fill_(0.5)  # defined contents (torch.empty may hold NaN, which never compares equal)
     before = prob.out.clone()
     pka.forward(prob.ctx, "idle", prob.md, None, None, None, None, None, None)
     empty = pka.Batch(prob.ctx, "decode", 0, 0, 0)
