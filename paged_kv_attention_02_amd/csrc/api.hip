@@ -220,6 +220,10 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
     } else if (c.k_scale != 1.f || c.v_scale != 1.f) {
         return fail(PKA_ERR_INVALID_ARG, "k_scale / v_scale apply to fp8 caches only (must be 1)");
     }
+    const int G = c.num_q_heads / c.num_kv_heads;
+    if (G > pka::extend_max_group(c.q_dtype, c.page_size))
+        return fail(PKA_ERR_UNSUPPORTED, "%d query heads per KV head (extend supports up to %d at page size %d)",
+                    G, pka::extend_max_group(c.q_dtype, c.page_size), c.page_size);
     pka_ctx* ctx = new (std::nothrow) pka_ctx;
     if (!ctx) return fail(PKA_ERR_INVALID_ARG, "out of host memory");
     ctx->cfg = c;
@@ -232,7 +236,7 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
     int wpb = 8;
     while (units % wpb) wpb >>= 1;
     ctx->wpb = wpb;
-    ctx->ext_tq = pka::extend_tq(c.q_dtype, c.kv_dtype, c.head_dim, ctx->G);
+    ctx->ext_tq = pka::extend_tq(c.q_dtype, c.kv_dtype, c.head_dim, ctx->G, c.page_size);
     *out = ctx;
     return PKA_OK;
 }

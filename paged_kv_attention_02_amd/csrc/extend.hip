@@ -11,13 +11,17 @@
 // gfx950 mapping of the bf16 variant.  A workgroup (4 waves) owns one
 // (request, query tile, KV head) item; its 128 query columns are the tile's
 // tokens times the G query heads sharing the KV head (GQA packing), so every
-// K/V tile staged in LDS feeds 128 columns.  Per 32-key tile and wave:
-//   S^T[key, col] = K . Q^T      8 x v_mfma_f32_32x32x16_bf16 (D = 128)
-//   O^T[d, col]  += V^T . P^T    8 x v_mfma_f32_32x32x16_bf16
+// K/V tile staged in LDS feeds 128 columns.  Per 64-key tile and wave:
+//   S^T[key, col] = K . Q^T      16 x v_mfma_f32_32x32x16_bf16 (D = 128)
+//   O^T[d, col]  += V^T . P^T    16 x v_mfma_f32_32x32x16_bf16
 // Column statistics of the online softmax live in the lane (two lanes per
-// column), P^T is used in place as the B operand, and V^T is built from
-// 8-byte LDS row reads with v_perm_b32.  K/V tiles are double-buffered in LDS
-// (next tile's global loads are in flight during the current tile's MFMAs).
+// column), P^T is used in place as the B operand, and V^T comes from LDS
+// through transposing reads.  K/V tiles are double-buffered in LDS and
+// filled by direct HBM -> LDS loads one tile ahead; within a wave the scores
+// of tile t+1 are computed while the probabilities of tile t are formed, so
+// the matrix cores have independent work during the softmax.  Workgroups of
+// one KV head are kept on one XCD, whose L2 then serves the K/V pages that
+// all query tiles of a request read.
 #include <type_traits>
 
 #include "pka_internal.h"
@@ -32,8 +36,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float LN2 = 0.69314718055994531f;
-constexpr int EXT_COLS = 128;  // query columns per workgroup (4 waves x 32)
+constexpr int EXT_WAVES = 4;   // waves per workgroup
+constexpr int EXT_COLS = 32 * EXT_WAVES;  // query columns per workgroup (32 per wave)
 constexpr int BN = 64;         // keys per tile (two 32-key MFMA blocks)
+constexpr int EXT_XCDS = 8;    // accelerator dies (each with its own L2)
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
     bf16x2_t v = {(__bf16)lo, (__bf16)hi};
@@ -92,30 +98,60 @@ template <int D> struct ExtTile {
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row (bf16)
     static constexpr int ROWB = D * 2;
     static constexpr int TILEB = BN * ROWB;            // bytes of one K or V tile
-    static constexpr int LOADS = TILEB / (256 * 16);   // DMA instructions per thread per tile
+    static constexpr int LOADS = TILEB / (64 * EXT_WAVES * 16);  // DMA instructions per thread per tile
     __device__ static constexpr int kchunk(int row, int c) { return c ^ (row & (CPR - 1)); }
     __device__ static constexpr int vchunk(int row, int c) { return c ^ ((4 * (row & 3)) & (CPR - 1)); }
 };
 
-template <int D, bool POS>
-__global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
+// Uniform 32-bit load through the scalar data cache (read only).
+__device__ inline int32_t load_uniform(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)p)[i];
+}
+
+// Direct HBM -> LDS load of 16 bytes per lane from a wave-uniform base plus
+// a 32-bit per-lane byte offset.
+__device__ inline void lds_dma16_s(const uint8_t* base, uint32_t voff, const uint8_t* lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff),
+                 "s"(base) : "m0");
+}
+
+// Software pipeline over 64-key tiles t (per wave):
+//   top of iteration t: K(t+1) and V(t) are in LDS, the raw scores S(t) are
+//   in registers; the direct loads of K(t+2) and V(t+1) start into the
+//   buffers that iteration t-1 finished with;
+//   softmax statistics of S(t), then one interleaved block in which the
+//   exponentials of S(t), the P.V MFMAs of tile t and the K.Q^T MFMAs of
+//   tile t+1 (independent of the softmax) are issued together, so the matrix
+//   cores run while the vector ALUs compute probabilities.
+// BIGPAGE (page size >= 64): a tile lies in one page, so its pool address is
+// a scalar and each lane only adds a fixed row offset.
+template <int D, bool POS, bool BIGPAGE>
+__global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void extend_mfma_kernel(AttnArgs a) {
     using T = ExtTile<D>;
-    constexpr int KSTEPS = D / 16;           // k-steps of q.k (32x32x16)
-    constexpr int VC = D / 32;               // 32-dim blocks of O^T (d = 32 c + row)
-    constexpr int SB = BN / 32;              // 32-key score blocks per tile
+    constexpr int KSTEPS = D / 16;              // k-steps of q.k (32x32x16)
+    constexpr int VC = D / 32;                  // 32-dim blocks of O^T (d = 32 c + row)
+    constexpr int SB = BN / 32;                 // 32-key score blocks per tile
+    constexpr int PK = BN / 16;                 // P.V k-steps per tile
+    constexpr int QPK = KSTEPS * SB / PK;       // next-tile K.Q^T MFMAs per P.V k-step
     constexpr int ROWS_PER_LOAD = 64 / T::CPR;  // rows one wave instruction fills
-    // one LDS object per stage and tensor, so the compiler can tell a tile
-    // being read from the next tile's direct loads
     __shared__ __attribute__((aligned(1024))) uint8_t sK0[T::TILEB], sK1[T::TILEB];
     __shared__ __attribute__((aligned(1024))) uint8_t sV0[T::TILEB], sV1[T::TILEB];
 
+    // Workgroups are dealt to the 8 XCDs round-robin (linear id mod 8).  The
+    // (KV head, item) list is cut into 8 contiguous chunks, one per XCD, so
+    // the items of one KV head (same K/V pages) share one XCD's L2.
     const int32_t* plan = a.plan;
-    const int32_t item = blockIdx.x;
+    // XCD x receives grid/8 workgroups, plus one when x < grid % 8.
+    const int32_t cap = gridDim.x / a.Hkv;  // item slots per KV head
+    const int32_t xcd = blockIdx.x % EXT_XCDS;
+    const int32_t base = gridDim.x / EXT_XCDS, extra = gridDim.x % EXT_XCDS;
+    const int32_t w = xcd * base + min(xcd, extra) + blockIdx.x / EXT_XCDS;
+    const int32_t g = w / cap, item = w % cap;
     if (item >= plan[PLAN_EXT_COUNT]) return;
     const int32_t TQ = plan[PLAN_EXT_TQ];
     const int32_t* items = plan + plan_ext_items(a.B);
     const int32_t b = items[2 * item], ti = items[2 * item + 1];
-    const int32_t g = blockIdx.y;
     const int32_t* F = plan + plan_seg_prefix(a.B);
     const int32_t q0 = a.qo_indptr[b];
     const int32_t nb = a.qo_indptr[b + 1] - q0;
@@ -126,7 +162,8 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
     const int32_t page_base = a.kv_indptr[b];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hh = lane >> 5;
     const int col = wave * 32 + n;
     const int ctok = tok_lo + col / a.G;
@@ -147,49 +184,84 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
 
     const int32_t kend = pb + tok_hi;  // keys 0 .. kend-1
     const int32_t ntiles = (kend + BN - 1) / BN;
-    const int64_t row_bytes = (int64_t)a.Hkv * T::ROWB;
+    const int32_t row_bytes = a.Hkv * T::ROWB;
     const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * T::ROWB;
     const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * T::ROWB;
     const int32_t P = 1 << a.page_shift;
 
-    // Direct loads of one tile.  Wave instruction j of wave w fills rows
-    // ROWS_PER_LOAD * (LOADS * w + j) .. ; lane i writes physical chunk
-    // i % CPR of its row, so it fetches the logical chunk that the swizzle
-    // places there.  Rows past the last key repeat it.  The pool slots of a
-    // tile's rows are looked up one tile ahead (slots_for), so the loads
-    // issue without waiting.
-    // raw page ids of the tile's rows (clamped and combined at use, a tile
-    // later, so nothing waits for these loads now)
-    auto slots_for = [&](int32_t kt0, int32_t (&pg)[T::LOADS], int32_t (&kp)[T::LOADS]) {
+    // Direct loads: wave instruction j of wave w fills LDS rows
+    // ROWS_PER_LOAD * (LOADS * w + j) ..; lane i writes physical chunk
+    // i % CPR of its row and fetches the logical chunk the swizzle puts
+    // there.  Rows past the last key repeat it.
+    const int pc = lane % T::CPR;
+    auto row_of = [&](int j) { return ROWS_PER_LOAD * (T::LOADS * wave + j) + lane / T::CPR; };
+    auto lds_row_block = [&](int j) { return (T::LOADS * wave + j) * 1024; };
+    // per-lane byte offsets of instruction j: the fetched chunk within a row
+    // (small pages), plus the row within the tile (BIGPAGE)
+    uint32_t koff[T::LOADS], voff[T::LOADS];
+    #pragma unroll
+    for (int j = 0; j < T::LOADS; ++j) {
+        const int r = row_of(j);
+        koff[j] = 16 * T::kchunk(r, pc) + (BIGPAGE ? r * row_bytes : 0);
+        voff[j] = 16 * T::vchunk(r, pc) + (BIGPAGE ? r * row_bytes : 0);
+    }
+
+    // pool byte offset of a tile's first row (BIGPAGE; wave-uniform)
+    auto tile_base = [&](int32_t pg, int32_t kt0) -> int64_t {
+        pg = min(max(pg, 0), a.num_pages - 1);
+        return (((int64_t)pg << a.page_shift) | (kt0 & (P - 1))) * (int64_t)row_bytes;
+    };
+    auto page_of_tile = [&](int32_t kt0) -> int32_t {
+        int64_t idx = (int64_t)page_base + (kt0 >> a.page_shift);
+        idx = idx < a.kv_cap ? idx : a.kv_cap - 1;
+        return load_uniform(a.kv_indices, idx);
+    };
+    // BIGPAGE: one tensor's tile from page pg (V when is_v)
+    auto dma_big = [&](const uint8_t* src, const uint32_t (&off)[T::LOADS], bool is_v, int32_t pg,
+                       int32_t kt0, uint8_t* dst) {
+        const uint8_t* tb = src + tile_base(pg, kt0);
+        const int32_t lim = kend - 1 - kt0;  // last row of the tile holding a key
+        if (lim >= BN - 1) {
+            #pragma unroll
+            for (int j = 0; j < T::LOADS; ++j) lds_dma16_s(tb, off[j], dst + lds_row_block(j));
+        } else {
+            #pragma unroll
+            for (int j = 0; j < T::LOADS; ++j) {
+                const int r = row_of(j);
+                const int ch = is_v ? T::vchunk(r, pc) : T::kchunk(r, pc);
+                lds_dma16_s(tb, (uint32_t)(min(r, lim) * row_bytes + 16 * ch), dst + lds_row_block(j));
+            }
+        }
+    };
+    // small pages: per-row slots; raw page ids are looked up an iteration
+    // before the slots are formed
+    auto lookup = [&](int32_t kt0, int32_t (&pg)[T::LOADS], int32_t (&kp)[T::LOADS]) {
         #pragma unroll
         for (int j = 0; j < T::LOADS; ++j) {
-            const int row = ROWS_PER_LOAD * (T::LOADS * wave + j) + lane / T::CPR;
-            kp[j] = min(kt0 + row, kend - 1);
+            kp[j] = min(kt0 + row_of(j), kend - 1);
             int64_t idx = (int64_t)page_base + (kp[j] >> a.page_shift);
             idx = idx < a.kv_cap ? idx : a.kv_cap - 1;
             pg[j] = a.kv_indices[idx];
         }
     };
-    auto load_tile = [&](const int32_t (&pg)[T::LOADS], const int32_t (&kp)[T::LOADS], uint8_t* dk,
-                         uint8_t* dv) {
+    auto form_slots = [&](const int32_t (&pg)[T::LOADS], const int32_t (&kp)[T::LOADS],
+                          int32_t (&slot)[T::LOADS]) {
         #pragma unroll
-        for (int j = 0; j < T::LOADS; ++j) {
-            const int row = ROWS_PER_LOAD * (T::LOADS * wave + j) + lane / T::CPR;
-            const int pc = lane % T::CPR;
-            const int32_t page = min(max(pg[j], 0), a.num_pages - 1);
-            const int64_t slot = ((int64_t)page << a.page_shift) | (kp[j] & (P - 1));
-            const int64_t off = slot * row_bytes;
-            const int ldsb = (T::LOADS * wave + j) * 1024;
-            lds_dma16(kbase + off + 16 * T::kchunk(row, pc), dk + ldsb);
-            lds_dma16(vbase + off + 16 * T::vchunk(row, pc), dv + ldsb);
-        }
+        for (int j = 0; j < T::LOADS; ++j)
+            slot[j] = (min(max(pg[j], 0), a.num_pages - 1) << a.page_shift) | (kp[j] & (P - 1));
     };
+    auto dma_small = [&](const uint8_t* src, const uint32_t (&choff)[T::LOADS],
+                         const int32_t (&slot)[T::LOADS], uint8_t* dst) {
+        #pragma unroll
+        for (int j = 0; j < T::LOADS; ++j)
+            lds_dma16(src + (int64_t)slot[j] * row_bytes + choff[j], dst + lds_row_block(j));
+    };
+
     // V^T operand: lane group G = lane/16 reads keys 4 (G/2) + s16/4 (+ 16 ks
     // + 8 r) at dims 16 (G%2) + 4 (s16%4) (+ 32 c) with the transposing load.
     const int G16 = lane >> 4, s16 = lane & 15;
     const int v_row = 4 * (G16 >> 1) + (s16 >> 2);
     const int v_byte = 32 * (G16 & 1) + 8 * (s16 & 3);  // byte within the 64-byte group of block c
-    // K operand: lane (n, hh) reads row 32 u + n, logical chunk 2 s + hh
 
     f32x16_t O[VC];
     #pragma unroll
@@ -200,32 +272,75 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
     const float c2 = a.scale_log2;
     const uint32_t ones = 0x3f803f80u;  // two bf16 1.0
 
-    // One tile: wait for its loads, start the next tile's loads into the
-    // other stage, then scores -> probabilities -> O += P.V.
-    int32_t pgs[T::LOADS], kps[T::LOADS];
-    auto tile = [&](int32_t t, const uint8_t* ks_, const uint8_t* vs_, uint8_t* kn, uint8_t* vn) {
-        const int32_t kt0 = t * BN;
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this tile's loads (and the slots) have landed
-        __syncthreads();                       // ... for every wave; the other stage is free
-        if (t + 1 < ntiles) {
-            load_tile(pgs, kps, kn, vn);
-            slots_for(kt0 + 2 * BN, pgs, kps);
-        }
+    // K.Q^T MFMA q (of KSTEPS * SB) of a tile: k-step q / SB, key block q % SB
+    auto qk_mfma = [&](const uint8_t* ks_, int q, f32x16_t* S) {
+        const int s = q / SB, u = q % SB;
+        const int row = 32 * u + n;
+        const u32x4_t kw = *(const u32x4_t*)(ks_ + row * T::ROWB + 16 * T::kchunk(row, 2 * s + hh));
+        // the first k-step starts from an inline zero accumulator
+        S[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), qop[s], s == 0 ? f32x16_t{} : S[u],
+                                                       0, 0, 0);
+    };
 
-        // S^T = K . Q^T, SB independent 32-key blocks
-        f32x16_t S[SB];
-        #pragma unroll
-        for (int u = 0; u < SB; ++u)
-            #pragma unroll
-            for (int r = 0; r < 16; ++r) S[u][r] = 0.f;
-        #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s)
-            #pragma unroll
-            for (int u = 0; u < SB; ++u) {
-                const int row = 32 * u + n;
-                const u32x4_t kw = *(const u32x4_t*)(ks_ + row * T::ROWB + 16 * T::kchunk(row, 2 * s + hh));
-                S[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), qop[s], S[u], 0, 0, 0);
+    // raw scores of the current and the next tile (the two sets swap roles
+    // from one iteration to the next)
+    f32x16_t SA[SB], SBn[SB];
+
+    // prologue: K(0), V(0), K(1) resident, S(0) computed
+    int32_t pgK = 0, pgV = 0;        // BIGPAGE: pages of tiles t+2 (K) and t+1 (V)
+    int32_t rawK[T::LOADS], kpK[T::LOADS], slotK[T::LOADS], slotV[T::LOADS];  // small pages
+    if constexpr (BIGPAGE) {
+        const int32_t p0 = page_of_tile(0);
+        dma_big(kbase, koff, false, p0, 0, sK0);
+        dma_big(vbase, voff, true, p0, 0, sV0);
+        if (ntiles > 1) {
+            const int32_t p1 = page_of_tile(BN);
+            dma_big(kbase, koff, false, p1, BN, sK1);
+            pgV = p1;
+        }
+        if (ntiles > 2) pgK = page_of_tile(2 * BN);
+    } else {
+        int32_t s0[T::LOADS];
+        lookup(0, rawK, kpK);
+        form_slots(rawK, kpK, s0);
+        dma_small(kbase, koff, s0, sK0);
+        dma_small(vbase, voff, s0, sV0);
+        lookup(BN, rawK, kpK);
+        form_slots(rawK, kpK, slotV);
+        if (ntiles > 1) dma_small(kbase, koff, slotV, sK1);
+        lookup(2 * BN, rawK, kpK);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    #pragma unroll
+    for (int q = 0; q < KSTEPS * SB; ++q) qk_mfma(sK0, q, SA);
+
+    auto iteration = [&](auto odd_c, auto next_c, int32_t t, f32x16_t (&S)[SB], f32x16_t (&Sn)[SB]) {
+        constexpr bool ODD = decltype(odd_c)::value;
+        constexpr bool NEXT = decltype(next_c)::value;  // t + 1 < ntiles
+        const uint8_t* vcur = ODD ? sV1 : sV0;  // V(t)
+        const uint8_t* knext = ODD ? sK0 : sK1; // K(t+1)
+        uint8_t* kdst = ODD ? sK1 : sK0;        // K(t+2)
+        uint8_t* vdst = ODD ? sV0 : sV1;        // V(t+1)
+        const int32_t kt0 = t * BN;
+
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): K(t+1), V(t) and lookups have landed
+        __syncthreads();                       // ... for every wave; iteration t-1 is done
+        if constexpr (BIGPAGE) {
+            if (t + 2 < ntiles) dma_big(kbase, koff, false, pgK, kt0 + 2 * BN, kdst);
+            if (NEXT) dma_big(vbase, voff, true, pgV, kt0 + BN, vdst);
+            pgV = pgK;
+            if (t + 3 < ntiles) pgK = page_of_tile(kt0 + 3 * BN);
+        } else {
+            if (NEXT) dma_small(vbase, voff, slotV, vdst);
+            if (t + 2 < ntiles) {
+                form_slots(rawK, kpK, slotK);
+                dma_small(kbase, koff, slotK, kdst);
+                #pragma unroll
+                for (int j = 0; j < T::LOADS; ++j) slotV[j] = slotK[j];
+                lookup(kt0 + 3 * BN, rawK, kpK);
             }
+        }
 
         // causal mask only where the tile crosses the diagonal of some column
         if (kt0 + BN - 1 > qpos_min) {
@@ -256,49 +371,56 @@ __global__ __launch_bounds__(256) void extend_mfma_kernel(AttnArgs a) {
             for (int c = 0; c < VC; ++c) O[c] *= alpha;
         }
 
-        // probabilities in bf16 (the normaliser sums the same rounded values),
-        // then O^T += V^T . P^T in k-steps of 16 keys.  A column has a valid
-        // key in every tile up to its own position, and tiles start at key 0,
-        // so m2 is finite from the first tile on.
+        // interleaved block: probabilities of S(t) (bf16; the normaliser sums
+        // the same rounded values), O^T += V^T . P^T over tile t, and the
+        // scores of tile t+1.  A column has a valid key in every tile up to
+        // its own position and tiles start at key 0, so m2 is finite here.
         #pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            uint32_t pw[8];
+        for (int pk = 0; pk < PK; ++pk) {
+            const int u = pk >> 1, r0 = 8 * (pk & 1);
+            uint32_t pw[4];
             #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float e0 = POS ? __builtin_fmaf(S[u][2 * i], c2, -m2) : S[u][2 * i] - m2;
-                const float e1 = POS ? __builtin_fmaf(S[u][2 * i + 1], c2, -m2) : S[u][2 * i + 1] - m2;
+            for (int i = 0; i < 4; ++i) {
+                const float s0 = S[u][r0 + 2 * i], s1 = S[u][r0 + 2 * i + 1];
+                const float e0 = POS ? __builtin_fmaf(s0, c2, -m2) : s0 - m2;
+                const float e1 = POS ? __builtin_fmaf(s1, c2, -m2) : s1 - m2;
                 pw[i] = pack_bf16(__builtin_amdgcn_exp2f(e0), __builtin_amdgcn_exp2f(e1));
                 lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
                                                         __builtin_bit_cast(bf16x2_t, ones), lsum, false);
             }
-            #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const int ks = 2 * u + k2;
-                const bf16x8_t pop = as_bf16x8(u32x4_t{pw[4 * k2], pw[4 * k2 + 1], pw[4 * k2 + 2], pw[4 * k2 + 3]});
+            if constexpr (NEXT) {
                 #pragma unroll
-                for (int c = 0; c < VC; ++c) {
-                    u32x2_t half[2];
-                    #pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        const int row = 16 * ks + 8 * r + v_row;
-                        const int lc = 4 * c + (v_byte >> 4);
-                        const uint8_t* p = vs_ + row * T::ROWB + 16 * T::vchunk(row, lc) + (v_byte & 15);
-                        half[r] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
-                    }
-                    const u32x4_t av = {half[0][0], half[0][1], half[1][0], half[1][1]};
-                    O[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
+                for (int qq = 0; qq < QPK; ++qq) qk_mfma(knext, pk * QPK + qq, Sn);
+            }
+            const bf16x8_t pop = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+            #pragma unroll
+            for (int c = 0; c < VC; ++c) {
+                u32x2_t half[2];
+                #pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    const int row = 16 * pk + 8 * r + v_row;
+                    const int lc = 4 * c + (v_byte >> 4);
+                    const uint8_t* p = vcur + row * T::ROWB + 16 * T::vchunk(row, lc) + (v_byte & 15);
+                    half[r] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
                 }
+                const u32x4_t av = {half[0][0], half[0][1], half[1][0], half[1][1]};
+                O[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
             }
         }
-        };
+    };
 
-    slots_for(0, pgs, kps);
-    load_tile(pgs, kps, sK0, sV0);
-    slots_for(BN, pgs, kps);
-    for (int32_t t = 0; t < ntiles; t += 2) {
-        tile(t, sK0, sV0, sK1, sV1);
-        if (t + 1 >= ntiles) break;
-        tile(t + 1, sK1, sV1, sK0, sV0);
+    using F_ = std::integral_constant<bool, false>;
+    using T_ = std::integral_constant<bool, true>;
+    int32_t t = 0;
+    for (; t + 2 < ntiles; t += 2) {
+        iteration(F_{}, T_{}, t, SA, SBn);
+        iteration(T_{}, T_{}, t + 1, SBn, SA);
+    }
+    if (t + 1 < ntiles) {
+        iteration(F_{}, T_{}, t, SA, SBn);
+        iteration(T_{}, F_{}, t + 1, SBn, SA);
+    } else {
+        iteration(F_{}, F_{}, t, SA, SBn);
     }
 
     // finish: the two lanes of a column hold halves of the sums
@@ -372,30 +494,41 @@ __global__ __launch_bounds__(256) void extend_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int extend_tq(pka_dtype q, pka_dtype /*kv*/, int /*D*/, int G) {
+int extend_tq(pka_dtype q, pka_dtype /*kv*/, int /*D*/, int G, int /*page_size*/) {
     if (q == PKA_F32) return 16;
     return G >= EXT_COLS ? 1 : EXT_COLS / G;
 }
 
+int extend_max_group(pka_dtype q, int /*page_size*/) {
+    if (q == PKA_F32) return 1 << 30;
+    return EXT_COLS;
+}
+
 hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hipStream_t s) {
-    const int tq = extend_tq(q, kv, D, a.G);
+    const int P = 1 << a.page_shift;
+    const int tq = extend_tq(q, kv, D, a.G, P);
     const int64_t items = plan_ext_capacity(a.B, a.N, tq);
     if (items == 0) return hipSuccess;
     if (q == PKA_F32) {
         const dim3 grid((unsigned)items, (a.Hq + 3) / 4);
         if (D == 128) hipLaunchKernelGGL((extend_f32_kernel<128>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((extend_f32_kernel<64>), grid, dim3(256), 0, s, a);
-    } else {
-        const dim3 grid((unsigned)items, a.Hkv);
-        const bool pos = a.scale_log2 > 0.f;
-        if (D == 128) {
-            if (pos) hipLaunchKernelGGL((extend_mfma_kernel<128, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((extend_mfma_kernel<128, false>), grid, dim3(256), 0, s, a);
-        } else {
-            if (pos) hipLaunchKernelGGL((extend_mfma_kernel<64, true>), grid, dim3(256), 0, s, a);
-            else hipLaunchKernelGGL((extend_mfma_kernel<64, false>), grid, dim3(256), 0, s, a);
-        }
+        return hipGetLastError();
     }
+    if (items * a.Hkv * 64 * EXT_WAVES > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(items * a.Hkv));
+    const bool pos = a.scale_log2 > 0.f;
+    const bool big = P >= BN;
+#define PKA_EXT(D_, POS_, BIG_) \
+    hipLaunchKernelGGL((extend_mfma_kernel<D_, POS_, BIG_>), grid, dim3(64 * EXT_WAVES), 0, s, a)
+    if (D == 128) {
+        if (pos) { if (big) PKA_EXT(128, true, true); else PKA_EXT(128, true, false); }
+        else { if (big) PKA_EXT(128, false, true); else PKA_EXT(128, false, false); }
+    } else {
+        if (pos) { if (big) PKA_EXT(64, true, true); else PKA_EXT(64, true, false); }
+        else { if (big) PKA_EXT(64, false, true); else PKA_EXT(64, false, false); }
+    }
+#undef PKA_EXT
     return hipGetLastError();
 }
 

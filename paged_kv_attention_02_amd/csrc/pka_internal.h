@@ -133,6 +133,8 @@ hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hi
 int decode_blocks_per_cu(pka_dtype kv, int D, int wpb);
 
 // Query tokens per extend item for a dtype pair.
-int extend_tq(pka_dtype q, pka_dtype kv, int D, int G);
+int extend_tq(pka_dtype q, pka_dtype kv, int D, int G, int page_size);
+// largest query-head group (Hq / Hkv) the extend kernels cover
+int extend_max_group(pka_dtype q, int page_size);
 
 }  // namespace pka

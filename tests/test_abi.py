@@ -61,6 +61,8 @@ def test_create_accepts_supported_configs():
     assert _create(kv_dtype=2, k_scale=0.01, v_scale=0.02, page_size=64) == 0
     assert _create(num_q_heads=64, num_kv_heads=4, page_size=1) == 0
     assert _create(num_q_heads=8, num_kv_heads=8, page_size=256) == 0
+    assert _create(num_q_heads=128, num_kv_heads=1) == 0      # largest bf16 head group
+    assert _create(num_q_heads=512, num_kv_heads=2, head_dim=64, q_dtype=0, kv_dtype=0) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -77,6 +79,7 @@ def test_create_accepts_supported_configs():
     (dict(kv_dtype=2, v_scale=float("inf")), -1),
     (dict(k_scale=0.5), -1),                 # scales only for fp8 caches
     (dict(scale=float("nan")), -1),
+    (dict(num_q_heads=256, num_kv_heads=1), -2),  # head group wider than an extend workgroup
 ])
 def test_create_refuses(kw, status):
     assert _create(**kw) == status
