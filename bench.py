@@ -162,6 +162,29 @@ def bench_extend(iters: int):
     return out
 
 
+def bench_gemm(iters: int, n: int = 8192):
+    """A square bf16 GEMM through the vendor library (torch.matmul), on
+    N(0,1) operands and on constant operands: what the matrix cores sustain
+    on this chip with data like the attention operands (the sustained clock
+    under MFMA load depends on the operand bits)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(7)
+    out = {"workload": f"bf16 GEMM {n}x{n}x{n} (torch.matmul)", "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS}
+    for kind in ("random", "constant"):
+        if kind == "random":
+            a = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16).contiguous()
+            b = torch.randn((n, n), generator=g, device="cuda").to(torch.bfloat16).contiguous()
+        else:
+            a = torch.ones((n, n), device="cuda", dtype=torch.bfloat16)
+            b = torch.ones((n, n), device="cuda", dtype=torch.bfloat16)
+        c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+        ms = time_events(lambda i: torch.matmul(a, b, out=c), iters)
+        out[f"{kind}_TFLOPs"] = round(2.0 * n ** 3 / ms / 1e9, 1)
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_copy(iters: int, nbytes: int = 1 << 30):
     """A plain device copy of known size: the reference for scaling HBM
     traffic counters (FETCH_SIZE / WRITE_SIZE) into bytes."""
@@ -181,7 +204,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the extend / other decode figures")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["extend", "decode3", "decode5", "copy"], default=None,
+    ap.add_argument("--only", choices=["extend", "decode3", "decode5", "copy", "gemm"], default=None,
                     help="run one extra leg alone (for profiling) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -200,6 +223,8 @@ def main():
     if args.only:
         if args.only == "copy":
             res = bench_copy(args.steps)
+        elif args.only == "gemm":
+            res = bench_gemm(args.steps)
         elif args.only == "extend":
             res = bench_extend(args.steps)
         else:
@@ -236,7 +261,7 @@ def main():
     ms_meta = time_events(lambda i: probs[i % 2].metadata_step(), args.steps)
     nbytes = decode_algorithmic_bytes(layout)
     achieved = nbytes / (ms_attn * 1e-3) / 1e9
-    src = source_hash("decode.hip", "pka_internal.h")
+    src = source_hash("decode.hip", "pka_internal.h", "fp8_encode.h")
     roof = {"bound": "hbm", "kernel": "decode_mfma_kernel + decode_merge_kernel (one attn_decode call)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -255,7 +280,7 @@ def main():
                    "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
                    "page_size": spec.page_size, "kv_tokens": layout.total_tokens,
                    "kv_bytes_per_step": kvb, "seed": spec.seed,
-                   "step": "init_metadata + save_kv + attn_decode",
+                   "step": "init_metadata + forward(save_kv_cache=True): new-token write fused into decode, then merge",
                    "metadata_ms": round(ms_meta, 4)},
         "roofline": roof,
     }
@@ -264,7 +289,11 @@ def main():
 
     if not args.no_extras:
         result["extend"] = bench_extend(args.steps)
+        result["mfma_reference"] = bench_gemm(min(args.steps, 20))
+        result["extend"]["frac_of_random_gemm"] = round(
+            result["extend"]["TFLOPs"] / result["mfma_reference"]["random_TFLOPs"], 4)
         log(f"extend: {result['extend']}")
+        log(f"bf16 GEMM reference: {result['mfma_reference']}")
         result["decode_configs"] = {}
         for cid in (3, 5):
             result["decode_configs"][str(cid)] = bench_decode_kernel(cid, args.steps)
