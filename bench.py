@@ -95,6 +95,82 @@ def time_events(fn, iters: int, warm: int = 2):
     return start.elapsed_time(stop) / iters
 
 
+def time_per_call(fn, iters: int, warm: int = 2):
+    """Median and min ms per call from one HIP event pair around each call."""
+    import torch
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4)}
+
+
+def _smi_sample():
+    """(mean gfx clock MHz over the XCDs, socket power W) from amd-smi, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        clk = [v["clk"]["value"] for k, v in g["clock"].items()
+               if k.startswith("gfx") and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        pw = g["power"]["socket_power"]["value"]
+        return (sum(clk) / len(clk), float(pw)) if clk else None
+    except Exception:
+        return None
+
+
+def gpu_state_under(fn, seconds: float = 1.5):
+    """Run fn(i) back to back for about `seconds` while amd-smi (a child
+    process) samples the gfx clock and socket power; medians of the samples."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        time.sleep(0.25)
+        while not stop.is_set():
+            s_ = _smi_sample()
+            if s_ is None:
+                return
+            samples.append(s_)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return None
+    clk = sorted(c for c, _ in samples)
+    pw = sorted(p for _, p in samples)
+    return {"gfx_clock_MHz": round(clk[len(clk) // 2]), "socket_power_W": round(pw[len(pw) // 2]),
+            "samples": len(samples)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(layout, values, budget_s: float = 20.0):
     """The oracle (fp64, OpenMP) on whole requests of the same workload until
     about budget_s of work; reported in the same unit as the GPU value."""
@@ -119,7 +195,8 @@ def cpu_baseline(layout, values, budget_s: float = 20.0):
             "sample": f"{len(done)} of {layout.batch} requests ({sum(int(layout.seq_lens[b]) for b in done)} "
                       f"cached tokens), all {spec.num_q_heads} heads, fp64 C oracle, "
                       f"{oracle.max_threads()} OpenMP threads, wall {t_total:.2f} s incl. "
-                      f"per-request cache repacking"}
+                      f"per-request cache repacking",
+            "cpu": cpu_model()}
 
 
 def bench_decode_kernel(cfg_id: int, iters: int):
@@ -142,7 +219,7 @@ def bench_decode_kernel(cfg_id: int, iters: int):
     return out
 
 
-def bench_extend(iters: int):
+def bench_extend(iters: int, gpu_state: bool = True):
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
@@ -150,13 +227,19 @@ def bench_extend(iters: int):
     prob = GpuProblem(layout)
     prob.attention_step(save=True)
     torch.cuda.synchronize()
-    ms = time_events(lambda i: prob.attention_step(save=False, lse=False), iters)
+    call = lambda i: prob.attention_step(save=False, lse=False)
+    ms = time_events(call, iters)
     fl = extend_flops(layout)
     tf = fl / ms / 1e9
-    out = {"workload": layout.spec.name, "q_tokens": layout.num_q_tokens,
+    spec = layout.spec
+    out = {"workload": spec.name, "q_tokens": layout.num_q_tokens,
            "kv_tokens": layout.total_tokens, "gflop": round(fl / 1e9, 2), "ms": round(ms, 4),
            "TFLOPs": round(tf, 1), "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
-           "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}
+           "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+           "ms_per_call": time_per_call(call, iters),
+           "variant": f"extend_mfma_kernel<{spec.head_dim}, scale>0, page {spec.page_size} >= 64>"}
+    if gpu_state:
+        out["gpu_state"] = gpu_state_under(call)
     del prob
     torch.cuda.empty_cache()
     return out
@@ -202,7 +285,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the extend / other decode figures")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the extend / other decode figures and the clock and power sampling")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["extend", "decode3", "decode5", "copy", "gemm"], default=None,
                     help="run one extra leg alone (for profiling) and print its figures")
@@ -226,7 +310,7 @@ def main():
         elif args.only == "gemm":
             res = bench_gemm(args.steps)
         elif args.only == "extend":
-            res = bench_extend(args.steps)
+            res = bench_extend(args.steps, gpu_state=False)
         else:
             res = bench_decode_kernel(int(args.only[-1]), args.steps)
         print(json.dumps(res), flush=True)
@@ -257,7 +341,10 @@ def main():
     log(f"step {ms_step:.4f} ms -> {value:.1f} GB/s KV read")
 
     # dominant kernel: the decode call (split kernel + merge) alone, HIP events
-    ms_attn = time_events(lambda i: probs[i % 2].attention_step(save=False, lse=False), args.steps)
+    attn_call = lambda i: probs[i % 2].attention_step(save=False, lse=False)
+    ms_attn = time_events(attn_call, args.steps)
+    attn_dist = time_per_call(attn_call, args.steps)
+    attn_state = None if args.no_extras else gpu_state_under(attn_call)
     ms_meta = time_events(lambda i: probs[i % 2].metadata_step(), args.steps)
     nbytes = decode_algorithmic_bytes(layout)
     achieved = nbytes / (ms_attn * 1e-3) / 1e9
@@ -267,6 +354,9 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_from_profiles("decode_llama3_8b", src),
             "bytes_per_launch": nbytes, "ms_per_launch": round(ms_attn, 4),
+            "ms_per_launch_per_call": attn_dist,
+            "variant": f"decode_mfma_kernel<{spec.head_dim}, {spec.kv_dtype} KV> + decode_merge_kernel",
+            "gpu_state": attn_state,
             "source_hash": src}
     log(f"attn_decode {ms_attn:.4f} ms -> {achieved:.1f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); "
         f"metadata {ms_meta:.4f} ms")
