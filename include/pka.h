@@ -9,7 +9,8 @@
  *
  *   pka_init_metadata  seq_lens + page table -> kv_indptr / kv_indices / ...
  *   pka_save_kv        scatter new K/V rows into the page pool
- *   pka_attn_decode    one query token per request (split-K flash decoding)
+ *   pka_attn_decode    one query token per request (split-K flash decoding;
+ *                      up to 16 causal query tokens for speculative verify)
  *   pka_attn_extend    a causal block of new tokens against prefix + itself
  *   pka_forward        ForwardMode-keyed dispatch between the two paths
  *
@@ -164,7 +165,15 @@ pka_status pka_save_kv(const pka_ctx* ctx, const pka_batch* md, const void* k_ne
 
 /* forward_decode: one query per request against its whole cache, split-K
  * flash decoding (split partials + log-sum-exp merge).  workspace: device
- * bytes >= pka_sizes.workspace_bytes.  lse may be NULL. */
+ * bytes >= pka_sizes.workspace_bytes.  lse may be NULL.
+ * With metadata built for TARGET_VERIFY / DRAFT_EXTEND (the speculative
+ * verify pass sent down the decode path, "[SGLang] Hybrid Attention",
+ * section on _select_backend), each request carries n_b = extend_lens[b]
+ * query rows (0 <= n_b <= 16); row i sits at position L_b - n_b + i and sees
+ * keys 0 .. L_b - n_b + i, the cache being read once for all of them.  Rows
+ * of a request with n_b > 16 beyond the 16th are not computed and
+ * PKA_DEV_BAD_LENGTH is raised.  The workspace then holds up to 16 partial
+ * rows per (request, workgroup): pka_batch_sizes sizes it by mode. */
 pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* q,
                            const void* k_pool, const void* v_pool, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
@@ -183,8 +192,10 @@ pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* 
 pka_path pka_select_path(pka_forward_mode mode, pka_spec_attn_mode spec_mode);
 
 /* One attention layer's forward: optional save_kv, then the path chosen by
- * pka_select_path.  The decode path takes one query per request, so a verify
- * batch routed to it must have num_q_tokens == batch (else UNSUPPORTED). */
+ * pka_select_path.  A verify batch routed to the decode path is computed as
+ * described at pka_attn_decode (several causal query rows per request).  On
+ * a bf16 / fp8 DECODE batch the cache write happens inside the decode kernel
+ * (one launch); otherwise save_kv runs first as its own kernel. */
 pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
                        const pka_batch* md, const void* q, const void* k_new, const void* v_new,
                        int save_kv, void* k_pool, void* v_pool, void* out, float* lse,

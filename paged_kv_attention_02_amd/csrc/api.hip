@@ -67,12 +67,20 @@ pka_status decode_wgs(const pka_ctx* ctx, int32_t* out) {
     return PKA_OK;
 }
 
-int64_t decode_ws_bytes(const pka_ctx* ctx, int32_t B, int32_t nwg) {
-    return ((int64_t)B + nwg) * ctx->cfg.num_q_heads * (ctx->cfg.head_dim + 1) * 4;
-}
-
 bool is_extend_like(pka_forward_mode m) {
     return m == PKA_MODE_EXTEND || m == PKA_MODE_TARGET_VERIFY || m == PKA_MODE_DRAFT_EXTEND;
+}
+
+// Decode partial slots per (request, workgroup): a decode batch has one query
+// row per request; an extend-like batch sent down the decode path
+// (speculative verify) may carry up to DEC_MAX_Q rows per request.
+int32_t decode_qslots(pka_forward_mode m, int32_t num_q_tokens) {
+    if (m == PKA_MODE_DECODE) return 1;
+    return std::max(1, std::min<int32_t>(pka::DEC_MAX_Q, num_q_tokens));
+}
+
+int64_t decode_ws_bytes(const pka_ctx* ctx, int32_t B, int32_t nwg, int32_t qslots) {
+    return ((int64_t)B + nwg) * qslots * ctx->cfg.num_q_heads * (ctx->cfg.head_dim + 1) * 4;
 }
 
 pka_status check_batch(const pka_ctx* ctx, const pka_batch* md) {
@@ -147,19 +155,20 @@ pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     if (write_new && (!k_new || !v_new)) return fail(PKA_ERR_INVALID_ARG, "null K/V pointer");
     if (write_new && (!aligned16(k_new) || !aligned16(v_new)))
         return fail(PKA_ERR_INVALID_ARG, "K/V rows must be 16-byte aligned");
-    if (md->num_q_tokens != md->batch)
-        return fail(PKA_ERR_UNSUPPORTED, "the decode path takes one query per request (%d tokens, %d requests)",
-                    md->num_q_tokens, md->batch);
+    const int32_t qslots = decode_qslots(md->mode, md->num_q_tokens);
+    if (write_new && qslots != 1)
+        return fail(PKA_ERR_INVALID_ARG, "the fused cache write serves decode batches only");
     int32_t nwg = 0;
     if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
-    const int64_t need = decode_ws_bytes(ctx, md->batch, nwg);
+    const int64_t need = decode_ws_bytes(ctx, md->batch, nwg, qslots);
     if (!workspace || (int64_t)workspace_bytes < need || !aligned16(workspace))
         return fail(PKA_ERR_WORKSPACE, "decode needs %lld workspace bytes (16-byte aligned), got %zu",
                     (long long)need, workspace_bytes);
     pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
     a.nwg = nwg;
+    a.qslots = qslots;
     a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * ctx->cfg.num_q_heads * ctx->cfg.head_dim;
+    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * qslots * ctx->cfg.num_q_heads * ctx->cfg.head_dim;
     if (write_new) {
         const pka_config& c = ctx->cfg;
         a.k_new = k_new;
@@ -262,7 +271,8 @@ pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t ba
     // may still be routed to it by the speculative-attention dispatch)
     out->workspace_bytes = mode == PKA_MODE_EXTEND || mode == PKA_MODE_IDLE
                                ? 0
-                               : decode_ws_bytes(ctx, batch, pka::DEC_MAX_WG);
+                               : decode_ws_bytes(ctx, batch, pka::DEC_MAX_WG,
+                                                 decode_qslots(mode, num_q_tokens));
     return PKA_OK;
 }
 
@@ -381,19 +391,20 @@ pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_
     if (md->mode != mode)
         return fail(PKA_ERR_INVALID_ARG, "metadata was built for mode %d, forward called with %d",
                     (int)md->mode, (int)mode);
-    if (path == PKA_PATH_DECODE && md->num_q_tokens != md->batch)
-        return fail(PKA_ERR_UNSUPPORTED, "speculative decode-mode verify needs one query per request");
     if (path == PKA_PATH_EXTEND && ctx->cfg.kv_dtype == PKA_FP8_E4M3FN)
         return fail(PKA_ERR_UNSUPPORTED, "extend over an fp8 cache is not supported");
     if (path == PKA_PATH_DECODE) {  // check the workspace before anything is enqueued
         int32_t nwg = 0;
         if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
-        if (!workspace || (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg))
+        if (!workspace ||
+            (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg, decode_qslots(md->mode, md->num_q_tokens)))
             return fail(PKA_ERR_WORKSPACE, "decode workspace too small");
     }
     // bf16 / fp8 decode writes the new tokens inside the decode kernel (one
-    // launch less); other paths write them first with the save_kv kernel
-    const bool fused = path == PKA_PATH_DECODE && save_kv && ctx->cfg.kv_dtype != PKA_F32;
+    // launch less); other paths (and verify batches on the decode path) write
+    // them first with the save_kv kernel
+    const bool fused = path == PKA_PATH_DECODE && save_kv && ctx->cfg.kv_dtype != PKA_F32 &&
+                       md->mode == PKA_MODE_DECODE;
     if (save_kv && !fused && (s = pka_save_kv(ctx, md, k_new, v_new, k_pool, v_pool, stream)) != PKA_OK)
         return s;
     if (fused)

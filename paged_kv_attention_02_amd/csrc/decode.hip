@@ -159,8 +159,10 @@ __device__ inline void load_tile(KVTile<D, FP8>& T, int32_t slot, const uint8_t*
 }
 
 // Scores, online-softmax update and P.V for one tile whose first `valid`
-// tokens are real (the rest are masked out).
-template <int D, bool FP8>
+// tokens are real for this lane's column (the rest are masked out).  With MQ
+// a column may have no real token yet (its causal limit lies beyond the
+// tile): its maximum stays -inf and it accumulates nothing.
+template <int D, bool FP8, bool MQ>
 __device__ inline void compute_tile(const KVTile<D, FP8>& T, const bf16x8_t* qop,
                                     f32x4_t* O, float& m2, float& lsum, int valid,
                                     float scale_log2, int j) {
@@ -199,12 +201,14 @@ __device__ inline void compute_tile(const KVTile<D, FP8>& T, const bf16x8_t* qop
         }
     mx = wave_max_xor_16_32(mx);
     const float mnew = fmaxf(m2, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+    // an empty column (mnew = -inf) subtracts 0: alpha and p become 0
+    const float msub = (MQ && mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(m2 - msub);
     m2 = mnew;
     float psum = 0.f;
     #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(p[i] - mnew);
+        p[i] = __builtin_amdgcn_exp2f(p[i] - msub);
         psum += p[i];
     }
     lsum = lsum * alpha + psum;
@@ -250,7 +254,12 @@ __device__ inline void compute_tile(const KVTile<D, FP8>& T, const bf16x8_t* qop
     }
 }
 
-template <int D, bool FP8>
+// MQ: several query tokens per request (speculative verify on the decode
+// path).  Columns are then (query token i, head h) pairs of the request, 16
+// per pass of the wave over its share; token i of a request with n query
+// tokens sits at position L - n + i and sees keys 0 .. L - n + i.  Partials
+// of token i go to slot (b + w) * qslots + i.
+template <int D, bool FP8, bool MQ>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     using S = DecodeShape<D, FP8>;
     const int lane = threadIdx.x & 63;
@@ -287,9 +296,22 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
         const int32_t L = f1 - f0;
         const int32_t b = seg;
         const int32_t page_base = a.kv_indptr[b];
-        const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);  // the request's query row
-        // the piece holding the request's last position writes the new token
-        if (a.k_new && hi == L) write_new_token<D, FP8>(a, qr, g, lane);
+        // query rows of the request: one (its last row) without MQ
+        int32_t q0, nq, pfx;
+        if constexpr (MQ) {
+            q0 = a.qo_indptr[b];
+            const int32_t nb = a.qo_indptr[b + 1] - q0;
+            nq = min(nb, a.qslots);
+            if (nb > a.qslots && lo == 0 && lane == 0 && unit == 0)
+                atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_LENGTH);
+            pfx = L - nb;
+        } else {
+            q0 = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
+            nq = 1;
+            pfx = L - 1;
+            // the piece holding the request's last position writes the new token
+            if (a.k_new && hi == L) write_new_token<D, FP8>(a, q0, g, lane);
+        }
         // slot of tile token `tok` of the tile starting at position t0; positions
         // past the piece repeat its last token (cached, never counted)
         auto slot_at = [&](int32_t t0) {
@@ -297,79 +319,93 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             return slot_of(a, page_base, pos < hi ? pos : hi - 1);
         };
 
-        KVTile<D, FP8> A, Bt;
-        int32_t slot_a = slot_at(lo);
-        int32_t slot_b = slot_at(lo + DEC_TILE);
-        load_tile(A, slot_a, kbase, vbase, row_bytes, n, j);
+        const int32_t cols = nq * nh;
+        for (int32_t c0 = 0; c0 < cols; c0 += 16) {
+            // this lane's column: query token qi, head h
+            const int32_t c = c0 + n;
+            const bool col_ok = c < cols;
+            const int32_t qi = MQ ? (col_ok ? c / nh : 0) : 0;
+            const int32_t h = h0 + (MQ ? c % nh : n);
+            const int32_t qr = q0 + qi;
+            // keys of this column within the piece: positions < kend_c
+            const int32_t kend_c = MQ ? min(hi, pfx + qi + 1) : hi;
 
-        // Q^T operand: lane (n, j) holds head h0+n at the dims its K lanes load.
-        bf16x8_t qop[S::KSTEPS];
-        {
-            const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + h0 + n) * D;
-            #pragma unroll
-            for (int ks = 0; ks < S::KSTEPS; ++ks) {
-                const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (n < nh) v = *(const u32x4_t*)(qrow + d0);
-                qop[ks] = as_bf16x8(v);
-            }
-        }
-
-        f32x4_t O[S::CPL];
-        #pragma unroll
-        for (int c = 0; c < S::CPL; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        float m2 = -INFINITY, lsum = 0.f;
-
-        // Two tiles in flight: while one tile is consumed the next one's
-        // loads are outstanding.  Loads are issued unconditionally (past the
-        // end they re-read the piece's last row) so the wait counts are the
-        // same on every iteration.
-        for (int32_t t0 = lo;; t0 += 2 * DEC_TILE) {
-            load_tile(Bt, slot_b, kbase, vbase, row_bytes, n, j);
-            slot_a = slot_at(t0 + 2 * DEC_TILE);
-            compute_tile<D, FP8>(A, qop, O, m2, lsum, hi - t0, a.scale_log2, j);
-            if (t0 + DEC_TILE >= hi) break;
+            KVTile<D, FP8> A, Bt;
+            int32_t slot_a = slot_at(lo);
+            int32_t slot_b = slot_at(lo + DEC_TILE);
             load_tile(A, slot_a, kbase, vbase, row_bytes, n, j);
-            slot_b = slot_at(t0 + 3 * DEC_TILE);
-            compute_tile<D, FP8>(Bt, qop, O, m2, lsum, hi - t0 - DEC_TILE, a.scale_log2, j);
-            if (t0 + 2 * DEC_TILE >= hi) break;
-        }
 
-        // finish: denominator over the four lane groups of each head
-        const float ltot = wave_sum_xor_16_32(lsum);
-        const float inv = 1.0f / ltot;
-        const float lse_nat = (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
-        if (n < nh) {
-            const int32_t h = h0 + n;
-            if (lo == 0 && hi == L) {
-                __bf16* orow = (__bf16*)a.out + ((int64_t)qr * a.Hq + h) * D;
-                emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
-                    #pragma unroll
-                    for (int i = 0; i < 4 * S::CPL; i += 8) {
-                        const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
-                                            pack_bf16(v[i + 4], v[i + 5]),
-                                            pack_bf16(v[i + 6], v[i + 7])};
-                        *(u32x4_t*)(orow + d0 + i) = pk;
-                    }
-                });
-                if (a.lse && j == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
-            } else {
-                const int64_t ps = (int64_t)b + w;  // partial slot of (request, workgroup)
-                float* prow = a.ws_o + (ps * a.Hq + h) * D;
-                emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
-                    #pragma unroll
-                    for (int i = 0; i < 4 * S::CPL; i += 4)
-                        *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
-                });
-                if (j == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
+            // Q^T operand: lane (n, j) holds its column at the dims its K lanes load.
+            bf16x8_t qop[S::KSTEPS];
+            {
+                const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + h) * D;
+                #pragma unroll
+                for (int ks = 0; ks < S::KSTEPS; ++ks) {
+                    const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
+                    u32x4_t v = {0u, 0u, 0u, 0u};
+                    if (MQ ? col_ok : n < nh) v = *(const u32x4_t*)(qrow + d0);
+                    qop[ks] = as_bf16x8(v);
+                }
+            }
+
+            f32x4_t O[S::CPL];
+            #pragma unroll
+            for (int cc = 0; cc < S::CPL; ++cc) O[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            float m2 = -INFINITY, lsum = 0.f;
+
+            // Two tiles in flight: while one tile is consumed the next one's
+            // loads are outstanding.  Loads are issued unconditionally (past
+            // the end they re-read the piece's last row) so the wait counts
+            // are the same on every iteration.
+            for (int32_t t0 = lo;; t0 += 2 * DEC_TILE) {
+                load_tile(Bt, slot_b, kbase, vbase, row_bytes, n, j);
+                slot_a = slot_at(t0 + 2 * DEC_TILE);
+                compute_tile<D, FP8, MQ>(A, qop, O, m2, lsum, kend_c - t0, a.scale_log2, j);
+                if (t0 + DEC_TILE >= hi) break;
+                load_tile(A, slot_a, kbase, vbase, row_bytes, n, j);
+                slot_b = slot_at(t0 + 3 * DEC_TILE);
+                compute_tile<D, FP8, MQ>(Bt, qop, O, m2, lsum, kend_c - t0 - DEC_TILE, a.scale_log2, j);
+                if (t0 + 2 * DEC_TILE >= hi) break;
+            }
+
+            // finish: denominator over the four lane groups of each column; a
+            // column with no key in this piece leaves weight 0 (lse -inf, o 0)
+            const float ltot = wave_sum_xor_16_32(lsum);
+            const float inv = MQ && !(ltot > 0.f) ? 0.f : 1.0f / ltot;
+            const float lse_nat = MQ && !(ltot > 0.f) ? -INFINITY : (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
+            if (MQ ? col_ok : n < nh) {
+                if (lo == 0 && hi == L) {
+                    __bf16* orow = (__bf16*)a.out + ((int64_t)qr * a.Hq + h) * D;
+                    emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+                        #pragma unroll
+                        for (int i = 0; i < 4 * S::CPL; i += 8) {
+                            const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
+                                                pack_bf16(v[i + 4], v[i + 5]),
+                                                pack_bf16(v[i + 6], v[i + 7])};
+                            *(u32x4_t*)(orow + d0 + i) = pk;
+                        }
+                    });
+                    if (a.lse && j == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
+                } else {
+                    // partial slot of (request, workgroup, query token)
+                    const int64_t ps = ((int64_t)b + w) * a.qslots + qi;
+                    float* prow = a.ws_o + (ps * a.Hq + h) * D;
+                    emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+                        #pragma unroll
+                        for (int i = 0; i < 4 * S::CPL; i += 4)
+                            *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
+                    });
+                    if (j == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
+                }
             }
         }
     }
 }
 
 // fp32 cache: a plain VALU variant with the same work partition (lanes over
-// head_dim, one token at a time).  Used for fp32 workloads.
-template <int D>
+// head_dim, one token at a time, 16 columns per pass as in the MFMA variant).
+// Used for fp32 workloads.
+template <int D, bool MQ>
 __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
     constexpr int EPL = D / 64;  // dims per lane
     const int lane = threadIdx.x & 63;
@@ -393,63 +429,86 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
         if (f0 >= end) break;
         const int32_t lo = (int32_t)(max(start, (int64_t)f0) - f0);
         const int32_t hi = (int32_t)(min(end, (int64_t)f1) - f0);
+        const int32_t L = f1 - f0;
         const int32_t b = seg, page_base = a.kv_indptr[b];
-        const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
-        float q[16][EPL], o[16][EPL], m[16], l[16];
-        #pragma unroll
-        for (int hh = 0; hh < 16; ++hh) {
-            m[hh] = -INFINITY;
-            l[hh] = 0.f;
-            #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                q[hh][e] = hh < nh ? ((const float*)a.q)[((int64_t)qr * a.Hq + h0 + hh) * D + e * 64 + lane] : 0.f;
-                o[hh][e] = 0.f;
-            }
+        int32_t q0, nq, pfx;
+        if constexpr (MQ) {
+            q0 = a.qo_indptr[b];
+            const int32_t nb = a.qo_indptr[b + 1] - q0;
+            nq = min(nb, a.qslots);
+            if (nb > a.qslots && lo == 0 && lane == 0 && unit == 0)
+                atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_LENGTH);
+            pfx = L - nb;
+        } else {
+            q0 = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
+            nq = 1;
+            pfx = L - 1;
         }
-        for (int32_t t = lo; t < hi; ++t) {
-            const int64_t base = ((int64_t)slot_of(a, page_base, t) * a.Hkv + g) * D;
-            float k[EPL], v[EPL];
+        const int32_t cols = nq * nh;
+        for (int32_t c0 = 0; c0 < cols; c0 += 16) {
+            const int ncol = min(16, cols - c0);
+            float q[16][EPL], o[16][EPL], m[16], l[16];
+            int32_t kend[16];
             #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                k[e] = ((const float*)a.k_pool)[base + e * 64 + lane];
-                v[e] = ((const float*)a.v_pool)[base + e * 64 + lane];
+            for (int cc = 0; cc < 16; ++cc) {
+                m[cc] = -INFINITY;
+                l[cc] = 0.f;
+                const int32_t c = c0 + cc;
+                const int32_t qi = cc < ncol ? c / nh : 0;
+                kend[cc] = min(hi, pfx + qi + 1);
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    q[cc][e] = cc < ncol ? ((const float*)a.q)[((int64_t)(q0 + qi) * a.Hq + h0 + c % nh) * D + e * 64 + lane] : 0.f;
+                    o[cc][e] = 0.f;
+                }
             }
+            for (int32_t t = lo; t < hi; ++t) {
+                const int64_t base = ((int64_t)slot_of(a, page_base, t) * a.Hkv + g) * D;
+                float k[EPL], v[EPL];
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    k[e] = ((const float*)a.k_pool)[base + e * 64 + lane];
+                    v[e] = ((const float*)a.v_pool)[base + e * 64 + lane];
+                }
+                #pragma unroll
+                for (int cc = 0; cc < 16; ++cc) {
+                    if (cc >= ncol || t >= kend[cc]) continue;
+                    float dot = 0.f;
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) dot += q[cc][e] * k[e];
+                    #pragma unroll
+                    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
+                    const float sc = dot * scale2;
+                    const float mn = fmaxf(m[cc], sc);
+                    const float al = __builtin_amdgcn_exp2f(m[cc] - mn);
+                    const float p = __builtin_amdgcn_exp2f(sc - mn);
+                    m[cc] = mn;
+                    l[cc] = l[cc] * al + p;
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) o[cc][e] = o[cc][e] * al + p * v[e];
+                }
+            }
+            const bool full = lo == 0 && hi == L;
             #pragma unroll
-            for (int hh = 0; hh < 16; ++hh) {
-                if (hh >= nh) continue;
-                float dot = 0.f;
-                #pragma unroll
-                for (int e = 0; e < EPL; ++e) dot += q[hh][e] * k[e];
-                #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
-                const float s = dot * scale2;
-                const float mn = fmaxf(m[hh], s);
-                const float al = __builtin_amdgcn_exp2f(m[hh] - mn);
-                const float p = __builtin_amdgcn_exp2f(s - mn);
-                m[hh] = mn;
-                l[hh] = l[hh] * al + p;
-                #pragma unroll
-                for (int e = 0; e < EPL; ++e) o[hh][e] = o[hh][e] * al + p * v[e];
-            }
-        }
-        const bool full = lo == 0 && hi == f1 - f0;
-        #pragma unroll
-        for (int hh = 0; hh < 16; ++hh) {
-            if (hh >= nh) continue;
-            const int32_t h = h0 + hh;
-            const float inv = 1.0f / l[hh];
-            const float lse_nat = (m[hh] + __builtin_amdgcn_logf(l[hh])) * LN2;
-            if (full) {
-                #pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    ((float*)a.out)[((int64_t)qr * a.Hq + h) * D + e * 64 + lane] = o[hh][e] * inv;
-                if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
-            } else {
-                const int64_t ps = (int64_t)b + w;
-                #pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    a.ws_o[(ps * a.Hq + h) * D + e * 64 + lane] = o[hh][e] * inv;
-                if (lane == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
+            for (int cc = 0; cc < 16; ++cc) {
+                if (cc >= ncol) continue;
+                const int32_t c = c0 + cc, qi = c / nh, h = h0 + c % nh, qr = q0 + qi;
+                // a column with no key in this piece leaves weight 0 (lse -inf, o 0)
+                const bool empty = !(l[cc] > 0.f);
+                const float inv = empty ? 0.f : 1.0f / l[cc];
+                const float lse_nat = empty ? -INFINITY : (m[cc] + __builtin_amdgcn_logf(l[cc])) * LN2;
+                if (full) {
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e)
+                        ((float*)a.out)[((int64_t)qr * a.Hq + h) * D + e * 64 + lane] = o[cc][e] * inv;
+                    if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
+                } else {
+                    const int64_t ps = ((int64_t)b + w) * a.qslots + qi;
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e)
+                        a.ws_o[(ps * a.Hq + h) * D + e * 64 + lane] = o[cc][e] * inv;
+                    if (lane == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
+                }
             }
         }
     }
@@ -476,50 +535,62 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     const int64_t w0 = f0 / share, w1 = (f1 - 1) / share;
     if (w0 == w1) return;  // written directly by its only workgroup
     const int32_t np = (int32_t)(w1 - w0 + 1);
-    const float* lse_col = a.ws_lse + (b + w0) * a.Hq + h;  // stride Hq per partial
-    const float* o_col = a.ws_o + ((b + w0) * a.Hq + h) * D;  // stride Hq*D per partial
-    const int64_t ostride = (int64_t)a.Hq * D;
+    // query rows of the request (one without multi-query partials)
+    int32_t q0, nq;
+    if (a.qslots > 1) {
+        q0 = a.qo_indptr[b];
+        nq = min(a.qo_indptr[b + 1] - q0, a.qslots);
+    } else {
+        q0 = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
+        nq = 1;
+    }
+    const int64_t lstride = (int64_t)a.qslots * a.Hq;  // per partial
+    const int64_t ostride = lstride * D;
+    for (int32_t qi = 0; qi < nq; ++qi) {
+        const float* lse_col = a.ws_lse + ((b + w0) * a.qslots + qi) * a.Hq + h;
+        const float* o_col = a.ws_o + (((b + w0) * a.qslots + qi) * a.Hq + h) * D;
 
-    float M = -INFINITY;
-    for (int32_t k = lane; k < np; k += 64) M = fmaxf(M, lse_col[(int64_t)k * a.Hq]);
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float den = 0.f, acc[EPL];
-    #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-    for (int32_t k0 = 0; k0 < np; k0 += 64) {
-        const int32_t k = k0 + lane;
-        const float wk = k < np ? expf(lse_col[(int64_t)k * a.Hq] - M) : 0.f;
-        den += wk;
-        const int32_t cnt = min(64, np - k0);
-        for (int32_t i = 0; i < cnt; i += UNROLL) {
-            float v[UNROLL][EPL], wt[UNROLL];
-            #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int32_t kk = min(i + u, cnt - 1);
-                wt[u] = i + u < cnt ? __shfl(wk, kk) : 0.f;
+        float M = -INFINITY;
+        for (int32_t k = lane; k < np; k += 64) M = fmaxf(M, lse_col[(int64_t)k * lstride]);
+        #pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        float den = 0.f, acc[EPL];
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+        for (int32_t k0 = 0; k0 < np; k0 += 64) {
+            const int32_t k = k0 + lane;
+            const float wk = k < np ? expf(lse_col[(int64_t)k * lstride] - M) : 0.f;
+            den += wk;
+            const int32_t cnt = min(64, np - k0);
+            for (int32_t i = 0; i < cnt; i += UNROLL) {
+                float v[UNROLL][EPL], wt[UNROLL];
                 #pragma unroll
-                for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)(k0 + kk) * ostride + e * 64 + lane];
+                for (int u = 0; u < UNROLL; ++u) {
+                    const int32_t kk = min(i + u, cnt - 1);
+                    wt[u] = i + u < cnt ? __shfl(wk, kk) : 0.f;
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)(k0 + kk) * ostride + e * 64 + lane];
+                }
+                #pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    #pragma unroll
+                    for (int e = 0; e < EPL; ++e) acc[e] += wt[u] * v[u][e];
             }
-            #pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                #pragma unroll
-                for (int e = 0; e < EPL; ++e) acc[e] += wt[u] * v[u][e];
         }
+        #pragma unroll
+        for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+        const float inv = 1.0f / den;
+        const int32_t qr = q0 + qi;
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int64_t o = ((int64_t)qr * a.Hq + h) * D + e * 64 + lane;
+            if constexpr (OUT_BF16)
+                ((__bf16*)a.out)[o] = (__bf16)(acc[e] * inv);
+            else
+                ((float*)a.out)[o] = acc[e] * inv;
+        }
+        if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = M + logf(den);
     }
-    #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
-    const float inv = 1.0f / den;
-    const int32_t qr = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
-    #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-        const int64_t o = ((int64_t)qr * a.Hq + h) * D + e * 64 + lane;
-        if constexpr (OUT_BF16)
-            ((__bf16*)a.out)[o] = (__bf16)(acc[e] * inv);
-        else
-            ((float*)a.out)[o] = acc[e] * inv;
-    }
-    if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = M + logf(den);
 }
 
 template <int D>
@@ -527,12 +598,17 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
     const int units = a.Hkv * a.qgroups;
     const dim3 grid(a.nwg, units / wpb);
     const dim3 block(64 * wpb);
-    if (kv == PKA_BF16)
-        hipLaunchKernelGGL((decode_mfma_kernel<D, false>), grid, block, 0, s, a);
-    else if (kv == PKA_FP8_E4M3FN)
-        hipLaunchKernelGGL((decode_mfma_kernel<D, true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_f32_kernel<D>), grid, block, 0, s, a);
+    const bool mq = a.qslots > 1;
+    if (kv == PKA_BF16) {
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<D, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<D, false, false>), grid, block, 0, s, a);
+    } else if (kv == PKA_FP8_E4M3FN) {
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<D, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<D, true, false>), grid, block, 0, s, a);
+    } else {
+        if (mq) hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, block, 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid(a.B, (a.Hq + 3) / 4);
@@ -548,11 +624,11 @@ int blocks_per_cu_d(pka_dtype kv, int wpb) {
     int n = 0;
     hipError_t e;
     if (kv == PKA_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, false>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, false, false>, 64 * wpb, 0);
     else if (kv == PKA_FP8_E4M3FN)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, true>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, true, false>, 64 * wpb, 0);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<D>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<D, false>, 64 * wpb, 0);
     return e == hipSuccess ? n : 0;
 }
 

@@ -35,6 +35,8 @@ constexpr int DEC_TILE = 32;
 constexpr int DEC_MIN_SHARE = 64;
 // Upper bound of decode workgroups (persistent grid).
 constexpr int DEC_MAX_WG = 2048;
+// Most query tokens per request on the decode path (speculative verify).
+constexpr int DEC_MAX_Q = 16;
 
 // plan offsets that depend on the batch size
 __host__ __device__ inline int64_t plan_seg_prefix(int32_t /*B*/) { return PLAN_HDR; }
@@ -113,6 +115,10 @@ struct AttnArgs {
     int32_t nwg;
     float scale_log2;  // scale * log2(e) * k_scale
     float v_scale;
+    // decode partial slots per (request, workgroup): 1, or up to DEC_MAX_Q
+    // when requests carry several query tokens (their rows are then the
+    // request's qo_indptr range and each is causal over the new tokens)
+    int32_t qslots;
     // cache write fused into decode (null k_new: none): the new token's K/V
     // row of each request is written by the wave that later reads it
     const void* k_new;

@@ -190,18 +190,6 @@ def test_speculative_modes_route_by_spec_mode(mode, spec_mode):
     run_and_check(spec, mode=mode, spec_mode=spec_mode)
 
 
-def test_decode_verify_with_several_tokens_is_refused():
-    spec = BASE_EXT.replace(batch=2, new_len_args=(3, 3), prefix_len_args=(0, 50), seed=44)
-    layout = workloads.make_layout(spec)
-    prob = GpuProblem(layout)
-    md = pka.Batch(prob.ctx, "target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages)
-    md.init(prob.seq_lens, prob.extend_lens, prob.page_table)
-    with pytest.raises(pka.PkaError) as e:
-        pka.forward(prob.ctx, "target_verify", md, prob.values.q, prob.k_new, prob.v_new, prob.k_pool,
-                    prob.v_pool, prob.out, spec_mode="decode")
-    assert e.value.status == -2
-
-
 def test_idle_and_empty_batches_launch_nothing():
     spec = BASE_DEC.replace(batch=2, seq_len_kind="uniform", seq_len_args=(5, 50))
     layout = workloads.make_layout(spec)

@@ -1,0 +1,118 @@
+"""Speculative verify on the decode path, through the C ABI.
+
+A TARGET_VERIFY / DRAFT_EXTEND batch with the decode speculative-attention
+mode goes to the decode path ("[SGLang] Hybrid Attention", section on
+_select_backend) carrying n_b query tokens per request; token i sees the
+cache up to position L_b - n_b + i.  Outputs are compared with the fp64
+oracle's extend semantics (bf16 / fp32: max-abs 2e-2, rel-RMS 5e-3; fp8:
+5e-2, 2e-2), and with the extend path on the same batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.oracle_ref import TOL, errors, oracle_full
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_attention_02_amd as pka
+    from tests.gpu_problem import GpuProblem
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    print(f"\n[case] {request.node.name}", flush=True)
+
+
+def _verify_problem(spec, mode="target_verify", seq_lens=None, extend_lens=None):
+    layout = workloads.make_layout(spec, seq_lens=seq_lens, extend_lens=extend_lens)
+    values = workloads.make_values(layout, device="cuda")
+    prob = GpuProblem(layout, values, prefix_only=True)
+    prob.mode = mode
+    prob.md = pka.Batch(prob.ctx, mode, layout.batch, layout.num_q_tokens, layout.kv_pages)
+    prob.metadata_step()
+    return prob, layout, values
+
+
+def _check(prob, layout, values, name):
+    prob.attention_step(save=True, spec_mode="decode")
+    torch.cuda.synchronize()
+    status = prob.md.status()
+    ref, ref_lse = oracle_full(layout, values)
+    got = prob.out_np()
+    max_abs, rel = errors(got, ref)
+    tol_abs, tol_rel = TOL[layout.spec.kv_dtype]
+    print(f"[parity] {name}: n={list(layout.extend_lens)[:8]} max_abs={max_abs:.2e} rel={rel:.2e}", flush=True)
+    assert status == 0, status
+    assert np.all(np.isfinite(got))
+    assert max_abs <= tol_abs and rel <= tol_rel, (max_abs, rel)
+    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=2e-3)
+
+
+BASE = workloads.Spec("verify", "extend", 6, 32, 8, 128, 16, "bf16", "bf16", seed=81,
+                      new_len_args=(2, 8), prefix_len_args=(1, 900))
+
+
+@pytest.mark.parametrize("name,spec", [
+    ("bf16_p16_g4", BASE),
+    ("bf16_p1_g16", BASE.replace(num_q_heads=64, num_kv_heads=4, page_size=1, seed=82)),
+    ("fp8_p64_g8", BASE.replace(num_q_heads=64, num_kv_heads=8, page_size=64, kv_dtype="fp8", seed=83)),
+    ("bf16_d64_g2", BASE.replace(num_q_heads=8, num_kv_heads=4, head_dim=64, page_size=32, seed=84)),
+    ("f32_p1_g2", BASE.replace(num_q_heads=4, num_kv_heads=2, head_dim=64, page_size=1, q_dtype="f32",
+                               kv_dtype="f32", seed=85)),
+])
+@pytest.mark.parametrize("mode", ["target_verify", "draft_extend"])
+def test_verify_on_decode_path(name, spec, mode):
+    prob, layout, values = _verify_problem(spec, mode)
+    _check(prob, layout, values, f"{name}/{mode}")
+
+
+def test_verify_long_requests_are_split_and_merged():
+    """Long contexts spread over many workgroups: every query token's rows
+    come from partials, including pieces where some tokens see no key."""
+    spec = BASE.replace(batch=3, seed=86)
+    prob, layout, values = _verify_problem(spec, seq_lens=[30000, 12000, 4100],
+                                           extend_lens=[8, 3, 16])
+    _check(prob, layout, values, "long_split")
+
+
+def test_verify_ragged_token_counts():
+    """n_b from 0 to 16 in one batch, lengths around tile and page edges."""
+    lens_new = [0, 1, 2, 5, 16, 7, 1, 12]
+    prefix = [40, 0, 31, 33, 64, 500, 2, 95]
+    spec = BASE.replace(batch=len(lens_new), seed=87)
+    prob, layout, values = _verify_problem(spec, seq_lens=[p + n if p + n > 0 else 1 for p, n in zip(prefix, lens_new)],
+                                           extend_lens=lens_new)
+    _check(prob, layout, values, "ragged")
+
+
+def test_verify_matches_the_extend_path():
+    spec = BASE.replace(batch=5, seed=88)
+    prob, layout, values = _verify_problem(spec)
+    prob.attention_step(save=True, spec_mode="decode")
+    torch.cuda.synchronize()
+    dec = prob.out.clone()
+    prob.attention_step(save=False, spec_mode="prefill")
+    torch.cuda.synchronize()
+    max_abs, rel = errors(dec.float().cpu().numpy().astype(np.float64), prob.out_np())
+    assert max_abs <= 1e-2 and rel <= 5e-3, (max_abs, rel)
+
+
+def test_more_than_16_tokens_is_flagged():
+    spec = BASE.replace(batch=2, seed=89)
+    prob, layout, values = _verify_problem(spec, seq_lens=[300, 100], extend_lens=[20, 3])
+    prob.out.fill_(0.0)
+    prob.attention_step(save=True, spec_mode="decode")
+    torch.cuda.synchronize()
+    assert prob.md.status() & 1  # PKA_DEV_BAD_LENGTH
+    ref, _ = oracle_full(layout, values)
+    got = prob.out_np()
+    # the first 16 rows of request 0 and all rows of request 1 are computed
+    rows = list(range(16)) + [20, 21, 22]
+    max_abs, rel = errors(got[rows], ref[rows])
+    assert max_abs <= 2e-2 and rel <= 5e-3, (max_abs, rel)
+    assert np.all(got[16:20] == 0)
