@@ -219,11 +219,14 @@ def bench_decode_kernel(cfg_id: int, iters: int):
     return out
 
 
-def bench_extend(iters: int, gpu_state: bool = True):
+def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16"):
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
-    layout = workloads.make_layout(workloads.CONFIGS[4])
+    spec = workloads.CONFIGS[4]
+    if kv_dtype != spec.kv_dtype:
+        spec = spec.replace(name=spec.name.replace("extend_bf16", f"extend_{kv_dtype}kv"), kv_dtype=kv_dtype)
+    layout = workloads.make_layout(spec)
     prob = GpuProblem(layout)
     prob.attention_step(save=True)
     torch.cuda.synchronize()
@@ -237,7 +240,8 @@ def bench_extend(iters: int, gpu_state: bool = True):
            "TFLOPs": round(tf, 1), "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
            "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
            "ms_per_call": time_per_call(call, iters),
-           "variant": f"extend_mfma_kernel<{spec.head_dim}, scale>0, page {spec.page_size} >= 64>"}
+           "variant": f"extend_mfma_kernel<{spec.head_dim}, scale>0, page {spec.page_size} >= 64, "
+                      f"{spec.kv_dtype} cache>"}
     if gpu_state:
         out["gpu_state"] = gpu_state_under(call)
     del prob
@@ -288,7 +292,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extend / other decode figures and the clock and power sampling")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["extend", "decode3", "decode5", "copy", "gemm"], default=None,
+    ap.add_argument("--only", choices=["extend", "extend_fp8", "decode3", "decode5", "copy", "gemm"], default=None,
                     help="run one extra leg alone (for profiling) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -311,6 +315,8 @@ def main():
             res = bench_gemm(args.steps)
         elif args.only == "extend":
             res = bench_extend(args.steps, gpu_state=False)
+        elif args.only == "extend_fp8":
+            res = bench_extend(args.steps, gpu_state=False, kv_dtype="fp8")
         else:
             res = bench_decode_kernel(int(args.only[-1]), args.steps)
         print(json.dumps(res), flush=True)
@@ -348,7 +354,7 @@ def main():
     ms_meta = time_events(lambda i: probs[i % 2].metadata_step(), args.steps)
     nbytes = decode_algorithmic_bytes(layout)
     achieved = nbytes / (ms_attn * 1e-3) / 1e9
-    src = source_hash("decode.hip", "pka_internal.h", "fp8_encode.h")
+    src = source_hash("decode.hip", "pka_internal.h", "fp8.h")
     roof = {"bound": "hbm", "kernel": "decode_mfma_kernel + decode_merge_kernel (one attn_decode call)",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -383,6 +389,8 @@ def main():
         result["extend"]["frac_of_random_gemm"] = round(
             result["extend"]["TFLOPs"] / result["mfma_reference"]["random_TFLOPs"], 4)
         log(f"extend: {result['extend']}")
+        result["extend_fp8kv"] = bench_extend(args.steps, gpu_state=False, kv_dtype="fp8")
+        log(f"extend over an fp8 cache: {result['extend_fp8kv']}")
         log(f"bf16 GEMM reference: {result['mfma_reference']}")
         result["decode_configs"] = {}
         for cid in (3, 5):

@@ -179,7 +179,11 @@ pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* forward_extend: each new token attends causally to its request's prefix and
- * to the new tokens up to itself.  Same buffers as decode. */
+ * to the new tokens up to itself.  Same buffers as decode (the workspace is
+ * not used).  bf16 and fp8 e4m3fn caches run on MFMA (fp8 tiles are widened
+ * to bf16 exactly on their way into LDS; k_scale and v_scale are applied to
+ * the scores and the output), fp32 on the vector ALUs.  bf16 queries cover
+ * up to 128 query heads per KV head (checked by pka_create). */
 pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* q,
                            const void* k_pool, const void* v_pool, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);

@@ -357,8 +357,6 @@ pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* 
     if (md->mode == PKA_MODE_IDLE || md->batch == 0 || md->num_q_tokens == 0) return PKA_OK;
     if (!is_extend_like(md->mode))
         return fail(PKA_ERR_INVALID_ARG, "metadata was built for a decode batch; extend needs extend metadata");
-    if (ctx->cfg.kv_dtype == PKA_FP8_E4M3FN)
-        return fail(PKA_ERR_UNSUPPORTED, "extend over an fp8 cache is not supported");
     pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
     hipError_t e = pka::launch_extend(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->cfg.head_dim, a,
                                       (hipStream_t)stream);
@@ -391,8 +389,6 @@ pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_
     if (md->mode != mode)
         return fail(PKA_ERR_INVALID_ARG, "metadata was built for mode %d, forward called with %d",
                     (int)md->mode, (int)mode);
-    if (path == PKA_PATH_EXTEND && ctx->cfg.kv_dtype == PKA_FP8_E4M3FN)
-        return fail(PKA_ERR_UNSUPPORTED, "extend over an fp8 cache is not supported");
     if (path == PKA_PATH_DECODE) {  // check the workspace before anything is enqueued
         int32_t nwg = 0;
         if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;

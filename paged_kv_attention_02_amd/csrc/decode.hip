@@ -19,7 +19,7 @@
 // as whole 256-byte (bf16) rows per 16 lanes and transposed in registers with
 // v_perm_b32 (fp8: byte gather + v_cvt_scalef32_pk_bf16_fp8).  The token order
 // inside a tile is a permutation chosen so every operand lines up.
-#include "fp8_encode.h"
+#include "fp8.h"
 #include "pka_internal.h"
 
 namespace pka {
@@ -41,13 +41,6 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 }
 
 __device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// two fp8 e4m3fn codes (bytes 0,1 or, with HI, bytes 2,3 of w) -> two bf16
-// (exact: every e4m3fn value has a bf16 representation)
-template <bool HI>
-__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
-    return bits(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
 
 // Pool slot of token position `pos` of a request whose pages start at
 // kv_indices[page_base]; indices and page ids are clamped into their buffers.

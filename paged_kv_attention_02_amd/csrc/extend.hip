@@ -24,6 +24,7 @@
 // all query tiles of a request read.
 #include <type_traits>
 
+#include "fp8.h"
 #include "pka_internal.h"
 
 namespace pka {
@@ -126,7 +127,7 @@ __device__ inline void lds_dma16_s(const uint8_t* base, uint32_t voff, const uin
 //   cores run while the vector ALUs compute probabilities.
 // BIGPAGE (page size >= 64): a tile lies in one page, so its pool address is
 // a scalar and each lane only adds a fixed row offset.
-template <int D, bool POS, bool BIGPAGE>
+template <int D, bool POS, bool BIGPAGE, bool FP8>
 __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void extend_mfma_kernel(AttnArgs a) {
     using T = ExtTile<D>;
     constexpr int KSTEPS = D / 16;              // k-steps of q.k (32x32x16)
@@ -184,27 +185,38 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
 
     const int32_t kend = pb + tok_hi;  // keys 0 .. kend-1
     const int32_t ntiles = (kend + BN - 1) / BN;
-    const int32_t row_bytes = a.Hkv * T::ROWB;
-    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * T::ROWB;
-    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * T::ROWB;
+    constexpr int ESZ = FP8 ? 1 : 2;  // cache bytes per element
+    const int32_t row_bytes = a.Hkv * D * ESZ;
+    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * D * ESZ;
+    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * D * ESZ;
     const int32_t P = 1 << a.page_shift;
 
-    // Direct loads: wave instruction j of wave w fills LDS rows
-    // ROWS_PER_LOAD * (LOADS * w + j) ..; lane i writes physical chunk
-    // i % CPR of its row and fetches the logical chunk the swizzle puts
-    // there.  Rows past the last key repeat it.
+    // Moving a tile into LDS.  bf16: direct loads; wave instruction j of wave
+    // w fills LDS rows ROWS_PER_LOAD * (LOADS * w + j) ..; lane i writes
+    // physical chunk i % CPR of its row and fetches the logical chunk the
+    // swizzle puts there.  fp8: thread t loads 16-byte pieces t + 256 j of
+    // the tile's rows (D/16 per row) into registers and, once the current
+    // tile is done, writes them converted to bf16 into the same swizzled
+    // layout.  Rows past the last key repeat it.
+    constexpr int PPR = D / 16;                 // fp8 16-byte pieces per row
+    constexpr int NR = FP8 ? D / 64 : T::LOADS;  // rows moved per thread, tile and tensor
     const int pc = lane % T::CPR;
-    auto row_of = [&](int j) { return ROWS_PER_LOAD * (T::LOADS * wave + j) + lane / T::CPR; };
+    auto row_of = [&](int j) {
+        if constexpr (FP8) return (tid + 256 * j) / PPR;
+        else return ROWS_PER_LOAD * (T::LOADS * wave + j) + lane / T::CPR;
+    };
+    auto piece_of = [&](int j) { return (tid + 256 * j) % PPR; };  // fp8: piece within its row
     auto lds_row_block = [&](int j) { return (T::LOADS * wave + j) * 1024; };
-    // per-lane byte offsets of instruction j: the fetched chunk within a row
-    // (small pages), plus the row within the tile (BIGPAGE)
-    uint32_t koff[T::LOADS], voff[T::LOADS];
+    // per-thread byte offsets of move j: the fetched chunk within a row (small
+    // pages), plus the row within the tile (BIGPAGE)
+    uint32_t koff[NR], voff[NR];
     #pragma unroll
-    for (int j = 0; j < T::LOADS; ++j) {
+    for (int j = 0; j < NR; ++j) {
         const int r = row_of(j);
-        koff[j] = 16 * T::kchunk(r, pc) + (BIGPAGE ? r * row_bytes : 0);
-        voff[j] = 16 * T::vchunk(r, pc) + (BIGPAGE ? r * row_bytes : 0);
+        koff[j] = (FP8 ? 16 * piece_of(j) : 16 * T::kchunk(r, pc)) + (BIGPAGE ? r * row_bytes : 0);
+        voff[j] = (FP8 ? 16 * piece_of(j) : 16 * T::vchunk(r, pc)) + (BIGPAGE ? r * row_bytes : 0);
     }
+    u32x4_t rk[NR], rv[NR];  // fp8: tiles on their way to LDS
 
     // pool byte offset of a tile's first row (BIGPAGE; wave-uniform)
     auto tile_base = [&](int32_t pg, int32_t kt0) -> int64_t {
@@ -217,16 +229,23 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         return load_uniform(a.kv_indices, idx);
     };
     // BIGPAGE: one tensor's tile from page pg (V when is_v)
-    auto dma_big = [&](const uint8_t* src, const uint32_t (&off)[T::LOADS], bool is_v, int32_t pg,
+    auto dma_big = [&](const uint8_t* src, const uint32_t (&off)[NR], bool is_v, int32_t pg,
                        int32_t kt0, uint8_t* dst) {
         const uint8_t* tb = src + tile_base(pg, kt0);
         const int32_t lim = kend - 1 - kt0;  // last row of the tile holding a key
-        if (lim >= BN - 1) {
+        if constexpr (FP8) {
+            u32x4_t (&rg)[NR] = is_v ? rv : rk;
             #pragma unroll
-            for (int j = 0; j < T::LOADS; ++j) lds_dma16_s(tb, off[j], dst + lds_row_block(j));
+            for (int j = 0; j < NR; ++j) {
+                const uint32_t o = lim >= BN - 1 ? off[j] : (uint32_t)(min(row_of(j), lim) * row_bytes + 16 * piece_of(j));
+                rg[j] = __builtin_nontemporal_load((const u32x4_t*)(tb + o));
+            }
+        } else if (lim >= BN - 1) {
+            #pragma unroll
+            for (int j = 0; j < NR; ++j) lds_dma16_s(tb, off[j], dst + lds_row_block(j));
         } else {
             #pragma unroll
-            for (int j = 0; j < T::LOADS; ++j) {
+            for (int j = 0; j < NR; ++j) {
                 const int r = row_of(j);
                 const int ch = is_v ? T::vchunk(r, pc) : T::kchunk(r, pc);
                 lds_dma16_s(tb, (uint32_t)(min(r, lim) * row_bytes + 16 * ch), dst + lds_row_block(j));
@@ -235,26 +254,50 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     };
     // small pages: per-row slots; raw page ids are looked up an iteration
     // before the slots are formed
-    auto lookup = [&](int32_t kt0, int32_t (&pg)[T::LOADS], int32_t (&kp)[T::LOADS]) {
+    auto lookup = [&](int32_t kt0, int32_t (&pg)[NR], int32_t (&kp)[NR]) {
         #pragma unroll
-        for (int j = 0; j < T::LOADS; ++j) {
+        for (int j = 0; j < NR; ++j) {
             kp[j] = min(kt0 + row_of(j), kend - 1);
             int64_t idx = (int64_t)page_base + (kp[j] >> a.page_shift);
             idx = idx < a.kv_cap ? idx : a.kv_cap - 1;
             pg[j] = a.kv_indices[idx];
         }
     };
-    auto form_slots = [&](const int32_t (&pg)[T::LOADS], const int32_t (&kp)[T::LOADS],
-                          int32_t (&slot)[T::LOADS]) {
+    auto form_slots = [&](const int32_t (&pg)[NR], const int32_t (&kp)[NR], int32_t (&slot)[NR]) {
         #pragma unroll
-        for (int j = 0; j < T::LOADS; ++j)
+        for (int j = 0; j < NR; ++j)
             slot[j] = (min(max(pg[j], 0), a.num_pages - 1) << a.page_shift) | (kp[j] & (P - 1));
     };
-    auto dma_small = [&](const uint8_t* src, const uint32_t (&choff)[T::LOADS],
-                         const int32_t (&slot)[T::LOADS], uint8_t* dst) {
+    auto dma_small = [&](const uint8_t* src, const uint32_t (&choff)[NR], bool is_v,
+                         const int32_t (&slot)[NR], uint8_t* dst) {
+        if constexpr (FP8) {
+            u32x4_t (&rg)[NR] = is_v ? rv : rk;
+            #pragma unroll
+            for (int j = 0; j < NR; ++j)
+                rg[j] = __builtin_nontemporal_load((const u32x4_t*)(src + (int64_t)slot[j] * row_bytes + choff[j]));
+        } else {
+            #pragma unroll
+            for (int j = 0; j < NR; ++j)
+                lds_dma16(src + (int64_t)slot[j] * row_bytes + choff[j], dst + lds_row_block(j));
+        }
+    };
+    // fp8: write one tensor's tile (registers) into LDS as bf16; each 16-byte
+    // piece becomes logical chunks 2 p and 2 p + 1 of its row (exact)
+    auto f8_finish = [&](bool is_v, uint8_t* dst) {
+        const u32x4_t (&rg)[NR] = is_v ? rv : rk;
         #pragma unroll
-        for (int j = 0; j < T::LOADS; ++j)
-            lds_dma16(src + (int64_t)slot[j] * row_bytes + choff[j], dst + lds_row_block(j));
+        for (int j = 0; j < NR; ++j) {
+            const int r = row_of(j), p2 = 2 * piece_of(j);
+            const u32x4_t w = rg[j];
+            const u32x4_t c0 = {fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                                fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y)};
+            const u32x4_t c1 = {fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
+                                fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w)};
+            const int ph0 = is_v ? T::vchunk(r, p2) : T::kchunk(r, p2);
+            const int ph1 = is_v ? T::vchunk(r, p2 + 1) : T::kchunk(r, p2 + 1);
+            *(u32x4_t*)(dst + r * T::ROWB + 16 * ph0) = c0;
+            *(u32x4_t*)(dst + r * T::ROWB + 16 * ph1) = c1;
+        }
     };
 
     // V^T operand: lane group G = lane/16 reads keys 4 (G/2) + s16/4 (+ 16 ks
@@ -288,29 +331,41 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
 
     // prologue: K(0), V(0), K(1) resident, S(0) computed
     int32_t pgK = 0, pgV = 0;        // BIGPAGE: pages of tiles t+2 (K) and t+1 (V)
-    int32_t rawK[T::LOADS], kpK[T::LOADS], slotK[T::LOADS], slotV[T::LOADS];  // small pages
+    int32_t rawK[NR], kpK[NR], slotK[NR], slotV[NR];  // small pages
     if constexpr (BIGPAGE) {
         const int32_t p0 = page_of_tile(0);
         dma_big(kbase, koff, false, p0, 0, sK0);
         dma_big(vbase, voff, true, p0, 0, sV0);
+        if constexpr (FP8) {
+            f8_finish(false, sK0);
+            f8_finish(true, sV0);
+        }
         if (ntiles > 1) {
             const int32_t p1 = page_of_tile(BN);
             dma_big(kbase, koff, false, p1, BN, sK1);
+            if constexpr (FP8) f8_finish(false, sK1);
             pgV = p1;
         }
         if (ntiles > 2) pgK = page_of_tile(2 * BN);
     } else {
-        int32_t s0[T::LOADS];
+        int32_t s0[NR];
         lookup(0, rawK, kpK);
         form_slots(rawK, kpK, s0);
-        dma_small(kbase, koff, s0, sK0);
-        dma_small(vbase, voff, s0, sV0);
+        dma_small(kbase, koff, false, s0, sK0);
+        dma_small(vbase, voff, true, s0, sV0);
+        if constexpr (FP8) {
+            f8_finish(false, sK0);
+            f8_finish(true, sV0);
+        }
         lookup(BN, rawK, kpK);
         form_slots(rawK, kpK, slotV);
-        if (ntiles > 1) dma_small(kbase, koff, slotV, sK1);
+        if (ntiles > 1) {
+            dma_small(kbase, koff, false, slotV, sK1);
+            if constexpr (FP8) f8_finish(false, sK1);
+        }
         lookup(2 * BN, rawK, kpK);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    if constexpr (!FP8) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the direct loads landed
     __syncthreads();
     #pragma unroll
     for (int q = 0; q < KSTEPS * SB; ++q) qk_mfma(sK0, q, SA);
@@ -324,20 +379,22 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         uint8_t* vdst = ODD ? sV0 : sV1;        // V(t+1)
         const int32_t kt0 = t * BN;
 
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): K(t+1), V(t) and lookups have landed
-        __syncthreads();                       // ... for every wave; iteration t-1 is done
+        // bf16: K(t+1), V(t) and the lookups have landed (fp8 tiles were
+        // written to LDS at the end of the previous iteration)
+        if constexpr (!FP8) __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();  // ... for every wave; iteration t-1 is done
         if constexpr (BIGPAGE) {
             if (t + 2 < ntiles) dma_big(kbase, koff, false, pgK, kt0 + 2 * BN, kdst);
             if (NEXT) dma_big(vbase, voff, true, pgV, kt0 + BN, vdst);
             pgV = pgK;
             if (t + 3 < ntiles) pgK = page_of_tile(kt0 + 3 * BN);
         } else {
-            if (NEXT) dma_small(vbase, voff, slotV, vdst);
+            if (NEXT) dma_small(vbase, voff, true, slotV, vdst);
             if (t + 2 < ntiles) {
                 form_slots(rawK, kpK, slotK);
-                dma_small(kbase, koff, slotK, kdst);
+                dma_small(kbase, koff, false, slotK, kdst);
                 #pragma unroll
-                for (int j = 0; j < T::LOADS; ++j) slotV[j] = slotK[j];
+                for (int j = 0; j < NR; ++j) slotV[j] = slotK[j];
                 lookup(kt0 + 3 * BN, rawK, kpK);
             }
         }
@@ -407,6 +464,12 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 O[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
             }
         }
+        // fp8: the next tiles go into the stages this iteration did not read;
+        // the next iteration's barrier publishes them
+        if constexpr (FP8) {
+            if (t + 2 < ntiles) f8_finish(false, kdst);
+            if (NEXT) f8_finish(true, vdst);
+        }
     };
 
     using F_ = std::integral_constant<bool, false>;
@@ -426,7 +489,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     // finish: the two lanes of a column hold halves of the sums
     const float ltot = sum_halves(lsum);
     if (!col_ok) return;
-    const float inv = 1.0f / ltot;
+    const float inv = a.v_scale / ltot;  // v_scale: fp8 V dequantisation (1 otherwise)
     __bf16* orow = (__bf16*)a.out + ((int64_t)(q0 + ctok) * a.Hq + head) * D;
     #pragma unroll
     for (int c = 0; c < VC; ++c)
@@ -519,15 +582,17 @@ hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hi
     const dim3 grid((unsigned)(items * a.Hkv));
     const bool pos = a.scale_log2 > 0.f;
     const bool big = P >= BN;
-#define PKA_EXT(D_, POS_, BIG_) \
-    hipLaunchKernelGGL((extend_mfma_kernel<D_, POS_, BIG_>), grid, dim3(64 * EXT_WAVES), 0, s, a)
-    if (D == 128) {
-        if (pos) { if (big) PKA_EXT(128, true, true); else PKA_EXT(128, true, false); }
-        else { if (big) PKA_EXT(128, false, true); else PKA_EXT(128, false, false); }
-    } else {
-        if (pos) { if (big) PKA_EXT(64, true, true); else PKA_EXT(64, true, false); }
-        else { if (big) PKA_EXT(64, false, true); else PKA_EXT(64, false, false); }
-    }
+#define PKA_EXT(D_, POS_, BIG_, F8_) \
+    hipLaunchKernelGGL((extend_mfma_kernel<D_, POS_, BIG_, F8_>), grid, dim3(64 * EXT_WAVES), 0, s, a)
+#define PKA_EXT_D(D_, F8_)                                                              \
+    do {                                                                                \
+        if (pos) { if (big) PKA_EXT(D_, true, true, F8_); else PKA_EXT(D_, true, false, F8_); }   \
+        else { if (big) PKA_EXT(D_, false, true, F8_); else PKA_EXT(D_, false, false, F8_); }     \
+    } while (0)
+    const bool f8 = kv == PKA_FP8_E4M3FN;
+    if (D == 128) { if (f8) PKA_EXT_D(128, true); else PKA_EXT_D(128, false); }
+    else { if (f8) PKA_EXT_D(64, true); else PKA_EXT_D(64, false); }
+#undef PKA_EXT_D
 #undef PKA_EXT
     return hipGetLastError();
 }

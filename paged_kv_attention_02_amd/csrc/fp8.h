@@ -1,4 +1,5 @@
-// fp32 -> OCP e4m3fn encoding shared by the cache writers (gfx950 device code).
+// OCP e4m3fn conversions shared by the kernels (gfx950 device code): the
+// encoder of the cache writers and the exact decoder of the readers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,6 +30,13 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float inv) {
     return e4m3fn_from_f32(bf16_lo(w0) * inv) | (e4m3fn_from_f32(bf16_hi(w0) * inv) << 8) |
            (e4m3fn_from_f32(bf16_lo(w1) * inv) << 16) | (e4m3fn_from_f32(bf16_hi(w1) * inv) << 24);
+}
+
+// Two e4m3fn codes (bytes 0,1 or, with HI, bytes 2,3 of w) -> two bf16, exact
+// (every e4m3fn value has a bf16 representation).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 }  // namespace pka

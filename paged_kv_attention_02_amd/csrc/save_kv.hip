@@ -4,7 +4,7 @@
 // the cache before attention reads it ("[SGLang] Hybrid Attention", forward
 // delegation).  Each thread moves 8 elements of one row; grid.y picks K or V.
 // An fp8 e4m3fn cache stores round-to-nearest-even(sat(x * fp32(1/scale))).
-#include "fp8_encode.h"
+#include "fp8.h"
 #include "pka_internal.h"
 
 namespace pka {

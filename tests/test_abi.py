@@ -116,11 +116,11 @@ def test_calls_refuse_bad_arguments_without_touching_the_device():
     # IDLE is a no-op that needs no buffers
     assert lib.pka_forward(ctx.handle, 2, 0, ctypes.byref(md), None, None, None, 1, None, None,
                            None, None, None, 0, None) == 0
-    # extend over an fp8 cache is refused before any launch
+    # extend on metadata built for a decode batch is refused before any launch
     ctx8 = pka.Context(32, 8, 128, 16, 100, "bf16", "fp8", 0.1, 0.01, 0.01)
     fake = 1 << 20  # aligned, never dereferenced: validation fails first
-    md8 = pka.BatchStruct(0, 4, 8, 40, fake, fake, fake, fake, fake, fake)
+    md8 = pka.BatchStruct(1, 4, 4, 40, fake, fake, fake, fake, fake, fake)
     st = lib.pka_attn_extend(ctx8.handle, ctypes.byref(md8), fake, fake, fake, fake, None, None, 0, None)
-    assert st == -2
+    assert st == -1
     for s in (0, -1, -2, -3, -4):
         assert lib.pka_status_string(s)

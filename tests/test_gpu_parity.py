@@ -161,8 +161,8 @@ def test_attention_parity_llama_decode_full():
     np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=2e-3)
 
 
-def _sampled(cfg, requests, heads=None, tokens=None):
-    spec = workloads.CONFIGS[cfg]
+def _sampled(cfg, requests, heads=None, tokens=None, spec=None):
+    spec = workloads.CONFIGS[cfg] if spec is None else spec
     layout = workloads.make_layout(spec)
     values = workloads.make_values(layout, device="cuda")
     prob = GpuProblem(layout, values)
@@ -182,7 +182,7 @@ def _sampled(cfg, requests, heads=None, tokens=None):
         g_all.append(out[rows][:, hs, :])
         r_all.append(ro)
         np.testing.assert_allclose(lse[rows][:, hs], rl, rtol=0, atol=2e-3)
-    _check_close(f"config{cfg} requests {reqs}", np.concatenate(g_all), np.concatenate(r_all),
+    _check_close(f"{spec.name} requests {reqs}", np.concatenate(g_all), np.concatenate(r_all),
                  spec.kv_dtype)
 
 
