@@ -16,7 +16,8 @@
 namespace pka {
 namespace {
 
-constexpr int SCAN_THREADS = 1024;
+constexpr int SORT_MAX = 2048;  // extend items sorted in LDS (heaviest first)
+constexpr int SCAN_THREADS = 256;  // small workgroups: cheap barriers, more of them share the gather
 
 // Inclusive block scan of three int64 values: a shuffle scan inside each
 // wave, then the wave totals (two barriers in all).
@@ -51,7 +52,8 @@ __device__ inline void block_scan3(int64_t& x0, int64_t& x1, int64_t& x2, int64_
 }
 
 __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
-    __shared__ int64_t sh[3 * SCAN_THREADS];  // scan scratch, then sorted extend items
+    // scan scratch, then the sorted extend items (at most SORT_MAX)
+    __shared__ int64_t sh[3 * SCAN_THREADS > SORT_MAX ? 3 * SCAN_THREADS : SORT_MAX];
     __shared__ int64_t carry[3];
     __shared__ int32_t s_status;
     // per-request prefixes kept in LDS when the gather is fused (B <= FUSE_MAX_B)
@@ -256,7 +258,6 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         int32_t count = s_count;
         if (count > cap) { flags |= PKA_DEV_CAPACITY; count = (int32_t)cap; }
         // sort by weight (descending) with a bitonic sort in LDS when small
-        constexpr int SORT_MAX = 2048;
         __shared__ uint32_t keys[SORT_MAX];
         if (count <= SORT_MAX && count > 1) {
             int n2 = 1;
