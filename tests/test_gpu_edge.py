@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import workloads
-from tests.oracle_ref import TOL, errors, oracle_full
+from tests.oracle_ref import LSE_ATOL, TOL, errors, oracle_full
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,7 @@ def run_and_check(spec, seq_lens=None, extend_lens=None, spec_mode="prefill", mo
     print(f"[parity] {spec.name} L={list(layout.seq_lens)[:6]}: max_abs={max_abs:.2e} rel={rel:.2e}", flush=True)
     assert np.all(np.isfinite(got))
     assert max_abs <= tol_abs and rel <= tol_rel, (max_abs, rel)
-    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=2e-3)
+    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=LSE_ATOL)
     return prob, layout, values
 
 

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import workloads
-from tests.oracle_ref import TOL, errors, oracle_full, oracle_pools, oracle_requests, raw_np
+from tests.oracle_ref import LSE_ATOL, TOL, errors, oracle_full, oracle_pools, oracle_requests, raw_np
 
 pytestmark = pytest.mark.gpu
 
@@ -145,7 +145,7 @@ def test_attention_parity_small(name):
     assert prob.md.status() == 0
     ref_out, ref_lse = oracle_full(layout, values)
     _check_close(name, prob.out_np(), ref_out, spec.kv_dtype)
-    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=2e-3)
+    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 def test_attention_parity_llama_decode_full():
@@ -158,7 +158,7 @@ def test_attention_parity_llama_decode_full():
     assert prob.md.status() == 0
     ref_out, ref_lse = oracle_full(layout, values)
     _check_close("config2", prob.out_np(), ref_out, spec.kv_dtype)
-    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=2e-3)
+    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 def _sampled(cfg, requests, heads=None, tokens=None, spec=None):
@@ -181,7 +181,7 @@ def _sampled(cfg, requests, heads=None, tokens=None, spec=None):
         rows = qo[b] + ts
         g_all.append(out[rows][:, hs, :])
         r_all.append(ro)
-        np.testing.assert_allclose(lse[rows][:, hs], rl, rtol=0, atol=2e-3)
+        np.testing.assert_allclose(lse[rows][:, hs], rl, rtol=0, atol=LSE_ATOL)
     _check_close(f"{spec.name} requests {reqs}", np.concatenate(g_all), np.concatenate(r_all),
                  spec.kv_dtype)
 

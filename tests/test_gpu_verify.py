@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads
-from tests.oracle_ref import TOL, errors, oracle_full
+from tests.oracle_ref import LSE_ATOL, TOL, errors, oracle_full
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def _check(prob, layout, values, name):
     assert status == 0, status
     assert np.all(np.isfinite(got))
     assert max_abs <= tol_abs and rel <= tol_rel, (max_abs, rel)
-    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=2e-3)
+    np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=LSE_ATOL)
 
 
 BASE = workloads.Spec("verify", "extend", 6, 32, 8, 128, 16, "bf16", "bf16", seed=81,
