@@ -56,9 +56,9 @@ def lib():
         L.oracle_metadata.argtypes = [i32, vp, vp, vp, i64, i32, i32, i32, vp, vp, i64, vp, vp,
                                       vp, i64]
         L.oracle_metadata.restype = ctypes.c_int
-        L.oracle_save_kv.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, f32, f32, vp, vp]
+        L.oracle_save_kv.argtypes = [i64, i32, i32, i32, i32, i32, vp, vp, vp, f32, f32, vp, vp]
         L.oracle_save_kv.restype = ctypes.c_int
-        L.oracle_attention.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i64, i32, i32, vp,
+        L.oracle_attention.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, i32, i32, vp,
                                        i32, vp, vp, f64, f64, f64, i64, vp, vp, vp, i32]
         L.oracle_attention.restype = ctypes.c_int
         L.oracle_pool_bytes.argtypes = [i64, i64, i64, i64]
@@ -149,12 +149,14 @@ def metadata(seq_lens, extend_lens, page_table, page_size: int, num_pages: int) 
 
 def save_kv(slots, k_new, v_new, src_dtype: str, kv_dtype: str, k_pool, v_pool,
             k_scale: float = 1.0, v_scale: float = 1.0) -> None:
-    """Scatter new rows [N, Hkv, D] into the pools in place."""
+    """Scatter new rows (K [N, Hkv, Dk], V [N, Hkv, Dv]) into the pools in place."""
     slots = np.ascontiguousarray(slots, dtype=np.int32)
     k_new, v_new = _raw(k_new, src_dtype), _raw(v_new, src_dtype)
     assert k_pool.flags["C_CONTIGUOUS"] and v_pool.flags["C_CONTIGUOUS"]
-    N, Hkv, D = k_new.shape
-    rc = lib().oracle_save_kv(N, Hkv, D, DT_CODE[src_dtype], DT_CODE[kv_dtype], _ptr(slots),
+    N, Hkv, Dk = k_new.shape
+    Dv = v_new.shape[2]
+    assert k_pool.shape[1:] == (Hkv, Dk) and v_pool.shape[1:] == (Hkv, Dv)
+    rc = lib().oracle_save_kv(N, Hkv, Dk, Dv, DT_CODE[src_dtype], DT_CODE[kv_dtype], _ptr(slots),
                               _ptr(k_new), _ptr(v_new), float(k_scale), float(v_scale),
                               _ptr(k_pool), _ptr(v_pool))
     if rc != 0:
@@ -166,26 +168,29 @@ def save_kv(slots, k_new, v_new, src_dtype: str, kv_dtype: str, k_pool, v_pool,
 def attention(seq_lens, extend_lens, page_table, page_size: int, num_pages: int, q, q_dtype: str,
               k_pool, v_pool, kv_dtype: str, scale: float, k_scale: float = 1.0,
               v_scale: float = 1.0, sel=None, threads: int = 0):
-    """fp64 attention.  q: [N, Hq, D] raw storage; pools: [slots, Hkv, D] raw.
+    """fp64 attention.  q: [N, Hq, Dk] raw storage; pools: K [slots, Hkv, Dk],
+    V [slots, Hkv, Dv] raw (the value width may differ from the key width).
 
-    Returns (out, lse): out [N, Hq, D] and lse [N, Hq] float64, or, with
-    ``sel`` (flat indices token*Hq + head), out [len(sel), D], lse [len(sel)].
+    Returns (out, lse): out [N, Hq, Dv] and lse [N, Hq] float64, or, with
+    ``sel`` (flat indices token*Hq + head), out [len(sel), Dv], lse [len(sel)].
     """
     seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
     ext = None if extend_lens is None else np.ascontiguousarray(extend_lens, dtype=np.int32)
     pt = np.ascontiguousarray(page_table, dtype=np.int32)
     q = _raw(q, q_dtype)
     k_pool, v_pool = _raw(k_pool, kv_dtype), _raw(v_pool, kv_dtype)
-    N, Hq, D = q.shape
+    N, Hq, Dk = q.shape
     Hkv = k_pool.shape[1]
+    Dv = v_pool.shape[2]
+    assert k_pool.shape[2] == Dk and v_pool.shape[1] == Hkv
     if sel is None:
         n_sel, sel_arr = N * Hq, None
     else:
         sel_arr = np.ascontiguousarray(sel, dtype=np.int64)
         n_sel = sel_arr.size
-    out = np.empty((n_sel, D), dtype=np.float64)
+    out = np.empty((n_sel, Dv), dtype=np.float64)
     lse = np.empty((n_sel,), dtype=np.float64)
-    rc = lib().oracle_attention(seq_lens.shape[0], Hq, Hkv, D, int(page_size), _ptr(seq_lens),
+    rc = lib().oracle_attention(seq_lens.shape[0], Hq, Hkv, Dk, Dv, int(page_size), _ptr(seq_lens),
                                 _ptr(ext), _ptr(pt), pt.shape[1], int(num_pages),
                                 DT_CODE[q_dtype], _ptr(q), DT_CODE[kv_dtype], _ptr(k_pool),
                                 _ptr(v_pool), float(scale), float(k_scale), float(v_scale), n_sel,
@@ -193,5 +198,5 @@ def attention(seq_lens, extend_lens, page_table, page_size: int, num_pages: int,
     if rc != 0:
         raise ValueError("oracle_attention rejected the input")
     if sel is None:
-        return out.reshape(N, Hq, D), lse.reshape(N, Hq)
+        return out.reshape(N, Hq, Dv), lse.reshape(N, Hq)
     return out, lse

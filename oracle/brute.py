@@ -45,8 +45,9 @@ def attention(seq_lens: Sequence[int], extend_lens, page_table, page_size: int, 
               k_pool, v_pool, kv_dtype: str, scale: float, k_scale: float = 1.0,
               v_scale: float = 1.0):
     """Returns (out, lse) as nested lists out[token][head][d], lse[token][head]."""
-    N, Hq, D = q.shape
+    N, Hq, D = q.shape            # key width D; values may be wider or narrower
     Hkv = k_pool.shape[1]
+    Dv = v_pool.shape[2]
     G = Hq // Hkv
     qv = decode_storage(q, q_dtype)
     kv = decode_storage(k_pool, kv_dtype, k_scale)
@@ -66,15 +67,14 @@ def attention(seq_lens: Sequence[int], extend_lens, page_table, page_size: int, 
                 scores, vrows = [], []
                 for t in range(pos + 1):
                     slot = int(page_table[b][t // page_size]) * page_size + t % page_size
-                    base = (slot * Hkv + g) * D
-                    krow = kv[base:base + D]
+                    krow = kv[(slot * Hkv + g) * D:(slot * Hkv + g + 1) * D]
                     scores.append(scale * math.fsum(a * c for a, c in zip(qrow, krow)))
-                    vrows.append(vv[base:base + D])
+                    vrows.append(vv[(slot * Hkv + g) * Dv:(slot * Hkv + g + 1) * Dv])
                 m = max(scores)
                 w = [math.exp(s - m) for s in scores]
                 z = math.fsum(w)
                 row_o.append([math.fsum(w[t] * vrows[t][d] for t in range(len(w))) / z
-                              for d in range(D)])
+                              for d in range(Dv)])
                 row_l.append(m + math.log(z))
             out.append(row_o)
             lse.append(row_l)

@@ -169,24 +169,26 @@ int oracle_metadata(int32_t B, const int32_t* seq_lens, const int32_t* extend_le
 /* --------------------------------------------------------------- save_kv */
 
 /*
- * Write new K/V rows [N, Hkv, D] (source dtype fp32 or bf16) into the pools
- * [slots, Hkv, D] at the given slots.  Same dtype: the bits are copied.
- * bf16 -> fp8: oracle_fp8_quantize with the per-tensor scale.
+ * Write new K rows [N, Hkv, Dk] and V rows [N, Hkv, Dv] (source dtype fp32 or
+ * bf16) into the pools [slots, Hkv, Dk] and [slots, Hkv, Dv] at the given
+ * slots (K and V may have different head widths).  Same dtype: the bits are
+ * copied.  bf16 -> fp8: oracle_fp8_quantize with the per-tensor scale.
  */
-int oracle_save_kv(int64_t N, int32_t Hkv, int32_t D, int32_t src_dtype, int32_t kv_dtype,
-                   const int32_t* slots, const void* k_new, const void* v_new, float k_scale,
-                   float v_scale, void* k_pool, void* v_pool) {
-    int64_t row = (int64_t)Hkv * D;
+int oracle_save_kv(int64_t N, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t src_dtype,
+                   int32_t kv_dtype, const int32_t* slots, const void* k_new, const void* v_new,
+                   float k_scale, float v_scale, void* k_pool, void* v_pool) {
+    int64_t krow = (int64_t)Hkv * Dk, vrow = (int64_t)Hkv * Dv;
     for (int64_t j = 0; j < N; ++j) {
-        int64_t dst = (int64_t)slots[j] * row;
-        int64_t src = j * row;
+        int64_t slot = slots[j];
         if (kv_dtype == src_dtype) {
             size_t eb = kv_dtype == OR_F32 ? 4 : 2;
-            memcpy((char*)k_pool + dst * eb, (const char*)k_new + src * eb, row * eb);
-            memcpy((char*)v_pool + dst * eb, (const char*)v_new + src * eb, row * eb);
+            memcpy((char*)k_pool + slot * krow * eb, (const char*)k_new + j * krow * eb, krow * eb);
+            memcpy((char*)v_pool + slot * vrow * eb, (const char*)v_new + j * vrow * eb, vrow * eb);
         } else if (src_dtype == OR_BF16 && kv_dtype == OR_FP8) {
-            oracle_fp8_quantize(row, (const uint16_t*)k_new + src, k_scale, (uint8_t*)k_pool + dst);
-            oracle_fp8_quantize(row, (const uint16_t*)v_new + src, v_scale, (uint8_t*)v_pool + dst);
+            oracle_fp8_quantize(krow, (const uint16_t*)k_new + j * krow, k_scale,
+                                (uint8_t*)k_pool + slot * krow);
+            oracle_fp8_quantize(vrow, (const uint16_t*)v_new + j * vrow, v_scale,
+                                (uint8_t*)v_pool + slot * vrow);
         } else {
             return -1;
         }
@@ -198,11 +200,13 @@ int oracle_save_kv(int64_t N, int32_t Hkv, int32_t D, int32_t src_dtype, int32_t
 
 /*
  * Attention for selected (query token, head) pairs.  sel[i] = token * Hq + h;
- * sel == NULL means every pair in order.  out: [n_sel, D], lse: [n_sel]
- * (natural log of the softmax denominator including the max).
- * extend_lens == NULL means decode (one query per request, at position L-1).
+ * sel == NULL means every pair in order.  Queries and keys have head width
+ * Dk, values and outputs Dv (a model may give K and V different widths).
+ * out: [n_sel, Dv], lse: [n_sel] (natural log of the softmax denominator
+ * including the max).  extend_lens == NULL means decode (one query per
+ * request, at position L-1).
  */
-int oracle_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+int oracle_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t Dk, int32_t Dv, int32_t P,
                      const int32_t* seq_lens, const int32_t* extend_lens,
                      const int32_t* page_table, int64_t stride, int32_t num_pages,
                      int32_t q_dtype, const void* q, int32_t kv_dtype, const void* k_pool,
@@ -241,8 +245,8 @@ int oracle_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
 #endif
     {
         double* s = (double*)malloc(sizeof(double) * max_len);
-        double* acc = (double*)malloc(sizeof(double) * D);
-        double* qv = (double*)malloc(sizeof(double) * D);
+        double* acc = (double*)malloc(sizeof(double) * Dv);
+        double* qv = (double*)malloc(sizeof(double) * Dk);
         if (!s || !acc || !qv) bad = 1;
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 1)
@@ -258,35 +262,35 @@ int oracle_attention(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
             int64_t n = extend_lens ? extend_lens[b] : 1;
             int64_t pos = L - n + tok_idx[j]; /* bottom-right causal alignment */
             int32_t g = h / G;                /* grouped query heads */
-            for (int32_t d = 0; d < D; ++d)
-                qv[d] = load_value(q_dtype, q, (j * Hq + h) * (int64_t)D + d, 1.0);
+            for (int32_t d = 0; d < Dk; ++d)
+                qv[d] = load_value(q_dtype, q, (j * Hq + h) * (int64_t)Dk + d, 1.0);
             /* pass 1: scores s_t = scale * q . k_t over the explicit page gather */
             double m = -INFINITY;
             for (int64_t t = 0; t <= pos; ++t) {
                 int32_t pg = page_table[b * stride + t / P];
                 if (pg < 0 || pg >= num_pages) { bad = 1; break; }
                 int64_t slot = (int64_t)pg * P + t % P;
-                int64_t base = (slot * Hkv + g) * (int64_t)D;
+                int64_t base = (slot * Hkv + g) * (int64_t)Dk;
                 double dot = 0.0;
-                for (int32_t d = 0; d < D; ++d)
+                for (int32_t d = 0; d < Dk; ++d)
                     dot += qv[d] * load_value(kv_dtype, k_pool, base + d, k_scale);
                 s[t] = scale * dot;
                 if (s[t] > m) m = s[t];
             }
             /* pass 2: weights, normaliser, weighted sum of V */
             double Z = 0.0;
-            for (int32_t d = 0; d < D; ++d) acc[d] = 0.0;
+            for (int32_t d = 0; d < Dv; ++d) acc[d] = 0.0;
             for (int64_t t = 0; t <= pos; ++t) {
                 int32_t pg = page_table[b * stride + t / P];
                 if (pg < 0 || pg >= num_pages) break;
                 int64_t slot = (int64_t)pg * P + t % P;
-                int64_t base = (slot * Hkv + g) * (int64_t)D;
+                int64_t base = (slot * Hkv + g) * (int64_t)Dv;
                 double w = exp(s[t] - m);
                 Z += w;
-                for (int32_t d = 0; d < D; ++d)
+                for (int32_t d = 0; d < Dv; ++d)
                     acc[d] += w * load_value(kv_dtype, v_pool, base + d, v_scale);
             }
-            for (int32_t d = 0; d < D; ++d) out[it * D + d] = acc[d] / Z;
+            for (int32_t d = 0; d < Dv; ++d) out[it * Dv + d] = acc[d] / Z;
             if (lse) lse[it] = m + log(Z);
         }
         free(s);

@@ -48,12 +48,12 @@ def place(seq_lens, P, pool_pages=None, rng=RNG, shuffle=True):
 
 def build_pools(seq_lens, table, P, pool_pages, k_all, v_all, src, kv, ks=1.0, vs=1.0):
     """Oracle cache write of every token; unused slots hold NaN."""
-    Hkv, D = k_all.shape[1], k_all.shape[2]
+    Hkv, Dk, Dv = k_all.shape[1], k_all.shape[2], v_all.shape[2]
     md = oracle.metadata(seq_lens, seq_lens, table, P, pool_pages)
     nanbits = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}[kv]
     dt = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[kv]
-    kp = np.full((pool_pages * P, Hkv, D), nanbits, dtype=dt)
-    vp = np.full((pool_pages * P, Hkv, D), nanbits, dtype=dt)
+    kp = np.full((pool_pages * P, Hkv, Dk), nanbits, dtype=dt)
+    vp = np.full((pool_pages * P, Hkv, Dv), nanbits, dtype=dt)
     oracle.save_kv(md["out_cache_loc"], k_all, v_all, src, kv, kp, vp, ks, vs)
     return kp, vp
 
@@ -70,12 +70,13 @@ def run(seq_lens, ext, P, q, k_all, v_all, dtype="f32", kv=None, scale=0.125, sh
 
 # ------------------------------------------------------------ closed forms
 
+@pytest.mark.parametrize("dv", [16, 8, 24])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_one_cached_token_returns_v(dtype):
-    D, Hq, Hkv = 16, 4, 2
+def test_one_cached_token_returns_v(dtype, dv):
+    D, Hq, Hkv = 16, 4, 2  # key width D; value width dv (may differ)
     q = storage(grid_values((1, Hq, D)), dtype)
     k = storage(grid_values((1, Hkv, D)), dtype)
-    v = storage(grid_values((1, Hkv, D)), dtype)
+    v = storage(grid_values((1, Hkv, dv)), dtype)
     out, lse = run([1], None, 1, q, k, v, dtype)
     vv = (v.astype(np.float64) if dtype == "f32" else oracle.bf16_value(v))
     qq = (q.astype(np.float64) if dtype == "f32" else oracle.bf16_value(q))
@@ -87,13 +88,14 @@ def test_one_cached_token_returns_v(dtype):
         assert lse[0, h] == pytest.approx(s0, abs=1e-15)
 
 
+@pytest.mark.parametrize("dv", [32, 12])
 @pytest.mark.parametrize("scale", [0.125, 0.0])
-def test_identical_keys_give_mean_of_v(scale):
+def test_identical_keys_give_mean_of_v(scale, dv):
     L, D, Hq, Hkv = 57, 32, 2, 1
     q = storage(grid_values((1, Hq, D)), "f32")
     k1 = grid_values((1, Hkv, D))
     k = storage(np.repeat(k1, L, axis=0), "f32")
-    v = storage(grid_values((L, Hkv, D)), "f32")
+    v = storage(grid_values((L, Hkv, dv)), "f32")
     out, lse = run([L], None, 4, q, k, v, "f32", scale=scale)
     mean_v = v.astype(np.float64).mean(axis=0)[0]
     for h in range(Hq):
@@ -215,6 +217,10 @@ CASES = [
     dict(seq_lens=[11, 6], ext=[4, 6], P=2, Hq=2, Hkv=2, D=8, dtype="bf16", kv="bf16"),
     dict(seq_lens=[9, 14], ext=None, P=4, Hq=4, Hkv=2, D=8, dtype="bf16", kv="fp8"),
     dict(seq_lens=[10], ext=[3], P=8, Hq=6, Hkv=3, D=4, dtype="bf16", kv="fp8"),
+    # value width different from the key width
+    dict(seq_lens=[7, 13], ext=[2, 5], P=4, Hq=4, Hkv=2, D=12, DV=8, dtype="bf16", kv="bf16"),
+    dict(seq_lens=[6, 9], ext=None, P=2, Hq=2, Hkv=1, D=6, DV=10, dtype="f32", kv="f32"),
+    dict(seq_lens=[11], ext=[4], P=4, Hq=4, Hkv=2, D=8, DV=4, dtype="bf16", kv="fp8"),
 ]
 
 
@@ -228,7 +234,7 @@ def test_brute_force_agrees(case):
     q = storage(rng.standard_normal((N, case["Hq"], case["D"])).astype(np.float32)
                 .astype(np.float64) if dt == "f32" else grid_values((N, case["Hq"], case["D"]), rng=rng), dt)
     k = storage(grid_values((T, case["Hkv"], case["D"]), rng=rng), dt)
-    v = storage(grid_values((T, case["Hkv"], case["D"]), rng=rng), dt)
+    v = storage(grid_values((T, case["Hkv"], case.get("DV", case["D"])), rng=rng), dt)
     ks = vs = 1.0
     if case["kv"] == "fp8":
         ks, vs = 0.0078125 * 1.3, 0.0078125 * 0.7
@@ -249,16 +255,18 @@ def _sdpa_reference(q, k, v, mask, scale):
         attn_mask=None if mask is None else torch.from_numpy(mask), scale=scale).numpy()
 
 
-def test_torch_sdpa_decode_and_extend_fp64():
+@pytest.mark.parametrize("dv", [16, 24])
+def test_torch_sdpa_decode_and_extend_fp64(dv):
     """P = 1 with contiguous slots and K/V heads repeated per group is torch's
-    dense SDPA: no mask for decode, an explicit bottom-right mask for extend."""
+    dense SDPA: no mask for decode, an explicit bottom-right mask for extend.
+    SDPA takes a value width different from the key width as well."""
     rng = np.random.default_rng(5)
     Hq, Hkv, D, G = 4, 2, 16, 2
     for mode in ("decode", "extend"):
         L, n = 23, (1 if mode == "decode" else 7)
         q = storage(rng.standard_normal((n, Hq, D)).astype(np.float32).astype(np.float64), "f32")
         k = storage(rng.standard_normal((L, Hkv, D)).astype(np.float32).astype(np.float64), "f32")
-        v = storage(rng.standard_normal((L, Hkv, D)).astype(np.float32).astype(np.float64), "f32")
+        v = storage(rng.standard_normal((L, Hkv, dv)).astype(np.float32).astype(np.float64), "f32")
         table = np.arange(L, dtype=np.int32)[None, :]
         ext = None if mode == "decode" else [n]
         out, _ = run([L], ext, 1, q, k, v, "f32", scale=0.25, table=table, pool_pages=L)
