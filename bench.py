@@ -33,28 +33,30 @@ def log(msg):
 
 
 def kv_bytes(layout) -> int:
+    """K and V bytes of every cached token (key width + value width per head)."""
     spec = layout.spec
     eb = {"f32": 4, "bf16": 2, "fp8": 1}[spec.kv_dtype]
-    return int(layout.total_tokens) * spec.num_kv_heads * spec.head_dim * 2 * eb
+    return int(layout.total_tokens) * spec.num_kv_heads * (spec.head_dim + spec.value_dim) * eb
 
 
 def decode_algorithmic_bytes(layout) -> int:
     """KV read + Q read + O write + index buffers (kv_indices, indptr, last_page_len)."""
     spec = layout.spec
     qb = {"f32": 4, "bf16": 2}[spec.q_dtype]
-    qo = layout.batch * spec.num_q_heads * spec.head_dim * qb * 2
+    qo = layout.batch * spec.num_q_heads * (spec.head_dim + spec.value_dim) * qb
     idx = 4 * (layout.kv_pages + 2 * layout.batch + 1)
     return kv_bytes(layout) + qo + idx
 
 
 def extend_flops(layout) -> float:
-    """4 * D * Hq * (causally valid query/key pairs): q.k and p.v, 2 flops per MAC."""
+    """2 * (Dk + Dv) * Hq * (causally valid query/key pairs): q.k over the key
+    width and p.v over the value width, 2 flops per MAC."""
     spec = layout.spec
     pairs = 0
     for L, n in zip(layout.seq_lens.tolist(), layout.extend_lens.tolist()):
         p = L - n
         pairs += n * p + n * (n + 1) // 2
-    return 4.0 * spec.head_dim * spec.num_q_heads * pairs
+    return 2.0 * (spec.head_dim + spec.value_dim) * spec.num_q_heads * pairs
 
 
 def source_hash(*names) -> str:
@@ -187,7 +189,7 @@ def cpu_baseline(layout, values, budget_s: float = 20.0):
         oracle_requests(layout, values, [b], threads=threads)
         t_total += time.perf_counter() - t0
         done.append(b)
-        kv += int(layout.seq_lens[b]) * spec.num_kv_heads * spec.head_dim * 2 * eb
+        kv += int(layout.seq_lens[b]) * spec.num_kv_heads * (spec.head_dim + spec.value_dim) * eb
         if t_total >= budget_s:
             break
     return {"value": round(kv / t_total / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -199,12 +201,12 @@ def cpu_baseline(layout, values, budget_s: float = 20.0):
             "cpu": cpu_model()}
 
 
-def bench_decode_kernel(cfg_id: int, iters: int):
+def bench_decode_kernel(spec, iters: int):
     """Kernel-level decode figure for one workload (attn_decode alone)."""
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
-    layout = workloads.make_layout(workloads.CONFIGS[cfg_id])
+    layout = workloads.make_layout(spec)
     prob = GpuProblem(layout)
     prob.attention_step(save=True)
     torch.cuda.synchronize()
@@ -219,11 +221,11 @@ def bench_decode_kernel(cfg_id: int, iters: int):
     return out
 
 
-def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16"):
+def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16", spec=None):
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
-    spec = workloads.CONFIGS[4]
+    spec = workloads.CONFIGS[4] if spec is None else spec
     if kv_dtype != spec.kv_dtype:
         spec = spec.replace(name=spec.name.replace("extend_bf16", f"extend_{kv_dtype}kv"), kv_dtype=kv_dtype)
     layout = workloads.make_layout(spec)
@@ -240,7 +242,8 @@ def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16"):
            "TFLOPs": round(tf, 1), "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
            "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
            "ms_per_call": time_per_call(call, iters),
-           "variant": f"extend_mfma_kernel<{spec.head_dim}, scale>0, page {spec.page_size} >= 64, "
+           "variant": f"extend_mfma_kernel<Dk {spec.head_dim}, Dv {spec.value_dim}, scale>0, "
+                      f"page {spec.page_size}{' >= 64' if spec.page_size >= 64 else ' < 64'}, "
                       f"{spec.kv_dtype} cache>"}
     if gpu_state:
         out["gpu_state"] = gpu_state_under(call)
@@ -292,7 +295,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extend / other decode figures and the clock and power sampling")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["extend", "extend_fp8", "decode3", "decode5", "copy", "gemm"], default=None,
+    ap.add_argument("--only", choices=["extend", "extend_fp8", "decode3", "decode5", "copy", "gemm",
+                                       "asym_extend", "asym_decode"], default=None,
                     help="run one extra leg alone (for profiling) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -317,8 +321,12 @@ def main():
             res = bench_extend(args.steps, gpu_state=False)
         elif args.only == "extend_fp8":
             res = bench_extend(args.steps, gpu_state=False, kv_dtype="fp8")
+        elif args.only == "asym_extend":
+            res = bench_extend(args.steps, gpu_state=False, spec=workloads.EXTRA["asym_extend"])
+        elif args.only == "asym_decode":
+            res = bench_decode_kernel(workloads.EXTRA["asym_decode"], args.steps)
         else:
-            res = bench_decode_kernel(int(args.only[-1]), args.steps)
+            res = bench_decode_kernel(workloads.CONFIGS[int(args.only[-1])], args.steps)
         print(json.dumps(res), flush=True)
         return
 
@@ -394,8 +402,14 @@ def main():
         log(f"bf16 GEMM reference: {result['mfma_reference']}")
         result["decode_configs"] = {}
         for cid in (3, 5):
-            result["decode_configs"][str(cid)] = bench_decode_kernel(cid, args.steps)
+            result["decode_configs"][str(cid)] = bench_decode_kernel(workloads.CONFIGS[cid], args.steps)
             log(f"decode config {cid}: {result['decode_configs'][str(cid)]}")
+        # key / value heads of different widths (192 / 128)
+        result["asym_extend"] = bench_extend(args.steps, gpu_state=False,
+                                             spec=workloads.EXTRA["asym_extend"])
+        log(f"extend, 192/128 widths: {result['asym_extend']}")
+        result["asym_decode"] = bench_decode_kernel(workloads.EXTRA["asym_decode"], args.steps)
+        log(f"decode, 192/128 widths: {result['asym_decode']}")
 
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")

@@ -21,9 +21,12 @@
  *   paths.  Work is enqueued on the caller's HIP stream (a hipStream_t passed
  *   as void*; NULL is the default stream).
  * - Layouts are row-major and contiguous:
- *     q, out            [num_q_tokens, num_q_heads, head_dim]   (q dtype)
- *     k_new, v_new      [num_q_tokens, num_kv_heads, head_dim]  (q dtype)
- *     k_pool, v_pool    [num_pages * page_size, num_kv_heads, head_dim]
+ *     q                 [num_q_tokens, num_q_heads, head_dim]     (q dtype)
+ *     out               [num_q_tokens, num_q_heads, v_head_dim]   (q dtype)
+ *     k_new             [num_q_tokens, num_kv_heads, head_dim]    (q dtype)
+ *     v_new             [num_q_tokens, num_kv_heads, v_head_dim]  (q dtype)
+ *     k_pool            [num_pages * page_size, num_kv_heads, head_dim]
+ *     v_pool            [num_pages * page_size, num_kv_heads, v_head_dim]
  *                       (kv dtype; separate K and V pools, token-major)
  *     lse               [num_q_tokens, num_q_heads] fp32, natural log
  *   Page p holds slots p*page_size .. p*page_size + page_size - 1.  Query
@@ -78,12 +81,21 @@ typedef enum { PKA_PATH_NONE = 0, PKA_PATH_DECODE = 1, PKA_PATH_EXTEND = 2 } pka
 
 /* Per-layer attention parameters (the analogue of one attention layer's
  * handle).  Supported:
- *   head_dim in {64, 128}; page_size in {1, 2, 4, ..., 256} (a power of two);
+ *   (head_dim, v_head_dim) in {(64, 64), (128, 128), (192, 128)}: head_dim
+ *   is the width of query and key heads, v_head_dim that of value and output
+ *   heads (0 means equal to head_dim).  The pages have one backend picked
+ *   for models whose K and V heads differ in width ("sglang-101 s4.2
+ *   --attention-backend", backend table and "How SGLang picks a default");
+ *   192 / 128 is the query-key width with a rotary part against a narrower
+ *   value, as in MLA models run as plain multi-head attention for prefill.
+ *   page_size in {1, 2, 4, ..., 256} (a power of two);
  *   num_q_heads a positive multiple of num_kv_heads;
- *   (q, kv) dtypes: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN);
- *   extend runs for (BF16, BF16) and (F32, F32).
+ *   (q, kv) dtypes: (F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN), on both
+ *   the decode and the extend path.
  * scale multiplies q.k; k_scale / v_scale are the per-tensor fp8 scales (the
- * cached code c stands for c * scale); they must be 1 for non-fp8 caches. */
+ * cached code c stands for c * scale); they must be 1 for non-fp8 caches.
+ * v_head_dim is the last member so a zero-initialised config keeps the
+ * equal-width behaviour. */
 typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -95,6 +107,7 @@ typedef struct {
     float scale;
     float k_scale;
     float v_scale;
+    int32_t v_head_dim; /* 0: same as head_dim */
 } pka_config;
 
 typedef struct pka_ctx pka_ctx;

@@ -46,7 +46,8 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("q_dtype", ctypes.c_int),
                 ("kv_dtype", ctypes.c_int), ("scale", ctypes.c_float),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("v_head_dim", ctypes.c_int32)]
 
 
 class BatchStruct(ctypes.Structure):
@@ -134,12 +135,17 @@ class Context:
 
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                  num_pages: int, q_dtype: str = "bf16", kv_dtype: str = "bf16",
-                 scale: Optional[float] = None, k_scale: float = 1.0, v_scale: float = 1.0):
+                 scale: Optional[float] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                 v_head_dim: Optional[int] = None):
+        """head_dim: query/key head width; v_head_dim: value/output head
+        width (None: the same as head_dim)."""
+        dv = head_dim if v_head_dim is None else v_head_dim
         self.cfg = Config(num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           DTYPES[q_dtype], DTYPES[kv_dtype],
-                          head_dim ** -0.5 if scale is None else scale, k_scale, v_scale)
+                          head_dim ** -0.5 if scale is None else scale, k_scale, v_scale, dv)
         self.q_dtype, self.kv_dtype = q_dtype, kv_dtype
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.v_head_dim = dv
         self.page_size, self.num_pages = page_size, num_pages
         h = ctypes.c_void_p()
         _check(lib().pka_create(ctypes.byref(self.cfg), ctypes.byref(h)))
@@ -158,7 +164,11 @@ class Context:
         return s
 
     def pool_shape(self):
+        """Shape of the K pool."""
         return (self.num_pages * self.page_size, self.num_kv_heads, self.head_dim)
+
+    def v_pool_shape(self):
+        return (self.num_pages * self.page_size, self.num_kv_heads, self.v_head_dim)
 
 
 class Batch:
@@ -215,24 +225,26 @@ class Batch:
         return v.value
 
 
-def _check_rows(ctx: Context, t, rows: int, heads: int, dtype: str, name: str):
+def _check_rows(ctx: Context, t, rows: int, heads: int, dtype: str, name: str, value: bool = False):
+    """value: the tensor has value-width rows (v_new, v_pool, out)."""
     import torch
     want = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
     if t.dtype != want or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous device {want} tensor, got {t.dtype}")
-    if tuple(t.shape) != (rows, heads, ctx.head_dim):
-        raise ValueError(f"{name}: expected shape {(rows, heads, ctx.head_dim)}, got {tuple(t.shape)}")
+    width = ctx.v_head_dim if value else ctx.head_dim
+    if tuple(t.shape) != (rows, heads, width):
+        raise ValueError(f"{name}: expected shape {(rows, heads, width)}, got {tuple(t.shape)}")
 
 
 def _check_pools(ctx: Context, k_pool, v_pool):
     slots = ctx.num_pages * ctx.page_size
     _check_rows(ctx, k_pool, slots, ctx.num_kv_heads, ctx.kv_dtype, "k_pool")
-    _check_rows(ctx, v_pool, slots, ctx.num_kv_heads, ctx.kv_dtype, "v_pool")
+    _check_rows(ctx, v_pool, slots, ctx.num_kv_heads, ctx.kv_dtype, "v_pool", value=True)
 
 
 def save_kv(ctx: Context, md: Batch, k_new, v_new, k_pool, v_pool, stream=None):
     _check_rows(ctx, k_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "k_new")
-    _check_rows(ctx, v_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "v_new")
+    _check_rows(ctx, v_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "v_new", value=True)
     _check_pools(ctx, k_pool, v_pool)
     _check(lib().pka_save_kv(ctx.handle, ctypes.byref(md.s), k_new.data_ptr(), v_new.data_ptr(),
                              k_pool.data_ptr(), v_pool.data_ptr(), _stream(stream)))
@@ -241,7 +253,7 @@ def save_kv(ctx: Context, md: Batch, k_new, v_new, k_pool, v_pool, stream=None):
 def _attn_common(ctx, md, q, k_pool, v_pool, out, lse):
     import torch
     _check_rows(ctx, q, md.num_q_tokens, ctx.num_q_heads, ctx.q_dtype, "q")
-    _check_rows(ctx, out, md.num_q_tokens, ctx.num_q_heads, ctx.q_dtype, "out")
+    _check_rows(ctx, out, md.num_q_tokens, ctx.num_q_heads, ctx.q_dtype, "out", value=True)
     _check_pools(ctx, k_pool, v_pool)
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != (md.num_q_tokens, ctx.num_q_heads)):
@@ -277,7 +289,7 @@ def forward(ctx: Context, mode: str, md: Batch, q, k_new, v_new, k_pool, v_pool,
         _attn_common(ctx, md, q, k_pool, v_pool, out, lse)
         if save_kv_cache:
             _check_rows(ctx, k_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "k_new")
-            _check_rows(ctx, v_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "v_new")
+            _check_rows(ctx, v_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "v_new", value=True)
     wp, wb = _ws(md.workspace if workspace is None else workspace)
     _check(lib().pka_forward(ctx.handle, MODES[mode], SPEC_MODES[spec_mode], ctypes.byref(md.s),
                              _ptr(q), _ptr(k_new), _ptr(v_new), int(bool(save_kv_cache)),

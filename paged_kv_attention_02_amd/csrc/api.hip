@@ -17,6 +17,8 @@
 
 struct pka_ctx {
     pka_config cfg;
+    int32_t dk;          // key (and query) head width
+    int32_t dv;          // value (and output) head width
     int32_t G;
     int32_t qgroups;     // ceil(G / 16): decode waves per KV head
     int32_t page_shift;
@@ -58,7 +60,7 @@ pka_status decode_wgs(const pka_ctx* ctx, int32_t* out) {
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_fail(e, "querying the device");
-        int per_cu = pka::decode_blocks_per_cu(ctx->cfg.kv_dtype, ctx->cfg.head_dim, ctx->wpb);
+        int per_cu = pka::decode_blocks_per_cu(ctx->cfg.kv_dtype, ctx->dk, ctx->dv, ctx->wpb);
         if (per_cu < 1) per_cu = 1;
         v = std::min<int32_t>(pka::DEC_MAX_WG, std::max(1, cus * per_cu));
         const_cast<pka_ctx*>(ctx)->nwg.store(v, std::memory_order_relaxed);
@@ -80,7 +82,7 @@ int32_t decode_qslots(pka_forward_mode m, int32_t num_q_tokens) {
 }
 
 int64_t decode_ws_bytes(const pka_ctx* ctx, int32_t B, int32_t nwg, int32_t qslots) {
-    return ((int64_t)B + nwg) * qslots * ctx->cfg.num_q_heads * (ctx->cfg.head_dim + 1) * 4;
+    return ((int64_t)B + nwg) * qslots * ctx->cfg.num_q_heads * (ctx->dv + 1) * 4;
 }
 
 pka_status check_batch(const pka_ctx* ctx, const pka_batch* md) {
@@ -168,7 +170,7 @@ pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     a.nwg = nwg;
     a.qslots = qslots;
     a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * qslots * ctx->cfg.num_q_heads * ctx->cfg.head_dim;
+    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * qslots * ctx->cfg.num_q_heads * ctx->dv;
     if (write_new) {
         const pka_config& c = ctx->cfg;
         a.k_new = k_new;
@@ -178,7 +180,7 @@ pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, c
         a.k_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f);
         a.v_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f);
     }
-    hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->cfg.head_dim, a,
+    hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
                                       ctx->wpb, (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
 }
@@ -209,8 +211,12 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
     if (c.num_q_heads < 1 || c.num_kv_heads < 1 || c.num_q_heads % c.num_kv_heads != 0)
         return fail(PKA_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                     c.num_q_heads, c.num_kv_heads);
-    if (c.head_dim != 64 && c.head_dim != 128)
-        return fail(PKA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c.head_dim);
+    const int32_t dv = c.v_head_dim == 0 ? c.head_dim : c.v_head_dim;
+    const bool widths_ok = (c.head_dim == 64 && dv == 64) || (c.head_dim == 128 && dv == 128) ||
+                           (c.head_dim == 192 && dv == 128);
+    if (!widths_ok)
+        return fail(PKA_ERR_UNSUPPORTED, "head widths K %d / V %d (supported: 64/64, 128/128, 192/128)",
+                    c.head_dim, dv);
     if (c.page_size < 1 || c.page_size > 256 || (c.page_size & (c.page_size - 1)))
         return fail(PKA_ERR_UNSUPPORTED, "page_size %d (supported: powers of two up to 256)", c.page_size);
     if (c.num_pages < 1 || (int64_t)c.num_pages * c.page_size > INT32_MAX)
@@ -236,6 +242,9 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
     pka_ctx* ctx = new (std::nothrow) pka_ctx;
     if (!ctx) return fail(PKA_ERR_INVALID_ARG, "out of host memory");
     ctx->cfg = c;
+    ctx->cfg.v_head_dim = dv;
+    ctx->dk = c.head_dim;
+    ctx->dv = dv;
     ctx->G = c.num_q_heads / c.num_kv_heads;
     ctx->qgroups = (ctx->G + 15) / 16;
     int shift = 0;
@@ -245,7 +254,7 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
     int wpb = 8;
     while (units % wpb) wpb >>= 1;
     ctx->wpb = wpb;
-    ctx->ext_tq = pka::extend_tq(c.q_dtype, c.kv_dtype, c.head_dim, ctx->G, c.page_size);
+    ctx->ext_tq = pka::extend_tq(c.q_dtype, c.kv_dtype, ctx->G, c.page_size);
     *out = ctx;
     return PKA_OK;
 }
@@ -334,11 +343,12 @@ pka_status pka_save_kv(const pka_ctx* ctx, const pka_batch* md, const void* k_ne
     a.out_cache_loc = md->out_cache_loc;
     a.plan = md->plan;
     a.N = md->num_q_tokens;
-    a.row_elems = c.num_kv_heads * c.head_dim;
+    a.k_row_elems = c.num_kv_heads * ctx->dk;
+    a.v_row_elems = c.num_kv_heads * ctx->dv;
     a.pool_slots = (int64_t)c.num_pages * c.page_size;
     a.k_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f);
     a.v_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f);
-    hipError_t e = pka::launch_save_kv(c.q_dtype, c.kv_dtype, c.head_dim, a, (hipStream_t)stream);
+    hipError_t e = pka::launch_save_kv(c.q_dtype, c.kv_dtype, a, (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "save_kv launch");
 }
 
@@ -358,7 +368,7 @@ pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* 
     if (!is_extend_like(md->mode))
         return fail(PKA_ERR_INVALID_ARG, "metadata was built for a decode batch; extend needs extend metadata");
     pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
-    hipError_t e = pka::launch_extend(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->cfg.head_dim, a,
+    hipError_t e = pka::launch_extend(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
                                       (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "extend launch");
 }

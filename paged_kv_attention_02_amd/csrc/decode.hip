@@ -79,7 +79,7 @@ __device__ inline void emit_rows(const f32x4_t (&O)[D / 16], float inv, int j, E
 // K on lanes 0..31, V on lanes 32..63, 8 elements per lane (bf16 copy or
 // bf16 -> fp8 quantisation).  The store is waited for before the wave reads
 // the pool, so the wave's own later load of that slot sees it.
-template <int D, bool FP8>
+template <int DK, int DV, bool FP8>
 __device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int g, int lane) {
     const int32_t slot = a.out_cache_loc[qr];
     if (slot < 0 || slot >= a.pool_slots) {
@@ -87,6 +87,7 @@ __device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int g, int
         return;
     }
     const bool is_v = lane >= 32;
+    const int D = is_v ? DV : DK;
     const int e = (lane & 31) * 8;  // first element of this lane
     if (e < D) {
         const int64_t src = ((int64_t)qr * a.Hkv + g) * D + e;
@@ -103,14 +104,15 @@ __device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int g, int
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stores have completed
 }
 
-template <int D, bool FP8>
+// DK: key (and query) width; DV: value (and output) width.
+template <int DK, int DV, bool FP8>
 struct DecodeShape {
-    static constexpr int ESZ = FP8 ? 1 : 2;   // cache bytes per element
-    static constexpr int KE = 16 / ESZ;       // elements per 16-byte K load
-    static constexpr int NKL = D * ESZ / 64;  // 16-byte K loads per lane per 16 tokens
-    static constexpr int KSTEPS = D / 32;     // MFMA k-steps of q.k
-    static constexpr int SPL = KE / 8;        // k-steps per K load
-    static constexpr int CPL = D / 16;        // V dims per lane per token = PV MFMAs
+    static constexpr int ESZ = FP8 ? 1 : 2;    // cache bytes per element
+    static constexpr int KE = 16 / ESZ;        // elements per 16-byte K load
+    static constexpr int NKL = DK * ESZ / 64;  // 16-byte K loads per lane per 16 tokens
+    static constexpr int KSTEPS = DK / 32;     // MFMA k-steps of q.k
+    static constexpr int SPL = KE / 8;         // k-steps per K load
+    static constexpr int CPL = DV / 16;        // V dims per lane per token = PV MFMAs
     static_assert(NKL * SPL == KSTEPS, "k-step bookkeeping");
     using vrow_t = typename std::conditional<
         CPL * ESZ == 16, u32x4_t,
@@ -121,9 +123,9 @@ struct DecodeShape {
 // tokens 16*sb + n (lane n = lane & 15); V k-slot q of lane group j holds
 // tile token 16*(q/4) + 4*j + q%4, the order in which the scores come out of
 // the first MFMA, so P^T needs no shuffle.
-template <int D, bool FP8>
+template <int DK, int DV, bool FP8>
 struct KVTile {
-    using S = DecodeShape<D, FP8>;
+    using S = DecodeShape<DK, DV, FP8>;
     u32x4_t kr[2][S::NKL];
     typename S::vrow_t vr[8];
 };
@@ -131,23 +133,23 @@ struct KVTile {
 // Issue the loads of one tile.  `slot` is the pool slot of tile token
 // (lane & 31); lanes exchange slots with cross-lane moves.  The cache is
 // read once per call, so the loads carry the non-temporal hint.
-template <int D, bool FP8>
-__device__ inline void load_tile(KVTile<D, FP8>& T, int32_t slot, const uint8_t* kbase,
-                                 const uint8_t* vbase, int64_t row_bytes, int n, int j) {
-    using S = DecodeShape<D, FP8>;
+template <int DK, int DV, bool FP8>
+__device__ inline void load_tile(KVTile<DK, DV, FP8>& T, int32_t slot, const uint8_t* kbase,
+                                 const uint8_t* vbase, int64_t krow, int64_t vrow, int n, int j) {
+    using S = DecodeShape<DK, DV, FP8>;
     const int32_t slot_x = __shfl_xor(slot, 16);
     const int32_t ks0 = (j & 1) ? slot_x : slot;
     const int32_t ks1 = (j & 1) ? slot : slot_x;
     #pragma unroll
     for (int s = 0; s < S::NKL; ++s) {
-        T.kr[0][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks0 * row_bytes + s * 64 + j * 16));
-        T.kr[1][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks1 * row_bytes + s * 64 + j * 16));
+        T.kr[0][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks0 * krow + s * 64 + j * 16));
+        T.kr[1][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks1 * krow + s * 64 + j * 16));
     }
     #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int32_t vs = __shfl(slot, 16 * (q >> 2) + 4 * j + (q & 3));
         T.vr[q] = __builtin_nontemporal_load(
-            (const typename S::vrow_t*)(vbase + vs * row_bytes + n * (S::CPL * S::ESZ)));
+            (const typename S::vrow_t*)(vbase + vs * vrow + n * (S::CPL * S::ESZ)));
     }
 }
 
@@ -155,11 +157,11 @@ __device__ inline void load_tile(KVTile<D, FP8>& T, int32_t slot, const uint8_t*
 // tokens are real for this lane's column (the rest are masked out).  With MQ
 // a column may have no real token yet (its causal limit lies beyond the
 // tile): its maximum stays -inf and it accumulates nothing.
-template <int D, bool FP8, bool MQ>
-__device__ inline void compute_tile(const KVTile<D, FP8>& T, const bf16x8_t* qop,
+template <int DK, int DV, bool FP8, bool MQ>
+__device__ inline void compute_tile(const KVTile<DK, DV, FP8>& T, const bf16x8_t* qop,
                                     f32x4_t* O, float& m2, float& lsum, int valid,
                                     float scale_log2, int j) {
-    using S = DecodeShape<D, FP8>;
+    using S = DecodeShape<DK, DV, FP8>;
     // S^T = K . Q^T, two 16-token row blocks
     f32x4_t st[2];
     #pragma unroll
@@ -252,9 +254,9 @@ __device__ inline void compute_tile(const KVTile<D, FP8>& T, const bf16x8_t* qop
 // per pass of the wave over its share; token i of a request with n query
 // tokens sits at position L - n + i and sees keys 0 .. L - n + i.  Partials
 // of token i go to slot (b + w) * qslots + i.
-template <int D, bool FP8, bool MQ>
+template <int DK, int DV, bool FP8, bool MQ>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
-    using S = DecodeShape<D, FP8>;
+    using S = DecodeShape<DK, DV, FP8>;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, j = lane >> 4;
     const int wpb = blockDim.x >> 6;
@@ -276,9 +278,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const int32_t* F = plan + plan_seg_prefix(a.B);
     int32_t seg = plan[plan_wg_seg(a.B) + w];
 
-    const int64_t row_bytes = (int64_t)a.Hkv * D * S::ESZ;  // one pool slot, all KV heads
-    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * D * S::ESZ;
-    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * D * S::ESZ;
+    // one pool slot, all KV heads
+    const int64_t krow = (int64_t)a.Hkv * DK * S::ESZ, vrow = (int64_t)a.Hkv * DV * S::ESZ;
+    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * DK * S::ESZ;
+    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * DV * S::ESZ;
     const int tok = lane & 31;  // tile token whose slot this lane looks up
 
     for (; seg < a.B; ++seg) {
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             nq = 1;
             pfx = L - 1;
             // the piece holding the request's last position writes the new token
-            if (a.k_new && hi == L) write_new_token<D, FP8>(a, q0, g, lane);
+            if (a.k_new && hi == L) write_new_token<DK, DV, FP8>(a, q0, g, lane);
         }
         // slot of tile token `tok` of the tile starting at position t0; positions
         // past the piece repeat its last token (cached, never counted)
@@ -323,15 +326,15 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             // keys of this column within the piece: positions < kend_c
             const int32_t kend_c = MQ ? min(hi, pfx + qi + 1) : hi;
 
-            KVTile<D, FP8> A, Bt;
+            KVTile<DK, DV, FP8> A, Bt;
             int32_t slot_a = slot_at(lo);
             int32_t slot_b = slot_at(lo + DEC_TILE);
-            load_tile(A, slot_a, kbase, vbase, row_bytes, n, j);
+            load_tile(A, slot_a, kbase, vbase, krow, vrow, n, j);
 
             // Q^T operand: lane (n, j) holds its column at the dims its K lanes load.
             bf16x8_t qop[S::KSTEPS];
             {
-                const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + h) * D;
+                const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + h) * DK;
                 #pragma unroll
                 for (int ks = 0; ks < S::KSTEPS; ++ks) {
                     const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
@@ -351,13 +354,13 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             // the end they re-read the piece's last row) so the wait counts
             // are the same on every iteration.
             for (int32_t t0 = lo;; t0 += 2 * DEC_TILE) {
-                load_tile(Bt, slot_b, kbase, vbase, row_bytes, n, j);
+                load_tile(Bt, slot_b, kbase, vbase, krow, vrow, n, j);
                 slot_a = slot_at(t0 + 2 * DEC_TILE);
-                compute_tile<D, FP8, MQ>(A, qop, O, m2, lsum, kend_c - t0, a.scale_log2, j);
+                compute_tile<DK, DV, FP8, MQ>(A, qop, O, m2, lsum, kend_c - t0, a.scale_log2, j);
                 if (t0 + DEC_TILE >= hi) break;
-                load_tile(A, slot_a, kbase, vbase, row_bytes, n, j);
+                load_tile(A, slot_a, kbase, vbase, krow, vrow, n, j);
                 slot_b = slot_at(t0 + 3 * DEC_TILE);
-                compute_tile<D, FP8, MQ>(Bt, qop, O, m2, lsum, kend_c - t0 - DEC_TILE, a.scale_log2, j);
+                compute_tile<DK, DV, FP8, MQ>(Bt, qop, O, m2, lsum, kend_c - t0 - DEC_TILE, a.scale_log2, j);
                 if (t0 + 2 * DEC_TILE >= hi) break;
             }
 
@@ -368,8 +371,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             const float lse_nat = MQ && !(ltot > 0.f) ? -INFINITY : (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
             if (MQ ? col_ok : n < nh) {
                 if (lo == 0 && hi == L) {
-                    __bf16* orow = (__bf16*)a.out + ((int64_t)qr * a.Hq + h) * D;
-                    emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+                    __bf16* orow = (__bf16*)a.out + ((int64_t)qr * a.Hq + h) * DV;
+                    emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
                         #pragma unroll
                         for (int i = 0; i < 4 * S::CPL; i += 8) {
                             const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
@@ -382,8 +385,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
                 } else {
                     // partial slot of (request, workgroup, query token)
                     const int64_t ps = ((int64_t)b + w) * a.qslots + qi;
-                    float* prow = a.ws_o + (ps * a.Hq + h) * D;
-                    emit_rows<D>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+                    float* prow = a.ws_o + (ps * a.Hq + h) * DV;
+                    emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
                         #pragma unroll
                         for (int i = 0; i < 4 * S::CPL; i += 4)
                             *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
@@ -398,9 +401,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
 // fp32 cache: a plain VALU variant with the same work partition (lanes over
 // head_dim, one token at a time, 16 columns per pass as in the MFMA variant).
 // Used for fp32 workloads.
-template <int D, bool MQ>
+template <int DK, int DV, bool MQ>
 __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
-    constexpr int EPL = D / 64;  // dims per lane
+    constexpr int EPK = DK / 64, EPV = DV / 64;  // key and value dims per lane
     const int lane = threadIdx.x & 63;
     const int wpb = blockDim.x >> 6;
     const int unit = blockIdx.y * wpb + (threadIdx.x >> 6);
@@ -440,7 +443,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
         const int32_t cols = nq * nh;
         for (int32_t c0 = 0; c0 < cols; c0 += 16) {
             const int ncol = min(16, cols - c0);
-            float q[16][EPL], o[16][EPL], m[16], l[16];
+            float q[16][EPK], o[16][EPV], m[16], l[16];
             int32_t kend[16];
             #pragma unroll
             for (int cc = 0; cc < 16; ++cc) {
@@ -450,25 +453,24 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
                 const int32_t qi = cc < ncol ? c / nh : 0;
                 kend[cc] = min(hi, pfx + qi + 1);
                 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    q[cc][e] = cc < ncol ? ((const float*)a.q)[((int64_t)(q0 + qi) * a.Hq + h0 + c % nh) * D + e * 64 + lane] : 0.f;
-                    o[cc][e] = 0.f;
-                }
+                for (int e = 0; e < EPK; ++e)
+                    q[cc][e] = cc < ncol ? ((const float*)a.q)[((int64_t)(q0 + qi) * a.Hq + h0 + c % nh) * DK + e * 64 + lane] : 0.f;
+                #pragma unroll
+                for (int e = 0; e < EPV; ++e) o[cc][e] = 0.f;
             }
             for (int32_t t = lo; t < hi; ++t) {
-                const int64_t base = ((int64_t)slot_of(a, page_base, t) * a.Hkv + g) * D;
-                float k[EPL], v[EPL];
+                const int64_t sg = (int64_t)slot_of(a, page_base, t) * a.Hkv + g;
+                float k[EPK], v[EPV];
                 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    k[e] = ((const float*)a.k_pool)[base + e * 64 + lane];
-                    v[e] = ((const float*)a.v_pool)[base + e * 64 + lane];
-                }
+                for (int e = 0; e < EPK; ++e) k[e] = ((const float*)a.k_pool)[sg * DK + e * 64 + lane];
+                #pragma unroll
+                for (int e = 0; e < EPV; ++e) v[e] = ((const float*)a.v_pool)[sg * DV + e * 64 + lane];
                 #pragma unroll
                 for (int cc = 0; cc < 16; ++cc) {
                     if (cc >= ncol || t >= kend[cc]) continue;
                     float dot = 0.f;
                     #pragma unroll
-                    for (int e = 0; e < EPL; ++e) dot += q[cc][e] * k[e];
+                    for (int e = 0; e < EPK; ++e) dot += q[cc][e] * k[e];
                     #pragma unroll
                     for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
                     const float sc = dot * scale2;
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
                     m[cc] = mn;
                     l[cc] = l[cc] * al + p;
                     #pragma unroll
-                    for (int e = 0; e < EPL; ++e) o[cc][e] = o[cc][e] * al + p * v[e];
+                    for (int e = 0; e < EPV; ++e) o[cc][e] = o[cc][e] * al + p * v[e];
                 }
             }
             const bool full = lo == 0 && hi == L;
@@ -492,14 +494,14 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
                 const float lse_nat = empty ? -INFINITY : (m[cc] + __builtin_amdgcn_logf(l[cc])) * LN2;
                 if (full) {
                     #pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        ((float*)a.out)[((int64_t)qr * a.Hq + h) * D + e * 64 + lane] = o[cc][e] * inv;
+                    for (int e = 0; e < EPV; ++e)
+                        ((float*)a.out)[((int64_t)qr * a.Hq + h) * DV + e * 64 + lane] = o[cc][e] * inv;
                     if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
                 } else {
                     const int64_t ps = ((int64_t)b + w) * a.qslots + qi;
                     #pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        a.ws_o[(ps * a.Hq + h) * D + e * 64 + lane] = o[cc][e] * inv;
+                    for (int e = 0; e < EPV; ++e)
+                        a.ws_o[(ps * a.Hq + h) * DV + e * 64 + lane] = o[cc][e] * inv;
                     if (lane == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
                 }
             }
@@ -512,6 +514,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
 // lse = M + ln(sum_c e^(lse_c - M)).  One wave per (request, head): lanes
 // first take one partial each (max and normaliser by wave reductions), then
 // lanes take head dims and sweep the partials with several loads in flight.
+// D: the value (output) width.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     constexpr int EPL = D / 64;
@@ -586,57 +589,59 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     }
 }
 
-template <int D>
+template <int DK, int DV>
 hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb, hipStream_t s) {
     const int units = a.Hkv * a.qgroups;
     const dim3 grid(a.nwg, units / wpb);
     const dim3 block(64 * wpb);
     const bool mq = a.qslots > 1;
     if (kv == PKA_BF16) {
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<D, false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_mfma_kernel<D, false, false>), grid, block, 0, s, a);
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false>), grid, block, 0, s, a);
     } else if (kv == PKA_FP8_E4M3FN) {
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<D, true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_mfma_kernel<D, true, false>), grid, block, 0, s, a);
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false>), grid, block, 0, s, a);
     } else {
-        if (mq) hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, block, 0, s, a);
+        if (mq) hipLaunchKernelGGL((decode_f32_kernel<DK, DV, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((decode_f32_kernel<DK, DV, false>), grid, block, 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 mgrid(a.B, (a.Hq + 3) / 4);
     if (q == PKA_BF16)
-        hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_merge_kernel<DV, true>), mgrid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_merge_kernel<D, false>), mgrid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_merge_kernel<DV, false>), mgrid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <int D>
+template <int DK, int DV>
 int blocks_per_cu_d(pka_dtype kv, int wpb) {
     int n = 0;
     hipError_t e;
     if (kv == PKA_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, false, false>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, false, false>, 64 * wpb, 0);
     else if (kv == PKA_FP8_E4M3FN)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<D, true, false>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, true, false>, 64 * wpb, 0);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<D, false>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<DK, DV, false>, 64 * wpb, 0);
     return e == hipSuccess ? n : 0;
 }
 
 }  // namespace
 
-int decode_blocks_per_cu(pka_dtype kv, int D, int wpb) {
-    if (D == 128) return blocks_per_cu_d<128>(kv, wpb);
-    if (D == 64) return blocks_per_cu_d<64>(kv, wpb);
+int decode_blocks_per_cu(pka_dtype kv, int DK, int DV, int wpb) {
+    if (DK == 128 && DV == 128) return blocks_per_cu_d<128, 128>(kv, wpb);
+    if (DK == 64 && DV == 64) return blocks_per_cu_d<64, 64>(kv, wpb);
+    if (DK == 192 && DV == 128) return blocks_per_cu_d<192, 128>(kv, wpb);
     return 0;
 }
 
-hipError_t launch_decode(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, int wpb,
+hipError_t launch_decode(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, int wpb,
                          hipStream_t s) {
-    if (D == 128) return launch_decode_d<128>(q, kv, a, wpb, s);
-    if (D == 64) return launch_decode_d<64>(q, kv, a, wpb, s);
+    if (DK == 128 && DV == 128) return launch_decode_d<128, 128>(q, kv, a, wpb, s);
+    if (DK == 64 && DV == 64) return launch_decode_d<64, 64>(q, kv, a, wpb, s);
+    if (DK == 192 && DV == 128) return launch_decode_d<192, 128>(q, kv, a, wpb, s);
     return hipErrorInvalidValue;
 }
 

@@ -89,19 +89,43 @@ __device__ inline void lds_dma16(const void* src, const uint8_t* lds_dst) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "m0");
 }
 
-// LDS tiles: BN keys x D dims of K and of V, rows of 16-byte chunks with no
+// LDS tiles: BN keys x D dims of K or of V, rows of 16-byte chunks with no
 // padding, filled by direct HBM -> LDS loads (each lane's 16 bytes land at
 // base + 16 * lane).  Chunks are XOR-swizzled per row so the reads are
-// bank-conflict free: K is read 16 rows x one chunk at a time (chunk ^ row),
-// V by the transposing loads, 4 rows x 4 chunks at a time
+// bank-conflict free: K is read 16 rows x one chunk at a time, so the 16
+// rows must land on 16 different 16-byte bank groups (256 bytes per bank
+// cycle): 256-byte rows use chunk ^ row; 128-byte rows (two per cycle) and
+// 384-byte rows (starting alternately at bank 0 and half-way round) use
+// chunk ^ (row / 2 % 8), which keeps every chunk inside its aligned group of
+// 8.  V is read by the transposing loads, 4 rows x 4 chunks at a time
 // (chunk ^ 4 * (row % 4)).
 template <int D> struct ExtTile {
     static constexpr int CPR = D / 8;                  // 16-byte chunks per row (bf16)
     static constexpr int ROWB = D * 2;
-    static constexpr int TILEB = BN * ROWB;            // bytes of one K or V tile
+    static constexpr int TILEB = BN * ROWB;            // bytes of one tile
     static constexpr int LOADS = TILEB / (64 * EXT_WAVES * 16);  // DMA instructions per thread per tile
-    __device__ static constexpr int kchunk(int row, int c) { return c ^ (row & (CPR - 1)); }
+    static constexpr bool POW2 = (CPR & (CPR - 1)) == 0;
+    static_assert(CPR == 8 || CPR == 16 || CPR == 24, "row widths: 64, 128 or 192 dims");
+    __device__ static constexpr int kchunk(int row, int c) {
+        return CPR == 16 ? c ^ (row & 15) : c ^ ((row >> 1) & 7);
+    }
     __device__ static constexpr int vchunk(int row, int c) { return c ^ ((4 * (row & 3)) & (CPR - 1)); }
+};
+
+// Which part of a tile thread `tid` of a workgroup moves (move j of NR).
+// bf16: wave instruction j of wave w fills bytes 1024 (LOADS w + j) .. of
+// the tile, lane i the 16-byte chunk 64 (LOADS w + j) + i, i.e. row
+// chunk / CPR at physical position chunk % CPR.  fp8: 16-byte pieces
+// tid + 256 j of the tile's rows (D / 16 per row) pass through registers.
+template <int D, bool FP8> struct Mover {
+    using T = ExtTile<D>;
+    static constexpr int PPR = D / 16;                 // fp8 16-byte pieces per row
+    static constexpr int NR = FP8 ? D / 64 : T::LOADS;  // moves per thread and tile
+    static_assert(FP8 ? 256 * NR == BN * PPR : 64 * EXT_WAVES * NR == BN * T::CPR, "tile coverage");
+    __device__ static int flat(int tid, int j) { return (T::LOADS * (tid >> 6) + j) * 64 + (tid & 63); }
+    __device__ static int row(int tid, int j) { return FP8 ? (tid + 256 * j) / PPR : flat(tid, j) / T::CPR; }
+    // bf16: physical chunk within the row; fp8: piece within the row
+    __device__ static int pos(int tid, int j) { return FP8 ? (tid + 256 * j) % PPR : flat(tid, j) % T::CPR; }
 };
 
 // Uniform 32-bit load through the scalar data cache (read only).
@@ -127,17 +151,23 @@ __device__ inline void lds_dma16_s(const uint8_t* base, uint32_t voff, const uin
 //   cores run while the vector ALUs compute probabilities.
 // BIGPAGE (page size >= 64): a tile lies in one page, so its pool address is
 // a scalar and each lane only adds a fixed row offset.
-template <int D, bool POS, bool BIGPAGE, bool FP8>
+// DK: key (and query) width; DV: value (and output) width.
+template <int DK, int DV, bool POS, bool BIGPAGE, bool FP8>
 __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void extend_mfma_kernel(AttnArgs a) {
-    using T = ExtTile<D>;
-    constexpr int KSTEPS = D / 16;              // k-steps of q.k (32x32x16)
-    constexpr int VC = D / 32;                  // 32-dim blocks of O^T (d = 32 c + row)
+    using TK = ExtTile<DK>;
+    using TV = ExtTile<DV>;
+    using MK = Mover<DK, FP8>;
+    using MV = Mover<DV, FP8>;
+    static_assert(TV::POW2, "value rows are read by the transposing loads");
+    constexpr bool SAME = DK == DV;             // K and V tiles moved by the same rows
+    constexpr int KSTEPS = DK / 16;             // k-steps of q.k (32x32x16)
+    constexpr int VC = DV / 32;                 // 32-dim blocks of O^T (d = 32 c + row)
     constexpr int SB = BN / 32;                 // 32-key score blocks per tile
     constexpr int PK = BN / 16;                 // P.V k-steps per tile
     constexpr int QPK = KSTEPS * SB / PK;       // next-tile K.Q^T MFMAs per P.V k-step
-    constexpr int ROWS_PER_LOAD = 64 / T::CPR;  // rows one wave instruction fills
-    __shared__ __attribute__((aligned(1024))) uint8_t sK0[T::TILEB], sK1[T::TILEB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sV0[T::TILEB], sV1[T::TILEB];
+    static_assert(QPK * PK == KSTEPS * SB, "K.Q^T MFMAs spread over the P.V k-steps");
+    __shared__ __attribute__((aligned(1024))) uint8_t sK0[TK::TILEB], sK1[TK::TILEB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sV0[TV::TILEB], sV1[TV::TILEB];
 
     // Workgroups are dealt to the 8 XCDs round-robin (linear id mod 8).  The
     // (KV head, item) list is cut into 8 contiguous chunks, one per XCD, so
@@ -178,7 +208,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     bf16x8_t qop[KSTEPS];
     {
         const int32_t qr = min(q0 + qtok, a.N - 1);  // rows past N only under a flagged batch
-        const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + head) * D;
+        const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + head) * DK;
         #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) qop[s] = as_bf16x8(*(const u32x4_t*)(qrow + 16 * s + 8 * hh));
     }
@@ -186,40 +216,44 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int32_t kend = pb + tok_hi;  // keys 0 .. kend-1
     const int32_t ntiles = (kend + BN - 1) / BN;
     constexpr int ESZ = FP8 ? 1 : 2;  // cache bytes per element
-    const int32_t row_bytes = a.Hkv * D * ESZ;
-    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * D * ESZ;
-    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * D * ESZ;
+    const int32_t krow = a.Hkv * DK * ESZ, vrow = a.Hkv * DV * ESZ;  // bytes of one pool slot
+    const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * DK * ESZ;
+    const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * DV * ESZ;
     const int32_t P = 1 << a.page_shift;
 
-    // Moving a tile into LDS.  bf16: direct loads; wave instruction j of wave
-    // w fills LDS rows ROWS_PER_LOAD * (LOADS * w + j) ..; lane i writes
-    // physical chunk i % CPR of its row and fetches the logical chunk the
-    // swizzle puts there.  fp8: thread t loads 16-byte pieces t + 256 j of
-    // the tile's rows (D/16 per row) into registers and, once the current
-    // tile is done, writes them converted to bf16 into the same swizzled
-    // layout.  Rows past the last key repeat it.
-    constexpr int PPR = D / 16;                 // fp8 16-byte pieces per row
-    constexpr int NR = FP8 ? D / 64 : T::LOADS;  // rows moved per thread, tile and tensor
-    const int pc = lane % T::CPR;
-    auto row_of = [&](int j) {
-        if constexpr (FP8) return (tid + 256 * j) / PPR;
-        else return ROWS_PER_LOAD * (T::LOADS * wave + j) + lane / T::CPR;
-    };
-    auto piece_of = [&](int j) { return (tid + 256 * j) % PPR; };  // fp8: piece within its row
-    auto lds_row_block = [&](int j) { return (T::LOADS * wave + j) * 1024; };
+    // Moving a tile into LDS (per tensor, as Mover lays out).  bf16: direct
+    // loads; the lane fetches the logical chunk that the swizzle puts at its
+    // physical position.  fp8: 16-byte pieces are loaded into registers and,
+    // once the current tile is done, written converted to bf16 into the
+    // same swizzled layout.  Rows past the last key repeat it.
+    // Tensor tags: K_ / V_ select the tile type, pool and registers.
+    using K_ = std::integral_constant<bool, false>;
+    using V_ = std::integral_constant<bool, true>;
     // per-thread byte offsets of move j: the fetched chunk within a row (small
     // pages), plus the row within the tile (BIGPAGE)
-    uint32_t koff[NR], voff[NR];
+    uint32_t koff[MK::NR], voff[MV::NR];
     #pragma unroll
-    for (int j = 0; j < NR; ++j) {
-        const int r = row_of(j);
-        koff[j] = (FP8 ? 16 * piece_of(j) : 16 * T::kchunk(r, pc)) + (BIGPAGE ? r * row_bytes : 0);
-        voff[j] = (FP8 ? 16 * piece_of(j) : 16 * T::vchunk(r, pc)) + (BIGPAGE ? r * row_bytes : 0);
+    for (int j = 0; j < MK::NR; ++j) {
+        const int r = MK::row(tid, j);
+        koff[j] = 16 * (FP8 ? MK::pos(tid, j) : TK::kchunk(r, MK::pos(tid, j))) + (BIGPAGE ? r * krow : 0);
     }
-    u32x4_t rk[NR], rv[NR];  // fp8: tiles on their way to LDS
+    #pragma unroll
+    for (int j = 0; j < MV::NR; ++j) {
+        const int r = MV::row(tid, j);
+        voff[j] = 16 * (FP8 ? MV::pos(tid, j) : TV::vchunk(r, MV::pos(tid, j))) + (BIGPAGE ? r * vrow : 0);
+    }
+    u32x4_t rk[MK::NR], rv[MV::NR];  // fp8: tiles on their way to LDS
+    // per-tensor views (the unused branch of each is discarded at compile time)
+    auto offs = [&](auto vt) -> auto& { if constexpr (decltype(vt)::value) return voff; else return koff; };
+    auto regs = [&](auto vt) -> auto& { if constexpr (decltype(vt)::value) return rv; else return rk; };
+    // logical chunk c of row r: its physical position
+    auto phys = [](auto vt, int r, int c) {
+        if constexpr (decltype(vt)::value) return TV::vchunk(r, c);
+        else return TK::kchunk(r, c);
+    };
 
     // pool byte offset of a tile's first row (BIGPAGE; wave-uniform)
-    auto tile_base = [&](int32_t pg, int32_t kt0) -> int64_t {
+    auto tile_base = [&](int32_t pg, int32_t kt0, int32_t row_bytes) -> int64_t {
         pg = min(max(pg, 0), a.num_pages - 1);
         return (((int64_t)pg << a.page_shift) | (kt0 & (P - 1))) * (int64_t)row_bytes;
     };
@@ -228,75 +262,86 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         idx = idx < a.kv_cap ? idx : a.kv_cap - 1;
         return load_uniform(a.kv_indices, idx);
     };
-    // BIGPAGE: one tensor's tile from page pg (V when is_v)
-    auto dma_big = [&](const uint8_t* src, const uint32_t (&off)[NR], bool is_v, int32_t pg,
-                       int32_t kt0, uint8_t* dst) {
-        const uint8_t* tb = src + tile_base(pg, kt0);
+    // BIGPAGE: one tensor's tile from page pg
+    auto dma_big = [&](auto vt, int32_t pg, int32_t kt0, uint8_t* dst) {
+        constexpr bool V = decltype(vt)::value;
+        using M = typename std::conditional<V, MV, MK>::type;
+        using TT = typename std::conditional<V, TV, TK>::type;
+        const int32_t rb = V ? vrow : krow;
+        const uint8_t* tb = (V ? vbase : kbase) + tile_base(pg, kt0, rb);
+        const auto& off = offs(vt);
         const int32_t lim = kend - 1 - kt0;  // last row of the tile holding a key
         if constexpr (FP8) {
-            u32x4_t (&rg)[NR] = is_v ? rv : rk;
+            auto& rg = regs(vt);
             #pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                const uint32_t o = lim >= BN - 1 ? off[j] : (uint32_t)(min(row_of(j), lim) * row_bytes + 16 * piece_of(j));
+            for (int j = 0; j < M::NR; ++j) {
+                const uint32_t o = lim >= BN - 1 ? off[j] : (uint32_t)(min(M::row(tid, j), lim) * rb + 16 * M::pos(tid, j));
                 rg[j] = __builtin_nontemporal_load((const u32x4_t*)(tb + o));
             }
         } else if (lim >= BN - 1) {
             #pragma unroll
-            for (int j = 0; j < NR; ++j) lds_dma16_s(tb, off[j], dst + lds_row_block(j));
+            for (int j = 0; j < M::NR; ++j) lds_dma16_s(tb, off[j], dst + (TT::LOADS * wave + j) * 1024);
         } else {
             #pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                const int r = row_of(j);
-                const int ch = is_v ? T::vchunk(r, pc) : T::kchunk(r, pc);
-                lds_dma16_s(tb, (uint32_t)(min(r, lim) * row_bytes + 16 * ch), dst + lds_row_block(j));
+            for (int j = 0; j < M::NR; ++j) {
+                const int r = M::row(tid, j);
+                const int ch = phys(vt, r, M::pos(tid, j));
+                lds_dma16_s(tb, (uint32_t)(min(r, lim) * rb + 16 * ch), dst + (TT::LOADS * wave + j) * 1024);
             }
         }
     };
     // small pages: per-row slots; raw page ids are looked up an iteration
     // before the slots are formed
-    auto lookup = [&](int32_t kt0, int32_t (&pg)[NR], int32_t (&kp)[NR]) {
+    auto lookup = [&](auto vt, int32_t kt0, auto& pg, auto& kp) {
+        using M = typename std::conditional<decltype(vt)::value, MV, MK>::type;
         #pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            kp[j] = min(kt0 + row_of(j), kend - 1);
+        for (int j = 0; j < M::NR; ++j) {
+            kp[j] = min(kt0 + M::row(tid, j), kend - 1);
             int64_t idx = (int64_t)page_base + (kp[j] >> a.page_shift);
             idx = idx < a.kv_cap ? idx : a.kv_cap - 1;
             pg[j] = a.kv_indices[idx];
         }
     };
-    auto form_slots = [&](const int32_t (&pg)[NR], const int32_t (&kp)[NR], int32_t (&slot)[NR]) {
+    auto form_slots = [&](auto vt, const auto& pg, const auto& kp, auto& slot) {
+        using M = typename std::conditional<decltype(vt)::value, MV, MK>::type;
         #pragma unroll
-        for (int j = 0; j < NR; ++j)
+        for (int j = 0; j < M::NR; ++j)
             slot[j] = (min(max(pg[j], 0), a.num_pages - 1) << a.page_shift) | (kp[j] & (P - 1));
     };
-    auto dma_small = [&](const uint8_t* src, const uint32_t (&choff)[NR], bool is_v,
-                         const int32_t (&slot)[NR], uint8_t* dst) {
+    auto dma_small = [&](auto vt, const auto& slot, uint8_t* dst) {
+        constexpr bool V = decltype(vt)::value;
+        using M = typename std::conditional<V, MV, MK>::type;
+        using TT = typename std::conditional<V, TV, TK>::type;
+        const int32_t rb = V ? vrow : krow;
+        const uint8_t* src = V ? vbase : kbase;
+        const auto& off = offs(vt);
         if constexpr (FP8) {
-            u32x4_t (&rg)[NR] = is_v ? rv : rk;
+            auto& rg = regs(vt);
             #pragma unroll
-            for (int j = 0; j < NR; ++j)
-                rg[j] = __builtin_nontemporal_load((const u32x4_t*)(src + (int64_t)slot[j] * row_bytes + choff[j]));
+            for (int j = 0; j < M::NR; ++j)
+                rg[j] = __builtin_nontemporal_load((const u32x4_t*)(src + (int64_t)slot[j] * rb + off[j]));
         } else {
             #pragma unroll
-            for (int j = 0; j < NR; ++j)
-                lds_dma16(src + (int64_t)slot[j] * row_bytes + choff[j], dst + lds_row_block(j));
+            for (int j = 0; j < M::NR; ++j)
+                lds_dma16(src + (int64_t)slot[j] * rb + off[j], dst + (TT::LOADS * wave + j) * 1024);
         }
     };
     // fp8: write one tensor's tile (registers) into LDS as bf16; each 16-byte
     // piece becomes logical chunks 2 p and 2 p + 1 of its row (exact)
-    auto f8_finish = [&](bool is_v, uint8_t* dst) {
-        const u32x4_t (&rg)[NR] = is_v ? rv : rk;
+    auto f8_finish = [&](auto vt, uint8_t* dst) {
+        using M = typename std::conditional<decltype(vt)::value, MV, MK>::type;
+        using TT = typename std::conditional<decltype(vt)::value, TV, TK>::type;
+        const auto& rg = regs(vt);
         #pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            const int r = row_of(j), p2 = 2 * piece_of(j);
+        for (int j = 0; j < M::NR; ++j) {
+            const int r = M::row(tid, j), p2 = 2 * M::pos(tid, j);
             const u32x4_t w = rg[j];
             const u32x4_t c0 = {fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
                                 fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y)};
             const u32x4_t c1 = {fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
                                 fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w)};
-            const int ph0 = is_v ? T::vchunk(r, p2) : T::kchunk(r, p2);
-            const int ph1 = is_v ? T::vchunk(r, p2 + 1) : T::kchunk(r, p2 + 1);
-            *(u32x4_t*)(dst + r * T::ROWB + 16 * ph0) = c0;
-            *(u32x4_t*)(dst + r * T::ROWB + 16 * ph1) = c1;
+            *(u32x4_t*)(dst + r * TT::ROWB + 16 * phys(vt, r, p2)) = c0;
+            *(u32x4_t*)(dst + r * TT::ROWB + 16 * phys(vt, r, p2 + 1)) = c1;
         }
     };
 
@@ -319,7 +364,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     auto qk_mfma = [&](const uint8_t* ks_, int q, f32x16_t* S) {
         const int s = q / SB, u = q % SB;
         const int row = 32 * u + n;
-        const u32x4_t kw = *(const u32x4_t*)(ks_ + row * T::ROWB + 16 * T::kchunk(row, 2 * s + hh));
+        const u32x4_t kw = *(const u32x4_t*)(ks_ + row * TK::ROWB + 16 * TK::kchunk(row, 2 * s + hh));
         // the first k-step starts from an inline zero accumulator
         S[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kw), qop[s], s == 0 ? f32x16_t{} : S[u],
                                                        0, 0, 0);
@@ -331,39 +376,61 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
 
     // prologue: K(0), V(0), K(1) resident, S(0) computed
     int32_t pgK = 0, pgV = 0;        // BIGPAGE: pages of tiles t+2 (K) and t+1 (V)
-    int32_t rawK[NR], kpK[NR], slotK[NR], slotV[NR];  // small pages
+    // small pages.  Equal widths: V(t+1) reuses the slots K(t+1) was loaded
+    // with.  Otherwise V's rows have lookups of their own, also an iteration
+    // ahead (rawV holds the page ids of V(t+1) at the top of iteration t).
+    int32_t rawK[MK::NR], kpK[MK::NR], slotK[MK::NR];
+    int32_t rawV[MV::NR], kpV[MV::NR], slotV[MV::NR];
     if constexpr (BIGPAGE) {
         const int32_t p0 = page_of_tile(0);
-        dma_big(kbase, koff, false, p0, 0, sK0);
-        dma_big(vbase, voff, true, p0, 0, sV0);
+        dma_big(K_{}, p0, 0, sK0);
+        dma_big(V_{}, p0, 0, sV0);
         if constexpr (FP8) {
-            f8_finish(false, sK0);
-            f8_finish(true, sV0);
+            f8_finish(K_{}, sK0);
+            f8_finish(V_{}, sV0);
         }
         if (ntiles > 1) {
             const int32_t p1 = page_of_tile(BN);
-            dma_big(kbase, koff, false, p1, BN, sK1);
-            if constexpr (FP8) f8_finish(false, sK1);
+            dma_big(K_{}, p1, BN, sK1);
+            if constexpr (FP8) f8_finish(K_{}, sK1);
             pgV = p1;
         }
         if (ntiles > 2) pgK = page_of_tile(2 * BN);
-    } else {
-        int32_t s0[NR];
-        lookup(0, rawK, kpK);
-        form_slots(rawK, kpK, s0);
-        dma_small(kbase, koff, false, s0, sK0);
-        dma_small(vbase, voff, true, s0, sV0);
+    } else if constexpr (SAME) {
+        lookup(K_{}, 0, rawK, kpK);
+        form_slots(K_{}, rawK, kpK, slotK);
+        dma_small(K_{}, slotK, sK0);
+        dma_small(V_{}, slotK, sV0);
         if constexpr (FP8) {
-            f8_finish(false, sK0);
-            f8_finish(true, sV0);
+            f8_finish(K_{}, sK0);
+            f8_finish(V_{}, sV0);
         }
-        lookup(BN, rawK, kpK);
-        form_slots(rawK, kpK, slotV);
+        lookup(K_{}, BN, rawK, kpK);
+        form_slots(K_{}, rawK, kpK, slotV);
         if (ntiles > 1) {
-            dma_small(kbase, koff, false, slotV, sK1);
-            if constexpr (FP8) f8_finish(false, sK1);
+            dma_small(K_{}, slotV, sK1);
+            if constexpr (FP8) f8_finish(K_{}, sK1);
         }
-        lookup(2 * BN, rawK, kpK);
+        lookup(K_{}, 2 * BN, rawK, kpK);
+    } else {
+        lookup(K_{}, 0, rawK, kpK);
+        form_slots(K_{}, rawK, kpK, slotK);
+        dma_small(K_{}, slotK, sK0);
+        lookup(V_{}, 0, rawV, kpV);
+        form_slots(V_{}, rawV, kpV, slotV);
+        dma_small(V_{}, slotV, sV0);
+        if constexpr (FP8) {
+            f8_finish(K_{}, sK0);
+            f8_finish(V_{}, sV0);
+        }
+        if (ntiles > 1) {
+            lookup(K_{}, BN, rawK, kpK);
+            form_slots(K_{}, rawK, kpK, slotK);
+            dma_small(K_{}, slotK, sK1);
+            if constexpr (FP8) f8_finish(K_{}, sK1);
+        }
+        lookup(V_{}, BN, rawV, kpV);
+        lookup(K_{}, 2 * BN, rawK, kpK);
     }
     if constexpr (!FP8) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the direct loads landed
     __syncthreads();
@@ -384,18 +451,29 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         if constexpr (!FP8) __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();  // ... for every wave; iteration t-1 is done
         if constexpr (BIGPAGE) {
-            if (t + 2 < ntiles) dma_big(kbase, koff, false, pgK, kt0 + 2 * BN, kdst);
-            if (NEXT) dma_big(vbase, voff, true, pgV, kt0 + BN, vdst);
+            if (t + 2 < ntiles) dma_big(K_{}, pgK, kt0 + 2 * BN, kdst);
+            if (NEXT) dma_big(V_{}, pgV, kt0 + BN, vdst);
             pgV = pgK;
             if (t + 3 < ntiles) pgK = page_of_tile(kt0 + 3 * BN);
-        } else {
-            if (NEXT) dma_small(vbase, voff, true, slotV, vdst);
+        } else if constexpr (SAME) {
+            if (NEXT) dma_small(V_{}, slotV, vdst);
             if (t + 2 < ntiles) {
-                form_slots(rawK, kpK, slotK);
-                dma_small(kbase, koff, false, slotK, kdst);
+                form_slots(K_{}, rawK, kpK, slotK);
+                dma_small(K_{}, slotK, kdst);
                 #pragma unroll
-                for (int j = 0; j < NR; ++j) slotV[j] = slotK[j];
-                lookup(kt0 + 3 * BN, rawK, kpK);
+                for (int j = 0; j < MK::NR; ++j) slotV[j] = slotK[j];
+                lookup(K_{}, kt0 + 3 * BN, rawK, kpK);
+            }
+        } else {
+            if (NEXT) {
+                form_slots(V_{}, rawV, kpV, slotV);
+                dma_small(V_{}, slotV, vdst);
+                lookup(V_{}, kt0 + 2 * BN, rawV, kpV);
+            }
+            if (t + 2 < ntiles) {
+                form_slots(K_{}, rawK, kpK, slotK);
+                dma_small(K_{}, slotK, kdst);
+                lookup(K_{}, kt0 + 3 * BN, rawK, kpK);
             }
         }
 
@@ -457,7 +535,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 for (int r = 0; r < 2; ++r) {
                     const int row = 16 * pk + 8 * r + v_row;
                     const int lc = 4 * c + (v_byte >> 4);
-                    const uint8_t* p = vcur + row * T::ROWB + 16 * T::vchunk(row, lc) + (v_byte & 15);
+                    const uint8_t* p = vcur + row * TV::ROWB + 16 * TV::vchunk(row, lc) + (v_byte & 15);
                     half[r] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
                 }
                 const u32x4_t av = {half[0][0], half[0][1], half[1][0], half[1][1]};
@@ -467,8 +545,8 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         // fp8: the next tiles go into the stages this iteration did not read;
         // the next iteration's barrier publishes them
         if constexpr (FP8) {
-            if (t + 2 < ntiles) f8_finish(false, kdst);
-            if (NEXT) f8_finish(true, vdst);
+            if (t + 2 < ntiles) f8_finish(K_{}, kdst);
+            if (NEXT) f8_finish(V_{}, vdst);
         }
     };
 
@@ -490,7 +568,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const float ltot = sum_halves(lsum);
     if (!col_ok) return;
     const float inv = a.v_scale / ltot;  // v_scale: fp8 V dequantisation (1 otherwise)
-    __bf16* orow = (__bf16*)a.out + ((int64_t)(q0 + ctok) * a.Hq + head) * D;
+    __bf16* orow = (__bf16*)a.out + ((int64_t)(q0 + ctok) * a.Hq + head) * DV;
     #pragma unroll
     for (int c = 0; c < VC; ++c)
         #pragma unroll
@@ -505,9 +583,9 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
 }
 
 // fp32 variant: one wave per (new token, query head), lanes over head_dim.
-template <int D>
+template <int DK, int DV>
 __global__ __launch_bounds__(256) void extend_f32_kernel(AttnArgs a) {
-    constexpr int EPL = D / 64;
+    constexpr int EPK = DK / 64, EPV = DV / 64;  // key and value dims per lane
     const int lane = threadIdx.x & 63;
     const int32_t item = blockIdx.x;
     if (item >= a.plan[PLAN_EXT_COUNT]) return;
@@ -523,18 +601,17 @@ __global__ __launch_bounds__(256) void extend_f32_kernel(AttnArgs a) {
     const int32_t page_base = a.kv_indptr[b];
     for (int32_t i = ti * TQ; i < min(ti * TQ + TQ, nb); ++i) {
         if (q0 + i >= a.N) break;
-        float q[EPL], o[EPL];
+        float q[EPK], o[EPV];
         #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            q[e] = ((const float*)a.q)[((int64_t)(q0 + i) * a.Hq + h) * D + e * 64 + lane];
-            o[e] = 0.f;
-        }
+        for (int e = 0; e < EPK; ++e) q[e] = ((const float*)a.q)[((int64_t)(q0 + i) * a.Hq + h) * DK + e * 64 + lane];
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) o[e] = 0.f;
         float m = -INFINITY, l = 0.f;
         for (int32_t t = 0; t <= pb + i; ++t) {
-            const int64_t base = ((int64_t)slot_of(a, page_base, t) * a.Hkv + g) * D;
+            const int64_t sg = (int64_t)slot_of(a, page_base, t) * a.Hkv + g;
             float dot = 0.f;
             #pragma unroll
-            for (int e = 0; e < EPL; ++e) dot += q[e] * ((const float*)a.k_pool)[base + e * 64 + lane];
+            for (int e = 0; e < EPK; ++e) dot += q[e] * ((const float*)a.k_pool)[sg * DK + e * 64 + lane];
             #pragma unroll
             for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off);
             const float s = dot * a.scale_log2;
@@ -544,12 +621,12 @@ __global__ __launch_bounds__(256) void extend_f32_kernel(AttnArgs a) {
             m = mn;
             l = l * al + p;
             #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                o[e] = o[e] * al + p * ((const float*)a.v_pool)[base + e * 64 + lane];
+            for (int e = 0; e < EPV; ++e)
+                o[e] = o[e] * al + p * ((const float*)a.v_pool)[sg * DV + e * 64 + lane];
         }
         #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            ((float*)a.out)[((int64_t)(q0 + i) * a.Hq + h) * D + e * 64 + lane] = o[e] / l;
+        for (int e = 0; e < EPV; ++e)
+            ((float*)a.out)[((int64_t)(q0 + i) * a.Hq + h) * DV + e * 64 + lane] = o[e] / l;
         if (a.lse && lane == 0)
             a.lse[(int64_t)(q0 + i) * a.Hq + h] = (m + __builtin_amdgcn_logf(l)) * LN2;
     }
@@ -557,7 +634,7 @@ __global__ __launch_bounds__(256) void extend_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int extend_tq(pka_dtype q, pka_dtype /*kv*/, int /*D*/, int G, int /*page_size*/) {
+int extend_tq(pka_dtype q, pka_dtype /*kv*/, int G, int /*page_size*/) {
     if (q == PKA_F32) return 16;
     return G >= EXT_COLS ? 1 : EXT_COLS / G;
 }
@@ -567,31 +644,35 @@ int extend_max_group(pka_dtype q, int /*page_size*/) {
     return EXT_COLS;
 }
 
-hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hipStream_t s) {
+hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, hipStream_t s) {
     const int P = 1 << a.page_shift;
-    const int tq = extend_tq(q, kv, D, a.G, P);
+    const int tq = extend_tq(q, kv, a.G, P);
     const int64_t items = plan_ext_capacity(a.B, a.N, tq);
     if (items == 0) return hipSuccess;
     if (q == PKA_F32) {
         const dim3 grid((unsigned)items, (a.Hq + 3) / 4);
-        if (D == 128) hipLaunchKernelGGL((extend_f32_kernel<128>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((extend_f32_kernel<64>), grid, dim3(256), 0, s, a);
+        if (DK == 128 && DV == 128) hipLaunchKernelGGL((extend_f32_kernel<128, 128>), grid, dim3(256), 0, s, a);
+        else if (DK == 64 && DV == 64) hipLaunchKernelGGL((extend_f32_kernel<64, 64>), grid, dim3(256), 0, s, a);
+        else if (DK == 192 && DV == 128) hipLaunchKernelGGL((extend_f32_kernel<192, 128>), grid, dim3(256), 0, s, a);
+        else return hipErrorInvalidValue;
         return hipGetLastError();
     }
     if (items * a.Hkv * 64 * EXT_WAVES > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)(items * a.Hkv));
     const bool pos = a.scale_log2 > 0.f;
     const bool big = P >= BN;
-#define PKA_EXT(D_, POS_, BIG_, F8_) \
-    hipLaunchKernelGGL((extend_mfma_kernel<D_, POS_, BIG_, F8_>), grid, dim3(64 * EXT_WAVES), 0, s, a)
-#define PKA_EXT_D(D_, F8_)                                                              \
-    do {                                                                                \
-        if (pos) { if (big) PKA_EXT(D_, true, true, F8_); else PKA_EXT(D_, true, false, F8_); }   \
-        else { if (big) PKA_EXT(D_, false, true, F8_); else PKA_EXT(D_, false, false, F8_); }     \
+#define PKA_EXT(DK_, DV_, POS_, BIG_, F8_) \
+    hipLaunchKernelGGL((extend_mfma_kernel<DK_, DV_, POS_, BIG_, F8_>), grid, dim3(64 * EXT_WAVES), 0, s, a)
+#define PKA_EXT_D(DK_, DV_, F8_)                                                                          \
+    do {                                                                                                  \
+        if (pos) { if (big) PKA_EXT(DK_, DV_, true, true, F8_); else PKA_EXT(DK_, DV_, true, false, F8_); }   \
+        else { if (big) PKA_EXT(DK_, DV_, false, true, F8_); else PKA_EXT(DK_, DV_, false, false, F8_); }     \
     } while (0)
     const bool f8 = kv == PKA_FP8_E4M3FN;
-    if (D == 128) { if (f8) PKA_EXT_D(128, true); else PKA_EXT_D(128, false); }
-    else { if (f8) PKA_EXT_D(64, true); else PKA_EXT_D(64, false); }
+    if (DK == 128 && DV == 128) { if (f8) PKA_EXT_D(128, 128, true); else PKA_EXT_D(128, 128, false); }
+    else if (DK == 64 && DV == 64) { if (f8) PKA_EXT_D(64, 64, true); else PKA_EXT_D(64, 64, false); }
+    else if (DK == 192 && DV == 128) { if (f8) PKA_EXT_D(192, 128, true); else PKA_EXT_D(192, 128, false); }
+    else return hipErrorInvalidValue;
 #undef PKA_EXT_D
 #undef PKA_EXT
     return hipGetLastError();

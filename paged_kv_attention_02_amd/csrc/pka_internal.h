@@ -84,7 +84,8 @@ struct SaveArgs {
     const int32_t* out_cache_loc;
     int32_t* plan;
     int32_t N;
-    int32_t row_elems;  // Hkv * D
+    int32_t k_row_elems;  // Hkv * key width
+    int32_t v_row_elems;  // Hkv * value width
     int64_t pool_slots;
     float k_inv;  // fp32(1 / k_scale)
     float v_inv;
@@ -96,7 +97,7 @@ struct AttnArgs {
     const void* v_pool;
     void* out;
     float* lse;
-    float* ws_o;    // split partials [(B + nwg), Hq, D] fp32
+    float* ws_o;    // split partials [(B + nwg) * qslots, Hq, value width] fp32
     float* ws_lse;  // [(B + nwg), Hq]
     const int32_t* kv_indptr;
     const int32_t* kv_indices;
@@ -130,16 +131,17 @@ struct AttnArgs {
 };
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
-hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, int D, const SaveArgs& a, hipStream_t s);
-hipError_t launch_decode(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, int waves_per_wg,
-                         hipStream_t s);
-hipError_t launch_extend(pka_dtype q, pka_dtype kv, int D, const AttnArgs& a, hipStream_t s);
+// DK: key (and query) head width; DV: value (and output) head width.
+hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, const SaveArgs& a, hipStream_t s);
+hipError_t launch_decode(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a,
+                         int waves_per_wg, hipStream_t s);
+hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, hipStream_t s);
 
 // Decode workgroups of `wpb` waves that fit on one compute unit at once.
-int decode_blocks_per_cu(pka_dtype kv, int D, int wpb);
+int decode_blocks_per_cu(pka_dtype kv, int DK, int DV, int wpb);
 
 // Query tokens per extend item for a dtype pair.
-int extend_tq(pka_dtype q, pka_dtype kv, int D, int G, int page_size);
+int extend_tq(pka_dtype q, pka_dtype kv, int G, int page_size);
 // largest query-head group (Hq / Hkv) the extend kernels cover
 int extend_max_group(pka_dtype q, int page_size);
 

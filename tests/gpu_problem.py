@@ -29,10 +29,9 @@ class GpuProblem:
         self.values = values
         self.ctx = pka.Context(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                                layout.num_pages, spec.q_dtype, spec.kv_dtype, spec.softmax_scale,
-                               values.k_scale, values.v_scale)
-        shape = self.ctx.pool_shape()
-        self.k_pool = sentinel_pool_gpu(shape, spec.kv_dtype, device)
-        self.v_pool = sentinel_pool_gpu(shape, spec.kv_dtype, device)
+                               values.k_scale, values.v_scale, v_head_dim=spec.value_dim)
+        self.k_pool = sentinel_pool_gpu(self.ctx.pool_shape(), spec.kv_dtype, device)
+        self.v_pool = sentinel_pool_gpu(self.ctx.v_pool_shape(), spec.kv_dtype, device)
         i32 = dict(dtype=torch.int32, device=device)
         self.seq_lens = torch.tensor(layout.seq_lens, **i32)
         self.extend_lens = torch.tensor(layout.extend_lens, **i32)
@@ -47,7 +46,7 @@ class GpuProblem:
         rows = torch.from_numpy(workloads.new_token_rows(layout)).to(device)
         self.k_new = values.k_all.index_select(0, rows).contiguous()
         self.v_new = values.v_all.index_select(0, rows).contiguous()
-        self.out = torch.empty((layout.num_q_tokens, spec.num_q_heads, spec.head_dim),
+        self.out = torch.empty((layout.num_q_tokens, spec.num_q_heads, spec.value_dim),
                                dtype=workloads.torch_dtype(spec.q_dtype), device=device)
         self.lse = torch.empty((layout.num_q_tokens, spec.num_q_heads), dtype=torch.float32,
                                device=device)

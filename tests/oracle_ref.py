@@ -42,7 +42,7 @@ def oracle_pools(layout: workloads.Layout, k_all: np.ndarray, v_all: np.ndarray,
                          layout.num_pages)
     slots = layout.num_pages * spec.page_size
     kp = sentinel_pool(slots, spec.num_kv_heads, spec.head_dim, spec.kv_dtype)
-    vp = sentinel_pool(slots, spec.num_kv_heads, spec.head_dim, spec.kv_dtype)
+    vp = sentinel_pool(slots, spec.num_kv_heads, spec.value_dim, spec.kv_dtype)
     oracle.save_kv(md["out_cache_loc"], k_all, v_all, spec.q_dtype, spec.kv_dtype, kp, vp,
                    k_scale, v_scale)
     return kp, vp
@@ -67,7 +67,7 @@ def oracle_requests(layout: workloads.Layout, values: workloads.Values, requests
     Each selected request is re-packed into a compact single-request problem
     (its own tokens, contiguous pages); attention of a request does not depend
     on where its pages sit in the pool.  ``tokens(n_b)`` may pick a subset of
-    the request's new tokens.  Returns {b: (token_idx, out [t, H, D], lse [t, H])}.
+    the request's new tokens.  Returns {b: (token_idx, out [t, H, Dv], lse [t, H])}.
     """
     spec = layout.spec
     offs = workloads.request_token_offsets(layout)
@@ -91,7 +91,7 @@ def oracle_requests(layout: workloads.Layout, values: workloads.Values, requests
         out, lse = oracle.attention(sub.seq_lens, ext, sub.page_table, P, pages, q, spec.q_dtype,
                                     kp, vp, spec.kv_dtype, spec.softmax_scale, values.k_scale,
                                     values.v_scale, sel=sel, threads=threads)
-        res[b] = (np.asarray(ts, dtype=np.int64), out.reshape(len(ts), len(hs), spec.head_dim),
+        res[b] = (np.asarray(ts, dtype=np.int64), out.reshape(len(ts), len(hs), spec.value_dim),
                   lse.reshape(len(ts), len(hs)))
     return res
 

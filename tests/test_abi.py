@@ -63,12 +63,23 @@ def test_create_accepts_supported_configs():
     assert _create(num_q_heads=8, num_kv_heads=8, page_size=256) == 0
     assert _create(num_q_heads=128, num_kv_heads=1) == 0      # largest bf16 head group
     assert _create(num_q_heads=512, num_kv_heads=2, head_dim=64, q_dtype=0, kv_dtype=0) == 0
+    # value heads narrower than key heads (0 = the key width)
+    assert _create(head_dim=192, v_head_dim=128) == 0
+    assert _create(head_dim=192, v_head_dim=128, kv_dtype=2, k_scale=0.01, v_scale=0.01) == 0
+    assert _create(head_dim=192, v_head_dim=128, q_dtype=0, kv_dtype=0, page_size=1) == 0
+    assert _create(head_dim=128, v_head_dim=128) == 0
+    assert _create(head_dim=64, v_head_dim=0) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=30), -1),              # not a multiple of num_kv_heads
     (dict(num_kv_heads=0), -1),
     (dict(head_dim=96), -2),                 # unsupported head_dim
+    (dict(head_dim=192), -2),                # 192-wide values
+    (dict(head_dim=192, v_head_dim=192), -2),
+    (dict(head_dim=128, v_head_dim=64), -2),  # unsupported width pair
+    (dict(head_dim=64, v_head_dim=128), -2),
+    (dict(head_dim=192, v_head_dim=-128), -2),
     (dict(page_size=24), -2),                # not a power of two
     (dict(page_size=512), -2),
     (dict(num_pages=0), -1),
@@ -84,6 +95,16 @@ def test_create_accepts_supported_configs():
 def test_create_refuses(kw, status):
     assert _create(**kw) == status
     assert pka.lib().pka_last_error()
+
+
+def test_workspace_scales_with_value_width():
+    """Decode partials hold value-width rows: the workspace of a 192 / 128
+    context equals that of a 128 / 128 one with the same heads."""
+    a = pka.Context(16, 4, 192, 16, 100, v_head_dim=128).sizes("decode", 8, 8, 80)
+    b = pka.Context(16, 4, 128, 16, 100).sizes("decode", 8, 8, 80)
+    assert a.workspace_bytes == b.workspace_bytes > 0
+    ctx = pka.Context(16, 4, 192, 16, 100, v_head_dim=128)
+    assert ctx.pool_shape() == (1600, 4, 192) and ctx.v_pool_shape() == (1600, 4, 128)
 
 
 def test_batch_sizes_and_refusals():

@@ -58,6 +58,11 @@ class Spec:
     scale: Optional[float] = None  # None -> 1/sqrt(head_dim)
     v_mean: float = 0.0
     q_mult: float = 1.0
+    v_head_dim: Optional[int] = None  # None -> head_dim
+
+    @property
+    def value_dim(self) -> int:
+        return self.head_dim if self.v_head_dim is None else self.v_head_dim
 
     @property
     def group(self) -> int:
@@ -90,6 +95,16 @@ CONFIGS = {
 EXTRA = {
     "l4_log_decode": Spec("l4_log_decode_bf16_b33_g4_d128_p1", "decode", 33, 32, 8, 128, 1, "bf16",
                           "bf16", seed=11, seq_len_kind="uniform", seq_len_args=(519, 719)),
+    # Key and value heads of different widths (the pages have a backend picked
+    # for such models): 192-wide query/key heads (128 + a 64-wide rotary part)
+    # against 128-wide values, 16 heads of one rank, plain multi-head (G = 1),
+    # pages of 128 tokens (the native page size the pages give that backend).
+    "asym_extend": Spec("asym_extend_bf16_b8_h16_dk192_dv128_p128", "extend", 8, 16, 16, 192, 128,
+                        "bf16", "bf16", seed=12, new_len_args=(512, 2048),
+                        prefix_len_args=(0, 4096), v_head_dim=128),
+    "asym_decode": Spec("asym_decode_bf16_b64_h16_dk192_dv128_p128", "decode", 64, 16, 16, 192, 128,
+                        "bf16", "bf16", seed=13, seq_len_kind="uniform",
+                        seq_len_args=(512, 8192), v_head_dim=128),
 }
 
 
@@ -178,7 +193,7 @@ class Values:
 
     q: "object"  # [N, Hq, D] in the Q dtype
     k_all: "object"  # [sum L, Hkv, D] in the Q dtype, request-major, position order
-    v_all: "object"
+    v_all: "object"  # [sum L, Hkv, Dv]
     k_scale: float  # fp32 per-tensor fp8 scale (1.0 for non-fp8 caches)
     v_scale: float
 
@@ -198,8 +213,8 @@ def make_values(layout: Layout, device="cpu") -> Values:
     Hq, Hkv, D = spec.num_q_heads, spec.num_kv_heads, spec.head_dim
     dt = torch_dtype(spec.q_dtype)
 
-    def draw(rows, heads, mean=0.0, mult=1.0):
-        x = torch.randn((rows, heads, D), generator=g, device=device, dtype=torch.float32)
+    def draw(rows, heads, mean=0.0, mult=1.0, width=D):
+        x = torch.randn((rows, heads, width), generator=g, device=device, dtype=torch.float32)
         if mult != 1.0:
             x.mul_(mult)
         if mean != 0.0:
@@ -208,7 +223,7 @@ def make_values(layout: Layout, device="cpu") -> Values:
 
     q = draw(N, Hq, mult=spec.q_mult)
     k = draw(T, Hkv)
-    v = draw(T, Hkv, mean=spec.v_mean)
+    v = draw(T, Hkv, mean=spec.v_mean, width=spec.value_dim)
     ks = vs = 1.0
     if spec.kv_dtype == "fp8":
         ks = float(np.float32(float(k.abs().amax().float()) / FP8_E4M3FN_MAX))
