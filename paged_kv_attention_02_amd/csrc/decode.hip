@@ -117,33 +117,81 @@ struct DecodeShape {
     using vrow_t = typename std::conditional<
         CPL * ESZ == 16, u32x4_t,
         typename std::conditional<CPL * ESZ == 8, u32x2_t, uint32_t>::type>::type;
+    // K rows of up to 256 bytes go through a per-wave LDS tile (see
+    // load_tile); wider rows are loaded straight into registers.
+    static constexpr int KROW = DK * ESZ;       // bytes of one token's K row (one head)
+    static constexpr int KCPR = KROW / 16;      // 16-byte chunks per K row
+    static constexpr bool KLDS = KROW <= 256;
+    static constexpr int KDMA = KCPR / 2;       // direct-to-LDS loads per lane and tile
+    static constexpr int KTILE = DEC_TILE * KROW;  // bytes of one LDS K tile
+    static_assert(KCPR == 4 || KCPR == 8 || KCPR == 12 || KCPR == 16 || KCPR == 24, "K row width");
+    // Chunk swizzle of the LDS K tile: the K operand reads 16 rows at one
+    // logical chunk, and those 16 rows must hit 16 different 16-byte bank
+    // groups (256 bytes per bank cycle).  An XOR inside the chunk's aligned
+    // group keeps every chunk in its row.
+    __device__ static constexpr int kswz(int row, int c) {
+        return KCPR == 16 ? c ^ (row & 15)
+             : (KCPR == 8 || KCPR == 24) ? c ^ ((row >> 1) & 7)
+             : c ^ ((row >> 2) & 3);
+    }
 };
 
-// One 32-token tile of K and V in registers.  Row block sb of K holds tile
-// tokens 16*sb + n (lane n = lane & 15); V k-slot q of lane group j holds
-// tile token 16*(q/4) + 4*j + q%4, the order in which the scores come out of
-// the first MFMA, so P^T needs no shuffle.
+// Direct HBM -> LDS load of 16 bytes per lane: lane i's bytes land at
+// lds_dst + 16 * i (lds_dst is wave-uniform).  The compiler does not track
+// it: the kernel waits for it with an explicit vmcnt(0) before the tile is
+// read.
+__device__ inline void lds_dma16(const void* src, const uint8_t* lds_dst) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+    // one wait state between the M0 write and the LDS-DMA instruction reading it
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
+                 : "m0", "memory");
+}
+
+// One 32-token tile: V in registers, K in registers or in the wave's LDS
+// stage `kst`.  Row block sb of K holds tile tokens 16*sb + n (lane n =
+// lane & 15); V k-slot q of lane group j holds tile token 16*(q/4) + 4*j +
+// q%4, the order in which the scores come out of the first MFMA, so P^T
+// needs no shuffle.
 template <int DK, int DV, bool FP8>
 struct KVTile {
     using S = DecodeShape<DK, DV, FP8>;
-    u32x4_t kr[2][S::NKL];
+    u32x4_t kr[2][S::KLDS ? 1 : S::NKL];
     typename S::vrow_t vr[8];
+    uint8_t* kst;
 };
 
 // Issue the loads of one tile.  `slot` is the pool slot of tile token
 // (lane & 31); lanes exchange slots with cross-lane moves.  The cache is
 // read once per call, so the loads carry the non-temporal hint.
+//
+// K through LDS: a wave instruction moves 1 KB of the tile, lane i the
+// 16-byte chunk f = 64 q + i of the tile's rows laid end to end (row f / KCPR,
+// physical chunk f % KCPR, fetched from the logical chunk the swizzle puts
+// there), so every instruction reads whole 128- or 256-byte row pieces; the
+// K operand's own layout (four lanes per token) would read 64-byte pieces,
+// which HBM serves markedly slower.
 template <int DK, int DV, bool FP8>
 __device__ inline void load_tile(KVTile<DK, DV, FP8>& T, int32_t slot, const uint8_t* kbase,
                                  const uint8_t* vbase, int64_t krow, int64_t vrow, int n, int j) {
     using S = DecodeShape<DK, DV, FP8>;
-    const int32_t slot_x = __shfl_xor(slot, 16);
-    const int32_t ks0 = (j & 1) ? slot_x : slot;
-    const int32_t ks1 = (j & 1) ? slot : slot_x;
-    #pragma unroll
-    for (int s = 0; s < S::NKL; ++s) {
-        T.kr[0][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks0 * krow + s * 64 + j * 16));
-        T.kr[1][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks1 * krow + s * 64 + j * 16));
+    const int lane = threadIdx.x & 63;
+    if constexpr (S::KLDS) {
+        #pragma unroll
+        for (int q = 0; q < S::KDMA; ++q) {
+            const int f = 64 * q + lane;
+            const int row = f / S::KCPR, pc = f % S::KCPR;
+            const int32_t ks = __shfl(slot, row);
+            lds_dma16(kbase + ks * krow + 16 * S::kswz(row, pc), T.kst + 1024 * q);
+        }
+    } else {
+        const int32_t slot_x = __shfl_xor(slot, 16);
+        const int32_t ks0 = (j & 1) ? slot_x : slot;
+        const int32_t ks1 = (j & 1) ? slot : slot_x;
+        #pragma unroll
+        for (int s = 0; s < S::NKL; ++s) {
+            T.kr[0][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks0 * krow + s * 64 + j * 16));
+            T.kr[1][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks1 * krow + s * 64 + j * 16));
+        }
     }
     #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -162,6 +210,17 @@ __device__ inline void compute_tile(const KVTile<DK, DV, FP8>& T, const bf16x8_t
                                     f32x4_t* O, float& m2, float& lsum, int valid,
                                     float scale_log2, int j) {
     using S = DecodeShape<DK, DV, FP8>;
+    const int n = threadIdx.x & 15;
+    // 16 bytes of K for row block sb, load slot s: chunk 4 s + j of token 16 sb + n
+    auto kraw = [&](int sb, int s) -> u32x4_t {
+        if constexpr (S::KLDS) {
+            const int row = 16 * sb + n;
+            typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+            return *(lds_u32x4_t*)(T.kst + row * S::KROW + 16 * S::kswz(row, 4 * s + j));
+        } else {
+            return T.kr[sb][s];
+        }
+    };
     // S^T = K . Q^T, two 16-token row blocks
     f32x4_t st[2];
     #pragma unroll
@@ -171,13 +230,13 @@ __device__ inline void compute_tile(const KVTile<DK, DV, FP8>& T, const bf16x8_t
         for (int ks = 0; ks < S::KSTEPS; ++ks) {
             u32x4_t kw;
             if constexpr (FP8) {
-                const u32x4_t raw = T.kr[sb][ks / S::SPL];
+                const u32x4_t raw = kraw(sb, ks / S::SPL);
                 const uint32_t w0 = (ks % S::SPL) ? raw.z : raw.x;
                 const uint32_t w1 = (ks % S::SPL) ? raw.w : raw.y;
                 kw = u32x4_t{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
                              fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
             } else {
-                kw = T.kr[sb][ks];
+                kw = kraw(sb, ks);
             }
             st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[ks], st[sb], 0, 0, 0);
         }
@@ -283,6 +342,19 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * DK * S::ESZ;
     const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * DV * S::ESZ;
     const int tok = lane & 31;  // tile token whose slot this lane looks up
+    // this wave's two LDS K stages (K rows of up to 256 bytes)
+    extern __shared__ __attribute__((aligned(1024))) uint8_t dec_lds[];
+    uint8_t* const kst0 = dec_lds + (threadIdx.x >> 6) * 2 * S::KTILE;
+    // K through LDS: the loads of a tile are waited for (vmcnt(0)) before the
+    // next tile's loads are issued and the tile is computed; the compiler
+    // fence keeps the LDS reads after the wait and the next direct loads
+    // after the reads of the stage they overwrite
+    auto landed = [&]() {
+        if constexpr (S::KLDS) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+            asm volatile("" ::: "memory");
+        }
+    };
 
     for (; seg < a.B; ++seg) {
         const int32_t f0 = F[seg], f1 = F[seg + 1];
@@ -327,8 +399,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             const int32_t kend_c = MQ ? min(hi, pfx + qi + 1) : hi;
 
             KVTile<DK, DV, FP8> A, Bt;
+            A.kst = kst0;
+            Bt.kst = kst0 + S::KTILE;
             int32_t slot_a = slot_at(lo);
             int32_t slot_b = slot_at(lo + DEC_TILE);
+            landed();  // loads of the previous piece into these stages are done
             load_tile(A, slot_a, kbase, vbase, krow, vrow, n, j);
 
             // Q^T operand: lane (n, j) holds its column at the dims its K lanes load.
@@ -349,16 +424,20 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             for (int cc = 0; cc < S::CPL; ++cc) O[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             float m2 = -INFINITY, lsum = 0.f;
 
-            // Two tiles in flight: while one tile is consumed the next one's
-            // loads are outstanding.  Loads are issued unconditionally (past
-            // the end they re-read the piece's last row) so the wait counts
-            // are the same on every iteration.
+            // While one tile is consumed the next one's loads are
+            // outstanding.  With K in registers the loads are issued
+            // unconditionally (past the end they re-read the piece's last
+            // row) so the compiler's wait counts are the same on every
+            // iteration; with K through LDS every tile is waited for
+            // explicitly and no load goes past the piece.
             for (int32_t t0 = lo;; t0 += 2 * DEC_TILE) {
-                load_tile(Bt, slot_b, kbase, vbase, krow, vrow, n, j);
+                landed();
+                if (!S::KLDS || t0 + DEC_TILE < hi) load_tile(Bt, slot_b, kbase, vbase, krow, vrow, n, j);
                 slot_a = slot_at(t0 + 2 * DEC_TILE);
                 compute_tile<DK, DV, FP8, MQ>(A, qop, O, m2, lsum, kend_c - t0, a.scale_log2, j);
                 if (t0 + DEC_TILE >= hi) break;
-                load_tile(A, slot_a, kbase, vbase, krow, vrow, n, j);
+                landed();
+                if (!S::KLDS || t0 + 2 * DEC_TILE < hi) load_tile(A, slot_a, kbase, vbase, krow, vrow, n, j);
                 slot_b = slot_at(t0 + 3 * DEC_TILE);
                 compute_tile<DK, DV, FP8, MQ>(Bt, qop, O, m2, lsum, kend_c - t0 - DEC_TILE, a.scale_log2, j);
                 if (t0 + 2 * DEC_TILE >= hi) break;
@@ -589,6 +668,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     }
 }
 
+// Dynamic LDS of a decode workgroup of wpb waves: two K stages per wave.
+template <int DK, int DV, bool FP8>
+size_t decode_lds_bytes(int wpb) {
+    using S = DecodeShape<DK, DV, FP8>;
+    return S::KLDS ? (size_t)wpb * 2 * S::KTILE : 0;
+}
+
 template <int DK, int DV>
 hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb, hipStream_t s) {
     const int units = a.Hkv * a.qgroups;
@@ -596,11 +682,13 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
     const dim3 block(64 * wpb);
     const bool mq = a.qslots > 1;
     if (kv == PKA_BF16) {
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false>), grid, block, 0, s, a);
+        const size_t lds = decode_lds_bytes<DK, DV, false>(wpb);
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true>), grid, block, lds, s, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false>), grid, block, lds, s, a);
     } else if (kv == PKA_FP8_E4M3FN) {
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false>), grid, block, 0, s, a);
+        const size_t lds = decode_lds_bytes<DK, DV, true>(wpb);
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true>), grid, block, lds, s, a);
+        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false>), grid, block, lds, s, a);
     } else {
         if (mq) hipLaunchKernelGGL((decode_f32_kernel<DK, DV, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((decode_f32_kernel<DK, DV, false>), grid, block, 0, s, a);
@@ -620,9 +708,11 @@ int blocks_per_cu_d(pka_dtype kv, int wpb) {
     int n = 0;
     hipError_t e;
     if (kv == PKA_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, false, false>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, false, false>, 64 * wpb,
+                                                         decode_lds_bytes<DK, DV, false>(wpb));
     else if (kv == PKA_FP8_E4M3FN)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, true, false>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, true, false>, 64 * wpb,
+                                                         decode_lds_bytes<DK, DV, true>(wpb));
     else
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<DK, DV, false>, 64 * wpb, 0);
     return e == hipSuccess ? n : 0;
