@@ -42,6 +42,11 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 
 __device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Uniform 32-bit load through the scalar data cache (read only).
+__device__ inline int32_t load_uniform(const int32_t* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)p)[i];
+}
+
 // Pool slot of token position `pos` of a request whose pages start at
 // kv_indices[page_base]; indices and page ids are clamped into their buffers.
 __device__ inline int32_t slot_of(const AttnArgs& a, int32_t page_base, int32_t pos) {
@@ -117,13 +122,13 @@ struct DecodeShape {
     using vrow_t = typename std::conditional<
         CPL * ESZ == 16, u32x4_t,
         typename std::conditional<CPL * ESZ == 8, u32x2_t, uint32_t>::type>::type;
-    // K rows of up to 256 bytes go through a per-wave LDS tile (see
-    // load_tile); wider rows are loaded straight into registers.
+    // K goes through one LDS tile per wave (see load_k), V into registers.
     static constexpr int KROW = DK * ESZ;       // bytes of one token's K row (one head)
     static constexpr int KCPR = KROW / 16;      // 16-byte chunks per K row
-    static constexpr bool KLDS = KROW <= 256;
     static constexpr int KDMA = KCPR / 2;       // direct-to-LDS loads per lane and tile
-    static constexpr int KTILE = DEC_TILE * KROW;  // bytes of one LDS K tile
+    static constexpr int KTILE = DEC_TILE * KROW;  // bytes of the LDS K tile
+    // LDS per wave: the K tile and one Q^T operand (1 KB per k-step)
+    static constexpr int WAVE_LDS = KTILE + KSTEPS * 1024;
     static_assert(KCPR == 4 || KCPR == 8 || KCPR == 12 || KCPR == 16 || KCPR == 24, "K row width");
     // Chunk swizzle of the LDS K tile: the K operand reads 16 rows at one
     // logical chunk, and those 16 rows must hit 16 different 16-byte bank
@@ -136,9 +141,11 @@ struct DecodeShape {
     }
 };
 
+typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
+
 // Direct HBM -> LDS load of 16 bytes per lane: lane i's bytes land at
 // lds_dst + 16 * i (lds_dst is wave-uniform).  The compiler does not track
-// it: the kernel waits for it with an explicit vmcnt(0) before the tile is
+// it: the kernel waits for it with an explicit vmcnt(0) before the data is
 // read.
 __device__ inline void lds_dma16(const void* src, const uint8_t* lds_dst) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
@@ -147,52 +154,40 @@ __device__ inline void lds_dma16(const void* src, const uint8_t* lds_dst) {
                  : "m0", "memory");
 }
 
-// One 32-token tile: V in registers, K in registers or in the wave's LDS
-// stage `kst`.  Row block sb of K holds tile tokens 16*sb + n (lane n =
-// lane & 15); V k-slot q of lane group j holds tile token 16*(q/4) + 4*j +
-// q%4, the order in which the scores come out of the first MFMA, so P^T
-// needs no shuffle.
+// V of one 32-token tile in registers: k-slot q of lane group j holds tile
+// token 16*(q/4) + 4*j + q%4, the order in which the scores come out of the
+// first MFMA, so P^T needs no shuffle.
 template <int DK, int DV, bool FP8>
-struct KVTile {
-    using S = DecodeShape<DK, DV, FP8>;
-    u32x4_t kr[2][S::KLDS ? 1 : S::NKL];
-    typename S::vrow_t vr[8];
-    uint8_t* kst;
+struct VTile {
+    typename DecodeShape<DK, DV, FP8>::vrow_t vr[8];
 };
 
-// Issue the loads of one tile.  `slot` is the pool slot of tile token
-// (lane & 31); lanes exchange slots with cross-lane moves.  The cache is
-// read once per call, so the loads carry the non-temporal hint.
+// The loads of one tile.  `slot` is the pool slot of tile token (lane & 31);
+// lanes exchange slots with cross-lane moves.  The cache is read once per
+// call, so the loads carry the non-temporal hint.
 //
-// K through LDS: a wave instruction moves 1 KB of the tile, lane i the
-// 16-byte chunk f = 64 q + i of the tile's rows laid end to end (row f / KCPR,
-// physical chunk f % KCPR, fetched from the logical chunk the swizzle puts
-// there), so every instruction reads whole 128- or 256-byte row pieces; the
-// K operand's own layout (four lanes per token) would read 64-byte pieces,
-// which HBM serves markedly slower.
+// K goes to the wave's LDS tile `kst`: a wave instruction moves 1 KB of the
+// tile, lane i the 16-byte chunk f = 64 q + i of the tile's rows laid end to
+// end (row f / KCPR, physical chunk f % KCPR, fetched from the logical chunk
+// the swizzle puts there), so every instruction reads whole 128- to
+// 256-byte row pieces; the K operand's own layout (four lanes per token)
+// would read 64-byte pieces, which HBM serves markedly slower.
 template <int DK, int DV, bool FP8>
-__device__ inline void load_tile(KVTile<DK, DV, FP8>& T, int32_t slot, const uint8_t* kbase,
-                                 const uint8_t* vbase, int64_t krow, int64_t vrow, int n, int j) {
+__device__ inline void load_k(uint8_t* kst, int32_t slot, const uint8_t* kbase, int64_t krow) {
     using S = DecodeShape<DK, DV, FP8>;
     const int lane = threadIdx.x & 63;
-    if constexpr (S::KLDS) {
-        #pragma unroll
-        for (int q = 0; q < S::KDMA; ++q) {
-            const int f = 64 * q + lane;
-            const int row = f / S::KCPR, pc = f % S::KCPR;
-            const int32_t ks = __shfl(slot, row);
-            lds_dma16(kbase + ks * krow + 16 * S::kswz(row, pc), T.kst + 1024 * q);
-        }
-    } else {
-        const int32_t slot_x = __shfl_xor(slot, 16);
-        const int32_t ks0 = (j & 1) ? slot_x : slot;
-        const int32_t ks1 = (j & 1) ? slot : slot_x;
-        #pragma unroll
-        for (int s = 0; s < S::NKL; ++s) {
-            T.kr[0][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks0 * krow + s * 64 + j * 16));
-            T.kr[1][s] = __builtin_nontemporal_load((const u32x4_t*)(kbase + ks1 * krow + s * 64 + j * 16));
-        }
+    #pragma unroll
+    for (int q = 0; q < S::KDMA; ++q) {
+        const int f = 64 * q + lane;
+        const int row = f / S::KCPR, pc = f % S::KCPR;
+        const int32_t ks = __shfl(slot, row);
+        lds_dma16(kbase + ks * krow + 16 * S::kswz(row, pc), kst + 1024 * q);
     }
+}
+template <int DK, int DV, bool FP8>
+__device__ inline void load_v(VTile<DK, DV, FP8>& T, int32_t slot, const uint8_t* vbase, int64_t vrow,
+                              int n, int j) {
+    using S = DecodeShape<DK, DV, FP8>;
     #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const int32_t vs = __shfl(slot, 16 * (q >> 2) + 4 * j + (q & 3));
@@ -201,28 +196,16 @@ __device__ inline void load_tile(KVTile<DK, DV, FP8>& T, int32_t slot, const uin
     }
 }
 
-// Scores, online-softmax update and P.V for one tile whose first `valid`
-// tokens are real for this lane's column (the rest are masked out).  With MQ
-// a column may have no real token yet (its causal limit lies beyond the
-// tile): its maximum stays -inf and it accumulates nothing.
-template <int DK, int DV, bool FP8, bool MQ>
-__device__ inline void compute_tile(const KVTile<DK, DV, FP8>& T, const bf16x8_t* qop,
-                                    f32x4_t* O, float& m2, float& lsum, int valid,
-                                    float scale_log2, int j) {
+// S^T = K . Q^T for one tile, two 16-token row blocks, K from the wave's LDS
+// tile: lane (n, j) of row block sb reads chunk 4 s + j of token 16 sb + n.
+template <int DK, int DV, bool FP8>
+__device__ inline void tile_scores(const uint8_t* kst, const bf16x8_t* qop, f32x4_t (&st)[2], int j) {
     using S = DecodeShape<DK, DV, FP8>;
     const int n = threadIdx.x & 15;
-    // 16 bytes of K for row block sb, load slot s: chunk 4 s + j of token 16 sb + n
     auto kraw = [&](int sb, int s) -> u32x4_t {
-        if constexpr (S::KLDS) {
-            const int row = 16 * sb + n;
-            typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
-            return *(lds_u32x4_t*)(T.kst + row * S::KROW + 16 * S::kswz(row, 4 * s + j));
-        } else {
-            return T.kr[sb][s];
-        }
+        const int row = 16 * sb + n;
+        return *(lds_u32x4_t*)(kst + row * S::KROW + 16 * S::kswz(row, 4 * s + j));
     };
-    // S^T = K . Q^T, two 16-token row blocks
-    f32x4_t st[2];
     #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
         st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -241,6 +224,16 @@ __device__ inline void compute_tile(const KVTile<DK, DV, FP8>& T, const bf16x8_t
             st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[ks], st[sb], 0, 0, 0);
         }
     }
+}
+
+// Online-softmax update and P.V for one tile whose first `valid` tokens are
+// real for this lane's column (the rest are masked out).  With MQ a column
+// may have no real token yet (its causal limit lies beyond the tile): its
+// maximum stays -inf and it accumulates nothing.
+template <int DK, int DV, bool FP8, bool MQ>
+__device__ inline void tile_update(const VTile<DK, DV, FP8>& T, const f32x4_t (&st)[2], f32x4_t* O,
+                                   float& m2, float& lsum, int valid, float scale_log2, int j) {
+    using S = DecodeShape<DK, DV, FP8>;
     // online softmax (log2 domain); lane (n, j) holds head n, tile tokens
     // 16*sb + 4*j + r
     float p[8];
@@ -342,138 +335,232 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * DK * S::ESZ;
     const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * DV * S::ESZ;
     const int tok = lane & 31;  // tile token whose slot this lane looks up
-    // this wave's two LDS K stages (K rows of up to 256 bytes)
+    // this wave's LDS: the K tile, then the queries of the next unit
     extern __shared__ __attribute__((aligned(1024))) uint8_t dec_lds[];
-    uint8_t* const kst0 = dec_lds + (threadIdx.x >> 6) * 2 * S::KTILE;
-    // K through LDS: the loads of a tile are waited for (vmcnt(0)) before the
-    // next tile's loads are issued and the tile is computed; the compiler
-    // fence keeps the LDS reads after the wait and the next direct loads
-    // after the reads of the stage they overwrite
-    auto landed = [&]() {
-        if constexpr (S::KLDS) {
-            __builtin_amdgcn_s_waitcnt(0x0f70);
-            asm volatile("" ::: "memory");
+    uint8_t* const kst = dec_lds + (threadIdx.x >> 6) * S::WAVE_LDS;
+    uint8_t* const qbuf = kst + S::KTILE;
+
+    // The wave's work is one stream of 32-position tiles.  A unit is one
+    // 16-column pass over one piece (the part of a request inside this
+    // workgroup's token share); units follow each other in request order, and
+    // the loads of a unit's first tile and its queries go out while the
+    // previous unit's last tile is computed, so a request boundary costs no
+    // extra round trip to memory.
+    // Iterator state is kept small (wave-uniform scalars): the piece's
+    // request, token range, pass and page offset, and the tile start; the
+    // request's query rows are read again where they are needed.
+    struct It {
+        int32_t seg;  // request; a.B: past the end of the share
+        int32_t lo, hi, c0, pb, t0;
+    };
+    // query rows of request sg: one (its last row) without MQ
+    struct Rows {
+        int32_t L, q0, nq, pfx;
+    };
+    auto rows_of = [&](int32_t sg) {
+        Rows r;
+        r.L = load_uniform(F, sg + 1) - load_uniform(F, sg);
+        if constexpr (MQ) {
+            r.q0 = load_uniform(a.qo_indptr, sg);
+            const int32_t nb = load_uniform(a.qo_indptr, sg + 1) - r.q0;
+            r.nq = min(nb, a.qslots);
+            r.pfx = r.L - nb;
+        } else {
+            r.q0 = min(max(load_uniform(a.qo_indptr, sg + 1) - 1, 0), a.N - 1);
+            r.nq = 1;
+            r.pfx = r.L - 1;
+        }
+        return r;
+    };
+    // first non-empty piece from request sg on (seg = a.B: the share is done)
+    auto open_piece = [&](int32_t sg, It& it) {
+        for (; sg < a.B; ++sg) {
+            const int32_t f0 = load_uniform(F, sg), f1 = load_uniform(F, sg + 1);
+            if (f0 >= end) break;
+            const int32_t lo = (int32_t)(max(start, (int64_t)f0) - f0);
+            const int32_t hi = (int32_t)(min(end, (int64_t)f1) - f0);
+            if (hi <= lo) continue;
+            if constexpr (MQ) {
+                const int32_t nb = load_uniform(a.qo_indptr, sg + 1) - load_uniform(a.qo_indptr, sg);
+                if (nb > a.qslots && lo == 0 && lane == 0 && unit == 0)
+                    atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_LENGTH);
+                if (min(nb, a.qslots) <= 0) continue;  // no query rows
+            }
+            it.seg = sg;
+            it.lo = lo;
+            it.hi = hi;
+            it.c0 = 0;
+            it.pb = load_uniform(a.kv_indptr, sg);
+            it.t0 = lo;
+            return;
+        }
+        it.seg = a.B;
+    };
+    // the tile after `cur`: the next 32 positions, else the next pass, else
+    // the next piece
+    auto advance = [&](const It& cur, It& nx) {
+        nx = cur;
+        if (cur.seg >= a.B) return;
+        nx.t0 = cur.t0 + DEC_TILE;
+        if (nx.t0 < cur.hi) return;
+        if (MQ && cur.c0 + 16 < rows_of(cur.seg).nq * nh) {
+            nx.c0 = cur.c0 + 16;
+            nx.t0 = cur.lo;
+        } else {
+            open_piece(cur.seg + 1, nx);
+        }
+    };
+    // pool slot of tile token `tok`; positions past the piece repeat its last
+    // token (loaded, never counted)
+    auto slot_for = [&](const It& it) {
+        const int32_t pos = it.t0 + tok;
+        return slot_of(a, it.pb, pos < it.hi ? pos : it.hi - 1);
+    };
+    // this lane's column of a unit: query token qi, head h
+    struct Col {
+        bool ok;
+        int32_t qi, h, qr, kend;  // keys of the column within the piece: positions < kend
+    };
+    auto column = [&](const It& u, const Rows& r) {
+        Col c;
+        const int32_t cc = u.c0 + n;
+        c.ok = MQ ? cc < r.nq * nh : n < nh;
+        c.qi = MQ ? (c.ok ? cc / nh : 0) : 0;
+        c.h = h0 + (MQ ? cc % nh : n);
+        c.qr = r.q0 + c.qi;
+        c.kend = MQ ? min(u.hi, r.pfx + c.qi + 1) : u.hi;
+        return c;
+    };
+    // Q^T operand: lane (n, j) holds its column at the dims its K lanes load.
+    // A unit's queries go to the wave's LDS buffer by direct loads (lane l's
+    // 16 bytes of k-step ks at 1024 ks + 16 l) when its first tile is issued,
+    // and into registers once that tile has landed; lanes without a column
+    // load nothing and take zeros.
+    auto fetch_q = [&](const It& u) {
+        const Col c = column(u, rows_of(u.seg));
+        if (c.ok) {
+            const __bf16* qrow = (const __bf16*)a.q + ((int64_t)c.qr * a.Hq + c.h) * DK;
+            #pragma unroll
+            for (int ks = 0; ks < S::KSTEPS; ++ks) {
+                const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
+                lds_dma16(qrow + d0, qbuf + 1024 * ks);
+            }
+        }
+    };
+    // the piece holding a request's last position writes its new token first
+    auto new_token = [&](const It& u) {
+        if constexpr (!MQ) {
+            if (a.k_new) {
+                const Rows r = rows_of(u.seg);
+                if (u.hi == r.L) write_new_token<DK, DV, FP8>(a, r.q0, g, lane);
+            }
         }
     };
 
-    for (; seg < a.B; ++seg) {
-        const int32_t f0 = F[seg], f1 = F[seg + 1];
-        if (f0 >= end) break;
-        const int32_t lo = (int32_t)(max(start, (int64_t)f0) - f0);
-        const int32_t hi = (int32_t)(min(end, (int64_t)f1) - f0);
-        const int32_t L = f1 - f0;
-        const int32_t b = seg;
-        const int32_t page_base = a.kv_indptr[b];
-        // query rows of the request: one (its last row) without MQ
-        int32_t q0, nq, pfx;
-        if constexpr (MQ) {
-            q0 = a.qo_indptr[b];
-            const int32_t nb = a.qo_indptr[b + 1] - q0;
-            nq = min(nb, a.qslots);
-            if (nb > a.qslots && lo == 0 && lane == 0 && unit == 0)
-                atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_LENGTH);
-            pfx = L - nb;
-        } else {
-            q0 = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
-            nq = 1;
-            pfx = L - 1;
-            // the piece holding the request's last position writes the new token
-            if (a.k_new && hi == L) write_new_token<DK, DV, FP8>(a, q0, g, lane);
+    It cur, nx, nn;
+    open_piece(seg, cur);
+    if (cur.seg >= a.B) return;
+    new_token(cur);
+    VTile<DK, DV, FP8> A, Bt;
+    {
+        const int32_t s0 = slot_for(cur);
+        load_k<DK, DV, FP8>(kst, s0, kbase, krow);
+        load_v(A, s0, vbase, vrow, n, j);
+    }
+    fetch_q(cur);
+    advance(cur, nx);
+    int32_t s_nx = nx.seg < a.B ? slot_for(nx) : 0;
+    Rows crow = rows_of(cur.seg);  // query rows of cur's request
+    Col col = column(cur, crow);
+    bf16x8_t qop[S::KSTEPS];
+    auto take_q = [&]() {
+        #pragma unroll
+        for (int ks = 0; ks < S::KSTEPS; ++ks) {
+            const u32x4_t v = *(lds_u32x4_t*)(qbuf + 1024 * ks + 16 * lane);
+            qop[ks] = as_bf16x8(col.ok ? v : u32x4_t{0u, 0u, 0u, 0u});
         }
-        // slot of tile token `tok` of the tile starting at position t0; positions
-        // past the piece repeat its last token (cached, never counted)
-        auto slot_at = [&](int32_t t0) {
-            const int32_t pos = t0 + tok;
-            return slot_of(a, page_base, pos < hi ? pos : hi - 1);
-        };
+        // the reads are done before a later direct load refills the buffer
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+    };
+    f32x4_t O[S::CPL];
+    #pragma unroll
+    for (int cc = 0; cc < S::CPL; ++cc) O[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m2 = -INFINITY, lsum = 0.f;
 
-        const int32_t cols = nq * nh;
-        for (int32_t c0 = 0; c0 < cols; c0 += 16) {
-            // this lane's column: query token qi, head h
-            const int32_t c = c0 + n;
-            const bool col_ok = c < cols;
-            const int32_t qi = MQ ? (col_ok ? c / nh : 0) : 0;
-            const int32_t h = h0 + (MQ ? c % nh : n);
-            const int32_t qr = q0 + qi;
-            // keys of this column within the piece: positions < kend_c
-            const int32_t kend_c = MQ ? min(hi, pfx + qi + 1) : hi;
-
-            KVTile<DK, DV, FP8> A, Bt;
-            A.kst = kst0;
-            Bt.kst = kst0 + S::KTILE;
-            int32_t slot_a = slot_at(lo);
-            int32_t slot_b = slot_at(lo + DEC_TILE);
-            landed();  // loads of the previous piece into these stages are done
-            load_tile(A, slot_a, kbase, vbase, krow, vrow, n, j);
-
-            // Q^T operand: lane (n, j) holds its column at the dims its K lanes load.
-            bf16x8_t qop[S::KSTEPS];
-            {
-                const __bf16* qrow = (const __bf16*)a.q + ((int64_t)qr * a.Hq + h) * DK;
+    // finish a unit: denominator over the four lane groups of each column; a
+    // column with no key in this piece leaves weight 0 (lse -inf, o 0)
+    auto finish = [&](const It& u) {
+        const float ltot = wave_sum_xor_16_32(lsum);
+        const float inv = MQ && !(ltot > 0.f) ? 0.f : 1.0f / ltot;
+        const float lse_nat = MQ && !(ltot > 0.f) ? -INFINITY : (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
+        if (!col.ok) return;
+        if (u.lo == 0 && u.hi == crow.L) {
+            __bf16* orow = (__bf16*)a.out + ((int64_t)col.qr * a.Hq + col.h) * DV;
+            emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
                 #pragma unroll
-                for (int ks = 0; ks < S::KSTEPS; ++ks) {
-                    const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
-                    u32x4_t v = {0u, 0u, 0u, 0u};
-                    if (MQ ? col_ok : n < nh) v = *(const u32x4_t*)(qrow + d0);
-                    qop[ks] = as_bf16x8(v);
+                for (int i = 0; i < 4 * S::CPL; i += 8) {
+                    const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
+                                        pack_bf16(v[i + 4], v[i + 5]), pack_bf16(v[i + 6], v[i + 7])};
+                    *(u32x4_t*)(orow + d0 + i) = pk;
                 }
-            }
+            });
+            if (a.lse && j == 0) a.lse[(int64_t)col.qr * a.Hq + col.h] = lse_nat;
+        } else {
+            // partial slot of (request, workgroup, query token)
+            const int64_t ps = ((int64_t)u.seg + w) * a.qslots + col.qi;
+            float* prow = a.ws_o + (ps * a.Hq + col.h) * DV;
+            emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+                #pragma unroll
+                for (int i = 0; i < 4 * S::CPL; i += 4)
+                    *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
+            });
+            if (j == 0) a.ws_lse[ps * a.Hq + col.h] = lse_nat;
+        }
+    };
 
-            f32x4_t O[S::CPL];
+    // One step: wait for tile `cur` (K in LDS, V in X); its scores; then,
+    // once the scores' LDS reads are done, the loads of tile `nx` (K into
+    // the same LDS tile, V into Y) and the slot lookups of the tile after
+    // it; then cur's softmax and P.V.  Every tile's loads are waited for
+    // before the next tile's go out, so one tile is in flight while
+    // another is computed.
+    auto step = [&](VTile<DK, DV, FP8>& X, VTile<DK, DV, FP8>& Y) -> bool {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile cur, its queries and nx's slots landed
+        asm volatile("" ::: "memory");       // LDS reads stay after the wait
+        if (cur.t0 == cur.lo) take_q();      // cur opens its unit
+        f32x4_t st[2];
+        tile_scores<DK, DV, FP8>(kst, qop, st, j);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the K reads are done ...
+        asm volatile("" ::: "memory");       // ... before the direct loads refill the tile
+        if (nx.seg < a.B) {
+            const bool opens = nx.t0 == nx.lo;  // nx is the first tile of its unit
+            if (opens) new_token(nx);
+            load_k<DK, DV, FP8>(kst, s_nx, kbase, krow);
+            load_v(Y, s_nx, vbase, vrow, n, j);
+            if (opens) fetch_q(nx);
+        }
+        advance(nx, nn);
+        const int32_t s_nn = nn.seg < a.B ? slot_for(nn) : 0;
+        tile_update<DK, DV, FP8, MQ>(X, st, O, m2, lsum, col.kend - cur.t0, a.scale_log2, j);
+        if (cur.t0 + DEC_TILE >= cur.hi) {  // last tile of its unit
+            finish(cur);
+            if (nx.seg >= a.B) return false;
+            if (nx.seg != cur.seg) crow = rows_of(nx.seg);
+            col = column(nx, crow);
             #pragma unroll
             for (int cc = 0; cc < S::CPL; ++cc) O[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            float m2 = -INFINITY, lsum = 0.f;
-
-            // While one tile is consumed the next one's loads are
-            // outstanding.  With K in registers the loads are issued
-            // unconditionally (past the end they re-read the piece's last
-            // row) so the compiler's wait counts are the same on every
-            // iteration; with K through LDS every tile is waited for
-            // explicitly and no load goes past the piece.
-            for (int32_t t0 = lo;; t0 += 2 * DEC_TILE) {
-                landed();
-                if (!S::KLDS || t0 + DEC_TILE < hi) load_tile(Bt, slot_b, kbase, vbase, krow, vrow, n, j);
-                slot_a = slot_at(t0 + 2 * DEC_TILE);
-                compute_tile<DK, DV, FP8, MQ>(A, qop, O, m2, lsum, kend_c - t0, a.scale_log2, j);
-                if (t0 + DEC_TILE >= hi) break;
-                landed();
-                if (!S::KLDS || t0 + 2 * DEC_TILE < hi) load_tile(A, slot_a, kbase, vbase, krow, vrow, n, j);
-                slot_b = slot_at(t0 + 3 * DEC_TILE);
-                compute_tile<DK, DV, FP8, MQ>(Bt, qop, O, m2, lsum, kend_c - t0 - DEC_TILE, a.scale_log2, j);
-                if (t0 + 2 * DEC_TILE >= hi) break;
-            }
-
-            // finish: denominator over the four lane groups of each column; a
-            // column with no key in this piece leaves weight 0 (lse -inf, o 0)
-            const float ltot = wave_sum_xor_16_32(lsum);
-            const float inv = MQ && !(ltot > 0.f) ? 0.f : 1.0f / ltot;
-            const float lse_nat = MQ && !(ltot > 0.f) ? -INFINITY : (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
-            if (MQ ? col_ok : n < nh) {
-                if (lo == 0 && hi == L) {
-                    __bf16* orow = (__bf16*)a.out + ((int64_t)qr * a.Hq + h) * DV;
-                    emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
-                        #pragma unroll
-                        for (int i = 0; i < 4 * S::CPL; i += 8) {
-                            const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
-                                                pack_bf16(v[i + 4], v[i + 5]),
-                                                pack_bf16(v[i + 6], v[i + 7])};
-                            *(u32x4_t*)(orow + d0 + i) = pk;
-                        }
-                    });
-                    if (a.lse && j == 0) a.lse[(int64_t)qr * a.Hq + h] = lse_nat;
-                } else {
-                    // partial slot of (request, workgroup, query token)
-                    const int64_t ps = ((int64_t)b + w) * a.qslots + qi;
-                    float* prow = a.ws_o + (ps * a.Hq + h) * DV;
-                    emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
-                        #pragma unroll
-                        for (int i = 0; i < 4 * S::CPL; i += 4)
-                            *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
-                    });
-                    if (j == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
-                }
-            }
+            m2 = -INFINITY;
+            lsum = 0.f;
         }
+        cur = nx;
+        nx = nn;
+        s_nx = s_nn;
+        return true;
+    };
+    for (;;) {
+        if (!step(A, Bt)) break;
+        if (!step(Bt, A)) break;
     }
 }
 
@@ -668,11 +755,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     }
 }
 
-// Dynamic LDS of a decode workgroup of wpb waves: two K stages per wave.
+// Dynamic LDS of a decode workgroup of wpb waves.
 template <int DK, int DV, bool FP8>
 size_t decode_lds_bytes(int wpb) {
-    using S = DecodeShape<DK, DV, FP8>;
-    return S::KLDS ? (size_t)wpb * 2 * S::KTILE : 0;
+    return (size_t)wpb * DecodeShape<DK, DV, FP8>::WAVE_LDS;
 }
 
 template <int DK, int DV>
