@@ -713,30 +713,54 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
         const float* o_col = a.ws_o + (((b + w0) * a.qslots + qi) * a.Hq + h) * D;
 
         float M = -INFINITY;
-        for (int32_t k = lane; k < np; k += 64) M = fmaxf(M, lse_col[(int64_t)k * lstride]);
-        #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
         float den = 0.f, acc[EPL];
         #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-        for (int32_t k0 = 0; k0 < np; k0 += 64) {
-            const int32_t k = k0 + lane;
-            const float wk = k < np ? expf(lse_col[(int64_t)k * lstride] - M) : 0.f;
-            den += wk;
-            const int32_t cnt = min(64, np - k0);
-            for (int32_t i = 0; i < cnt; i += UNROLL) {
-                float v[UNROLL][EPL], wt[UNROLL];
+        if (np <= UNROLL) {
+            // few partials: their outputs are loaded together with the
+            // log-sum-exps (one round trip), then weighted
+            const float lv = lane < np ? lse_col[(int64_t)lane * lstride] : -INFINITY;
+            float v[UNROLL][EPL];
+            #pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int32_t kk = min(u, np - 1);
                 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u) {
-                    const int32_t kk = min(i + u, cnt - 1);
-                    wt[u] = i + u < cnt ? __shfl(wk, kk) : 0.f;
+                for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)kk * ostride + e * 64 + lane];
+            }
+            M = lv;
+            #pragma unroll
+            for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+            const float wk = lane < np ? expf(lv - M) : 0.f;
+            den = wk;
+            #pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const float wt = u < np ? __shfl(wk, u) : 0.f;
+                #pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[e] += wt * v[u][e];
+            }
+        } else {
+            for (int32_t k = lane; k < np; k += 64) M = fmaxf(M, lse_col[(int64_t)k * lstride]);
+            #pragma unroll
+            for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+            for (int32_t k0 = 0; k0 < np; k0 += 64) {
+                const int32_t k = k0 + lane;
+                const float wk = k < np ? expf(lse_col[(int64_t)k * lstride] - M) : 0.f;
+                den += wk;
+                const int32_t cnt = min(64, np - k0);
+                for (int32_t i = 0; i < cnt; i += UNROLL) {
+                    float v[UNROLL][EPL], wt[UNROLL];
                     #pragma unroll
-                    for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)(k0 + kk) * ostride + e * 64 + lane];
+                    for (int u = 0; u < UNROLL; ++u) {
+                        const int32_t kk = min(i + u, cnt - 1);
+                        wt[u] = i + u < cnt ? __shfl(wk, kk) : 0.f;
+                        #pragma unroll
+                        for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)(k0 + kk) * ostride + e * 64 + lane];
+                    }
+                    #pragma unroll
+                    for (int u = 0; u < UNROLL; ++u)
+                        #pragma unroll
+                        for (int e = 0; e < EPL; ++e) acc[e] += wt[u] * v[u][e];
                 }
-                #pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
-                    #pragma unroll
-                    for (int e = 0; e < EPL; ++e) acc[e] += wt[u] * v[u][e];
             }
         }
         #pragma unroll
