@@ -201,22 +201,25 @@ def cpu_baseline(layout, values, budget_s: float = 20.0):
             "cpu": cpu_model()}
 
 
-def bench_decode_kernel(spec, iters: int):
-    """Kernel-level decode figure for one workload (attn_decode alone)."""
+def bench_decode_kernel(spec, iters: int, warm: int = 10):
+    """Kernel-level decode figure for one workload (attn_decode alone), on two
+    copies of pools and metadata used alternately (as for the headline batch)."""
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
     layout = workloads.make_layout(spec)
-    prob = GpuProblem(layout)
-    prob.attention_step(save=True)
+    values = workloads.make_values(layout, device="cuda")
+    probs = [GpuProblem(layout, values), GpuProblem(layout, values)]
+    for p in probs:
+        p.attention_step(save=True)
     torch.cuda.synchronize()
-    ms = time_events(lambda i: prob.attention_step(save=False, lse=False), iters)
+    ms = time_events(lambda i: probs[i % 2].attention_step(save=False, lse=False), iters, warm=warm)
     nbytes = decode_algorithmic_bytes(layout)
     out = {"workload": layout.spec.name, "kv_tokens": layout.total_tokens,
            "ms": round(ms, 4), "kv_read_GBps": round(kv_bytes(layout) / ms / 1e6, 1),
            "algorithmic_GBps": round(nbytes / ms / 1e6, 1),
            "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    del prob
+    del probs
     torch.cuda.empty_cache()
     return out
 
