@@ -234,7 +234,7 @@ def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16", spe
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
-    spec = workloads.CONFIGS[4] if spec is None else spec
+    spec = workloads.WORKLOADS["llama3_8b_extend"] if spec is None else spec
     if kv_dtype != spec.kv_dtype:
         spec = spec.replace(name=spec.name.replace("extend_bf16", f"extend_{kv_dtype}kv"), kv_dtype=kv_dtype)
     layout = workloads.make_layout(spec)
@@ -304,7 +304,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extend / other decode figures and the clock and power sampling")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["extend", "extend_fp8", "decode3", "decode5", "copy", "gemm",
+    ap.add_argument("--only", choices=["extend", "extend_fp8", "qwen3_235b_decode", "long_fp8_decode", "copy", "gemm",
                                        "asym_extend", "asym_decode"], default=None,
                     help="run one extra leg alone (for profiling) and print its figures")
     args = ap.parse_args()
@@ -335,11 +335,11 @@ def main():
         elif args.only == "asym_decode":
             res = bench_decode_kernel(workloads.EXTRA["asym_decode"], args.steps)
         else:
-            res = bench_decode_kernel(workloads.CONFIGS[int(args.only[-1])], args.steps)
+            res = bench_decode_kernel(workloads.WORKLOADS[args.only], args.steps)
         print(json.dumps(res), flush=True)
         return
 
-    spec = workloads.CONFIGS[2]
+    spec = workloads.WORKLOADS["llama3_8b_decode"]
     layout = workloads.make_layout(spec)
     log(f"workload {spec.name}: B={layout.batch} tokens={layout.total_tokens} pages={layout.kv_pages}")
     values = workloads.make_values(layout, device="cuda")
@@ -409,10 +409,10 @@ def main():
         result["extend_fp8kv"] = bench_extend(args.steps, gpu_state=False, kv_dtype="fp8")
         log(f"extend over an fp8 cache: {result['extend_fp8kv']}")
         log(f"bf16 GEMM reference: {result['mfma_reference']}")
-        result["decode_configs"] = {}
-        for cid in (3, 5):
-            result["decode_configs"][str(cid)] = bench_decode_kernel(workloads.CONFIGS[cid], args.steps)
-            log(f"decode config {cid}: {result['decode_configs'][str(cid)]}")
+        result["decode_workloads"] = {}
+        for wl in ("qwen3_235b_decode", "long_fp8_decode"):
+            result["decode_workloads"][wl] = bench_decode_kernel(workloads.WORKLOADS[wl], args.steps)
+            log(f"decode {wl}: {result['decode_workloads'][wl]}")
         # key / value heads of different widths (192 / 128)
         result["asym_extend"] = bench_extend(args.steps, gpu_state=False,
                                              spec=workloads.EXTRA["asym_extend"])

@@ -29,14 +29,14 @@ def _need_gpu(request):
 
 
 CASES = {
-    "decode_bf16_p16": workloads.CONFIGS[2].replace(batch=11, seq_len_args=(1, 900)),
-    "decode_bf16_p1_g16": workloads.CONFIGS[3].replace(batch=5, seq_len_kind="uniform",
+    "decode_bf16_p16": workloads.WORKLOADS["llama3_8b_decode"].replace(batch=11, seq_len_args=(1, 900)),
+    "decode_bf16_p1_g16": workloads.WORKLOADS["qwen3_235b_decode"].replace(batch=5, seq_len_kind="uniform",
                                                        seq_len_args=(1, 700)),
-    "decode_fp8_p64": workloads.CONFIGS[5].replace(batch=7, seq_len_args=(1, 1500)),
+    "decode_fp8_p64": workloads.WORKLOADS["long_fp8_decode"].replace(batch=7, seq_len_args=(1, 1500)),
     "decode_fp8_d64_g32": workloads.Spec("fp8_d64_g32", "decode", 4, 64, 2, 64, 32, "bf16", "fp8",
                                          seed=61, seq_len_kind="uniform", seq_len_args=(1, 600)),
-    "decode_f32": workloads.CONFIGS[1],
-    "extend_bf16": workloads.CONFIGS[4].replace(batch=3, new_len_args=(1, 200),
+    "decode_f32": workloads.WORKLOADS["tiny_decode"],
+    "extend_bf16": workloads.WORKLOADS["llama3_8b_extend"].replace(batch=3, new_len_args=(1, 200),
                                                 prefix_len_args=(0, 300)),
 }
 
@@ -76,11 +76,11 @@ def test_without_the_write_the_sentinel_is_read():
     assert torch.isnan(prob.out.float()).any(dim=-1).all()
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
+@pytest.mark.parametrize("cfg", ["llama3_8b_decode", "long_fp8_decode"])
 def test_full_size_new_token_rows(cfg):
     """Full-size decode batches: every new token's slot holds exactly the
     oracle's encoding of that token (bf16 copy or fp8 quantisation)."""
-    spec = workloads.CONFIGS[cfg]
+    spec = workloads.WORKLOADS[cfg]
     layout = workloads.make_layout(spec)
     values = workloads.make_values(layout, device="cuda")
     prob = GpuProblem(layout, values, prefix_only=True)

@@ -153,7 +153,7 @@ def test_page_placement_is_bit_identical(mode):
 
 
 def test_runs_are_deterministic():
-    spec = workloads.CONFIGS[2].replace(batch=12, seq_len_args=(1, 3000))
+    spec = workloads.WORKLOADS["llama3_8b_decode"].replace(batch=12, seq_len_args=(1, 3000))
     layout = workloads.make_layout(spec)
     prob = GpuProblem(layout)
     outs = []

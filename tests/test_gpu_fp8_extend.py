@@ -67,6 +67,6 @@ def test_fp8_extend_ragged():
 def test_fp8_extend_prefill_batch_sampled():
     """The 8-request prefill batch (new U[512, 2048] on prefixes U[0, 4096],
     page 128) with an fp8 cache, on sampled requests, heads and tokens."""
-    spec = workloads.CONFIGS[4].replace(name="extend_fp8kv_b8_g4_d128_p128", kv_dtype="fp8")
-    _sampled(4, lambda L: [int(np.argmax(L)), int(np.argmin(L)), 5], heads=[0, 7, 18, 31],
+    spec = workloads.WORKLOADS["llama3_8b_extend"].replace(name="extend_fp8kv_b8_g4_d128_p128", kv_dtype="fp8")
+    _sampled("llama3_8b_extend", lambda L: [int(np.argmax(L)), int(np.argmin(L)), 5], heads=[0, 7, 18, 31],
              tokens=lambda n: sorted(set(list(range(0, n, 41)) + [n - 1])), spec=spec)

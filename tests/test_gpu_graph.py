@@ -43,9 +43,9 @@ def _capture(prob):
 
 
 @pytest.mark.parametrize("name,spec", [
-    ("decode_bf16_p16", workloads.CONFIGS[2].replace(batch=9, seq_len_args=(40, 900), seed=71)),
-    ("decode_fp8_p64", workloads.CONFIGS[5].replace(batch=5, seq_len_args=(100, 3000), seed=72)),
-    ("extend_bf16_p128", workloads.CONFIGS[4].replace(batch=3, new_len_args=(1, 150),
+    ("decode_bf16_p16", workloads.WORKLOADS["llama3_8b_decode"].replace(batch=9, seq_len_args=(40, 900), seed=71)),
+    ("decode_fp8_p64", workloads.WORKLOADS["long_fp8_decode"].replace(batch=5, seq_len_args=(100, 3000), seed=72)),
+    ("extend_bf16_p128", workloads.WORKLOADS["llama3_8b_extend"].replace(batch=3, new_len_args=(1, 150),
                                                       prefix_len_args=(0, 300), seed=73)),
 ])
 def test_graph_replays_match_eager(name, spec):
@@ -80,7 +80,7 @@ def test_graph_replays_match_eager(name, spec):
 
 def test_graph_replay_matches_oracle():
     """The replayed step is also right: one replay checked against the oracle."""
-    spec = workloads.CONFIGS[2].replace(batch=6, seq_len_args=(10, 700), seed=74)
+    spec = workloads.WORKLOADS["llama3_8b_decode"].replace(batch=6, seq_len_args=(10, 700), seed=74)
     layout = workloads.make_layout(spec)
     values = workloads.make_values(layout, device="cuda")
     prob = GpuProblem(layout, values)

@@ -26,18 +26,18 @@ def _need_gpu(request):
     print(f"\n[case] {request.node.name}", flush=True)
 
 
-def _small(cfg_id, **kw):
-    return workloads.CONFIGS[cfg_id].replace(**kw)
+def _small(name, **kw):
+    return workloads.WORKLOADS[name].replace(**kw)
 
 
 # Reduced shapes of the five workloads (same heads, dims, page sizes and
 # dtypes; fewer/shorter requests) for element-by-element parity.
 SMALL = {
-    "tiny": (workloads.CONFIGS[1], None),
-    "llama_b9": (_small(2, batch=9, seq_len_args=(1, 700)), None),
-    "qwen_b5_p1": (_small(3, batch=5, seq_len_kind="uniform", seq_len_args=(1, 900)), None),
-    "fp8_b6_p64": (_small(5, batch=6, seq_len_args=(1, 1500)), None),
-    "extend_b3": (_small(4, batch=3, new_len_args=(1, 300), prefix_len_args=(0, 500)), None),
+    "tiny": (workloads.WORKLOADS["tiny_decode"], None),
+    "llama_b9": (_small("llama3_8b_decode", batch=9, seq_len_args=(1, 700)), None),
+    "qwen_b5_p1": (_small("qwen3_235b_decode", batch=5, seq_len_kind="uniform", seq_len_args=(1, 900)), None),
+    "fp8_b6_p64": (_small("long_fp8_decode", batch=6, seq_len_args=(1, 1500)), None),
+    "extend_b3": (_small("llama3_8b_extend", batch=3, new_len_args=(1, 300), prefix_len_args=(0, 500)), None),
 }
 
 
@@ -52,9 +52,9 @@ def _check_close(name, gpu, ref, kv_dtype):
 
 # ------------------------------------------------------------- metadata
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", list(workloads.WORKLOADS))
 def test_metadata_bit_exact(cfg):
-    layout = workloads.make_layout(workloads.CONFIGS[cfg])
+    layout = workloads.make_layout(workloads.WORKLOADS[cfg])
     spec = layout.spec
     ctx = pka.Context(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                       layout.num_pages, spec.q_dtype, spec.kv_dtype, spec.softmax_scale,
@@ -149,7 +149,7 @@ def test_attention_parity_small(name):
 
 
 def test_attention_parity_llama_decode_full():
-    spec = workloads.CONFIGS[2]
+    spec = workloads.WORKLOADS["llama3_8b_decode"]
     layout = workloads.make_layout(spec)
     values = workloads.make_values(layout, device="cuda")
     prob = GpuProblem(layout, values)
@@ -162,7 +162,7 @@ def test_attention_parity_llama_decode_full():
 
 
 def _sampled(cfg, requests, heads=None, tokens=None, spec=None):
-    spec = workloads.CONFIGS[cfg] if spec is None else spec
+    spec = workloads.WORKLOADS[cfg] if spec is None else spec
     layout = workloads.make_layout(spec)
     values = workloads.make_values(layout, device="cuda")
     prob = GpuProblem(layout, values)
@@ -187,13 +187,13 @@ def _sampled(cfg, requests, heads=None, tokens=None, spec=None):
 
 
 def test_attention_parity_qwen_decode_sampled():
-    _sampled(3, lambda L: [int(np.argmax(L)), int(np.argmin(L)), 0, len(L) - 1, len(L) // 2])
+    _sampled("qwen3_235b_decode", lambda L: [int(np.argmax(L)), int(np.argmin(L)), 0, len(L) - 1, len(L) // 2])
 
 
 def test_attention_parity_fp8_long_decode_sampled():
-    _sampled(5, lambda L: [int(np.argmax(L)), int(np.argmin(L)), 7])
+    _sampled("long_fp8_decode", lambda L: [int(np.argmax(L)), int(np.argmin(L)), 7])
 
 
 def test_attention_parity_extend_sampled():
-    _sampled(4, lambda L: [int(np.argmax(L)), int(np.argmin(L)), 3], heads=[0, 5, 13, 31],
+    _sampled("llama3_8b_extend", lambda L: [int(np.argmax(L)), int(np.argmin(L)), 3], heads=[0, 5, 13, 31],
              tokens=lambda n: sorted(set(list(range(0, n, 37)) + [n - 1])))

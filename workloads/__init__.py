@@ -76,17 +76,17 @@ class Spec:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads the attention path is judged on.
-CONFIGS = {
-    1: Spec("tiny_decode_f32_b2_g2_d64_p1", "decode", 2, 4, 2, 64, 1, "f32", "f32", seed=1,
+# The seeded workloads the path is checked and measured on, named by shape.
+WORKLOADS = {
+    "tiny_decode": Spec("tiny_decode_f32_b2_g2_d64_p1", "decode", 2, 4, 2, 64, 1, "f32", "f32", seed=1,
             seq_len_kind="fixed", seq_len_args=(37, 100), pool_pages=256, scale=1.0 / 8.0),
-    2: Spec("llama3_8b_decode_bf16_b64_g4_d128_p16", "decode", 64, 32, 8, 128, 16, "bf16", "bf16",
+    "llama3_8b_decode": Spec("llama3_8b_decode_bf16_b64_g4_d128_p16", "decode", 64, 32, 8, 128, 16, "bf16", "bf16",
             seed=2, seq_len_kind="uniform", seq_len_args=(512, 4096)),
-    3: Spec("qwen3_235b_decode_bf16_b128_g16_d128_p1", "decode", 128, 64, 4, 128, 1, "bf16", "bf16",
+    "qwen3_235b_decode": Spec("qwen3_235b_decode_bf16_b128_g16_d128_p1", "decode", 128, 64, 4, 128, 1, "bf16", "bf16",
             seed=3, seq_len_kind="loguniform", seq_len_args=(2048, 32768)),
-    4: Spec("extend_bf16_b8_g4_d128_p128", "extend", 8, 32, 8, 128, 128, "bf16", "bf16", seed=4,
+    "llama3_8b_extend": Spec("extend_bf16_b8_g4_d128_p128", "extend", 8, 32, 8, 128, 128, "bf16", "bf16", seed=4,
             new_len_args=(512, 2048), prefix_len_args=(0, 4096)),
-    5: Spec("long_decode_fp8kv_b16_g8_d128_p64", "decode", 16, 64, 8, 128, 64, "bf16", "fp8", seed=5,
+    "long_fp8_decode": Spec("long_decode_fp8kv_b16_g8_d128_p64", "decode", 16, 64, 8, 128, 64, "bf16", "fp8", seed=5,
             seq_len_kind="uniform", seq_len_args=(32768, 131072)),
 }
 
