@@ -51,7 +51,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t elem_bytes(pka_dtype t) { return t == PKA_F32 ? 4 : t == PKA_BF16 ? 2 : 1; }
 
 // Decode workgroups: exactly one resident round (every workgroup on the
-// device at once, so the equal token shares finish together), from the
+// device at once, so the equal tile shares finish together), from the
 // device's CU count and the kernel's occupancy.  Queried once per context.
 pka_status decode_wgs(const pka_ctx* ctx, int32_t* out) {
     int32_t v = ctx->nwg.load(std::memory_order_relaxed);

@@ -3,22 +3,25 @@
 // Decode reads one query against a long cache and is memory-bound
 // ("sglang-101 s4.2 --attention-backend", section "Two backends in one
 // server"; "[SGLang] Hybrid Attention", introduction).  The kernel is split-K
-// flash decoding: the batch's tokens, laid end to end, are cut into one equal
-// share per workgroup; each wave of a workgroup serves one KV head (16 query
-// heads of its group at most) over that share with an online softmax, and a
-// share that covers only part of a request leaves an fp32 partial (output and
-// log-sum-exp) that a merge kernel combines.
+// flash decoding: the batch's 32-token tiles, laid end to end, are cut into
+// one share per workgroup (equal to within a tile); each wave of a workgroup
+// serves one KV head (16 query heads of its group at most) over that share
+// with an online softmax, and a share that covers only part of a request
+// leaves an fp32 partial (output and log-sum-exp) that a merge kernel
+// combines.
 //
 // gfx950 mapping of the MFMA variant (bf16 or fp8 e4m3fn cache):
 //   S^T[token, head]  = K[token, :] . Q^T        v_mfma_f32_16x16x32_bf16
 //   O^T[d, head]     += V^T[d, token] . P^T      v_mfma_f32_16x16x32_bf16
-// K rows are loaded straight into the A operand (16 bytes per lane, every
-// lane group of 16 covering whole 64-byte row segments); the scores come out
+// K tiles reach a per-wave LDS tile by direct HBM -> LDS loads that read whole
+// row pieces (the A operand's own layout would read 64-byte pieces, which
+// HBM serves slower) and are read back as the A operand; the scores come out
 // with one head per lane column, so the softmax row statistics stay in the
 // lane and P^T feeds the second MFMA without a shuffle.  V rows are loaded
-// as whole 256-byte (bf16) rows per 16 lanes and transposed in registers with
-// v_perm_b32 (fp8: byte gather + v_cvt_scalef32_pk_bf16_fp8).  The token order
-// inside a tile is a permutation chosen so every operand lines up.
+// into registers as whole 256-byte (bf16) rows per 16 lanes and transposed
+// with v_perm_b32 (fp8: byte gather + v_cvt_scalef32_pk_bf16_fp8).  The token
+// order inside a tile is a permutation chosen so every operand lines up.
+// Each wave walks its share as one stream of tiles with one tile in flight.
 #include "fp8.h"
 #include "pka_internal.h"
 
@@ -164,7 +167,7 @@ struct VTile {
 
 // The loads of one tile.  `slot` is the pool slot of tile token (lane & 31);
 // lanes exchange slots with cross-lane moves.  The cache is read once per
-// call, so the loads carry the non-temporal hint.
+// call, so the V loads carry the non-temporal hint.
 //
 // K goes to the wave's LDS tile `kst`: a wave instruction moves 1 KB of the
 // tile, lane i the 16-byte chunk f = 64 q + i of the tile's rows laid end to
@@ -322,12 +325,15 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const int32_t w = blockIdx.x;
     const int32_t nwg = plan[PLAN_NWG];
     if (w >= nwg) return;
-    const int64_t share = plan[PLAN_SHARE];
+    // this workgroup's share: tiles [start, end) of the requests' tiles laid
+    // end to end
+    const int64_t shq = plan[PLAN_SHARE], shr = plan[PLAN_SHARE_REM];
     const int64_t W = plan[PLAN_TOTAL];
-    const int64_t start = (int64_t)w * share;
+    const int64_t start = share_start(w, shq, shr);
     if (start >= W) return;
-    const int64_t end = min(start + share, W);
+    const int64_t end = min(share_start(w + 1, shq, shr), W);
     const int32_t* F = plan + plan_seg_prefix(a.B);
+    const int32_t* T = plan + plan_tile_prefix(a.B);
     int32_t seg = plan[plan_wg_seg(a.B) + w];
 
     // one pool slot, all KV heads
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
 
     // The wave's work is one stream of 32-position tiles.  A unit is one
     // 16-column pass over one piece (the part of a request inside this
-    // workgroup's token share); units follow each other in request order, and
+    // workgroup's tile share); units follow each other in request order, and
     // the loads of a unit's first tile and its queries go out while the
     // previous unit's last tile is computed, so a request boundary costs no
     // extra round trip to memory.
@@ -375,10 +381,12 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     // first non-empty piece from request sg on (seg = a.B: the share is done)
     auto open_piece = [&](int32_t sg, It& it) {
         for (; sg < a.B; ++sg) {
-            const int32_t f0 = load_uniform(F, sg), f1 = load_uniform(F, sg + 1);
-            if (f0 >= end) break;
-            const int32_t lo = (int32_t)(max(start, (int64_t)f0) - f0);
-            const int32_t hi = (int32_t)(min(end, (int64_t)f1) - f0);
+            const int32_t t0 = load_uniform(T, sg), t1 = load_uniform(T, sg + 1);
+            if (t0 >= end) break;
+            // token range of the piece: whole tiles, up to the request's end
+            const int32_t L = load_uniform(F, sg + 1) - load_uniform(F, sg);
+            const int32_t lo = (int32_t)(max(start, (int64_t)t0) - t0) * DEC_TILE;
+            const int32_t hi = end >= t1 ? L : (int32_t)(end - t0) * DEC_TILE;
             if (hi <= lo) continue;
             if constexpr (MQ) {
                 const int32_t nb = load_uniform(a.qo_indptr, sg + 1) - load_uniform(a.qo_indptr, sg);
@@ -580,18 +588,19 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
     const int32_t* plan = a.plan;
     const int32_t w = blockIdx.x;
     if (w >= plan[PLAN_NWG]) return;
-    const int64_t share = plan[PLAN_SHARE], W = plan[PLAN_TOTAL];
-    const int64_t start = (int64_t)w * share;
+    const int64_t shq = plan[PLAN_SHARE], shr = plan[PLAN_SHARE_REM], W = plan[PLAN_TOTAL];  // in tiles
+    const int64_t start = share_start(w, shq, shr);
     if (start >= W) return;
-    const int64_t end = min(start + share, W);
+    const int64_t end = min(share_start(w + 1, shq, shr), W);
     const int32_t* F = plan + plan_seg_prefix(a.B);
+    const int32_t* T = plan + plan_tile_prefix(a.B);
     const float scale2 = a.scale_log2;
     for (int32_t seg = plan[plan_wg_seg(a.B) + w]; seg < a.B; ++seg) {
-        const int32_t f0 = F[seg], f1 = F[seg + 1];
-        if (f0 >= end) break;
-        const int32_t lo = (int32_t)(max(start, (int64_t)f0) - f0);
-        const int32_t hi = (int32_t)(min(end, (int64_t)f1) - f0);
-        const int32_t L = f1 - f0;
+        const int32_t t0 = T[seg], t1 = T[seg + 1];
+        if (t0 >= end) break;
+        const int32_t L = F[seg + 1] - F[seg];
+        const int32_t lo = (int32_t)(max(start, (int64_t)t0) - t0) * DEC_TILE;
+        const int32_t hi = end >= t1 ? L : (int32_t)(end - t0) * DEC_TILE;
         const int32_t b = seg, page_base = a.kv_indptr[b];
         int32_t q0, nq, pfx;
         if constexpr (MQ) {
@@ -690,11 +699,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     const int32_t h = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (h >= a.Hq) return;
     const int32_t* plan = a.plan;
-    const int64_t share = plan[PLAN_SHARE];
-    const int32_t* F = plan + plan_seg_prefix(a.B);
-    const int64_t f0 = F[b], f1 = F[b + 1];
-    if (f1 <= f0) return;
-    const int64_t w0 = f0 / share, w1 = (f1 - 1) / share;
+    const int64_t shq = plan[PLAN_SHARE], shr = plan[PLAN_SHARE_REM];
+    const int32_t* T = plan + plan_tile_prefix(a.B);
+    const int64_t t0 = T[b], t1 = T[b + 1];
+    if (t1 <= t0) return;
+    const int64_t w0 = share_of(t0, shq, shr), w1 = share_of(t1 - 1, shq, shr);
     if (w0 == w1) return;  // written directly by its only workgroup
     const int32_t np = (int32_t)(w1 - w0 + 1);
     // query rows of the request (one without multi-query partials)

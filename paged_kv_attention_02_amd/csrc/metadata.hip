@@ -19,61 +19,61 @@ namespace {
 constexpr int SORT_MAX = 2048;  // extend items sorted in LDS (heaviest first)
 constexpr int SCAN_THREADS = 256;  // small workgroups: cheap barriers, more of them share the gather
 
-// Inclusive block scan of three int64 values: a shuffle scan inside each
-// wave, then the wave totals (two barriers in all).
-__device__ inline void block_scan3(int64_t& x0, int64_t& x1, int64_t& x2, int64_t* sh) {
+// Inclusive block scan of NV int64 values per thread: a shuffle scan inside
+// each wave, then the wave totals (two barriers in all).
+template <int NV>
+__device__ inline void block_scan(int64_t (&x)[NV], int64_t* sh) {
     constexpr int NW = SCAN_THREADS / 64;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int64_t y0 = __shfl_up(x0, off), y1 = __shfl_up(x1, off), y2 = __shfl_up(x2, off);
+        int64_t y[NV];
+        #pragma unroll
+        for (int v = 0; v < NV; ++v) y[v] = __shfl_up(x[v], off);
         if (lane >= off) {
-            x0 += y0;
-            x1 += y1;
-            x2 += y2;
+            #pragma unroll
+            for (int v = 0; v < NV; ++v) x[v] += y[v];
         }
     }
     if (lane == 63) {
-        sh[wv] = x0;
-        sh[NW + wv] = x1;
-        sh[2 * NW + wv] = x2;
+        #pragma unroll
+        for (int v = 0; v < NV; ++v) sh[v * NW + wv] = x[v];
     }
     __syncthreads();
-    int64_t p0 = 0, p1 = 0, p2 = 0;
-    for (int k = 0; k < wv; ++k) {
-        p0 += sh[k];
-        p1 += sh[NW + k];
-        p2 += sh[2 * NW + k];
+    #pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        int64_t p = 0;
+        for (int k = 0; k < wv; ++k) p += sh[v * NW + k];
+        x[v] += p;
     }
-    x0 += p0;
-    x1 += p1;
-    x2 += p2;
     __syncthreads();
 }
 
 __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
     // scan scratch, then the sorted extend items (at most SORT_MAX)
-    __shared__ int64_t sh[3 * SCAN_THREADS > SORT_MAX ? 3 * SCAN_THREADS : SORT_MAX];
-    __shared__ int64_t carry[3];
+    __shared__ int64_t sh[SCAN_THREADS > SORT_MAX ? SCAN_THREADS : SORT_MAX];
+    __shared__ int64_t carry[4];
     __shared__ int32_t s_status;
     // per-request prefixes kept in LDS when the gather is fused (B <= FUSE_MAX_B)
-    __shared__ int32_t sP[FUSE_MAX_B + 1], sQ[FUSE_MAX_B + 1], sF[FUSE_MAX_B + 1],
+    __shared__ int32_t sP[FUSE_MAX_B + 1], sQ[FUSE_MAX_B + 1], sT[FUSE_MAX_B + 1],
         sLen[FUSE_MAX_B];
     const int t = threadIdx.x;
     const int blk = blockIdx.x;  // > 0 only when the gather is fused: slices of it
     const bool lead = blk == 0;  // the one workgroup that writes the CSR arrays and plan
     const int32_t P = 1 << a.page_shift;
     int32_t* F = a.plan + plan_seg_prefix(a.B);
+    int32_t* T = a.plan + plan_tile_prefix(a.B);
     if (t == 0) {
-        carry[0] = carry[1] = carry[2] = 0;
+        carry[0] = carry[1] = carry[2] = carry[3] = 0;
         s_status = 0;
         sP[0] = 0;
         sQ[0] = 0;
-        sF[0] = 0;
+        sT[0] = 0;
         if (lead) {
             a.kv_indptr[0] = 0;
             a.qo_indptr[0] = 0;
             F[0] = 0;
+            T[0] = 0;
         }
     }
     __syncthreads();
@@ -95,29 +95,31 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
                 if (n > L) n = L;
             }
         }
-        int64_t ip = pages, iq = n, iL = L;
-        block_scan3(ip, iq, iL, sh);
+        // pages, new tokens, tokens, decode tiles
+        int64_t x[4] = {pages, n, L, (L + DEC_TILE - 1) / DEC_TILE};
+        block_scan<4>(x, sh);
         if (b < a.B) {
-            const int64_t cp = carry[0] + ip, cq = carry[1] + iq, cL = carry[2] + iL;
+            const int64_t cp = carry[0] + x[0], cq = carry[1] + x[1], cL = carry[2] + x[2],
+                          cT = carry[3] + x[3];
             if (cp > a.max_kv_pages || cq > a.N || cL > INT32_MAX) flags |= PKA_DEV_CAPACITY;
             if (lead) {
                 a.kv_indptr[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
                 a.qo_indptr[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
                 F[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
+                T[b + 1] = (int32_t)min(cT, (int64_t)INT32_MAX);
                 a.kv_last_page_len[b] = (int32_t)(L - ((pages - 1) << a.page_shift));
             }
             if (a.B <= FUSE_MAX_B) {
                 sP[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
                 sQ[b + 1] = (int32_t)min(cq, (int64_t)INT32_MAX);
-                sF[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
+                sT[b + 1] = (int32_t)min(cT, (int64_t)INT32_MAX);
                 sLen[b] = (int32_t)L;
             }
         }
         __syncthreads();
         if (t == SCAN_THREADS - 1) {
-            carry[0] += ip;
-            carry[1] += iq;
-            carry[2] += iL;
+            #pragma unroll
+            for (int v = 0; v < 4; ++v) carry[v] += x[v];
         }
         __syncthreads();
     }
@@ -199,25 +201,30 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         if (t == 0) a.plan[PLAN_MDST + blk] = s_status;
         return;
     }
-    const int64_t W = min(carry[2], (int64_t)INT32_MAX);
+    const int64_t W = min(carry[3], (int64_t)INT32_MAX);
     {
         // Decode partition (built for every batch, so a verify batch can take
-        // either path): the flattened token range [0, W) is cut into nwg equal
-        // shares, rounded up to whole tiles; workgroup w starts in the request
-        // that holds token w * share.
-        int64_t share = (W + a.nwg - 1) / a.nwg;
-        share = (share + DEC_TILE - 1) / DEC_TILE * DEC_TILE;
-        if (share < DEC_MIN_SHARE) share = DEC_MIN_SHARE;
+        // either path): every request is laid out as its ceil(L / DEC_TILE)
+        // tiles, the requests end to end, and that tile range [0, W) is cut
+        // into nwg shares of q or q + 1 tiles (at least DEC_MIN_SHARE);
+        // workgroup w starts in the request that holds its first tile.
+        // Cutting at tile boundaries leaves no partial tile except a
+        // request's last, so the shares differ by at most one tile of work.
+        int64_t share = W / a.nwg, rem = W % a.nwg;
+        if (share < DEC_MIN_SHARE) {
+            share = DEC_MIN_SHARE;
+            rem = 0;
+        }
         int32_t* wg_seg = a.plan + plan_wg_seg(a.B);
         for (int32_t w = t; w < a.nwg; w += SCAN_THREADS) {
-            const int64_t pos = (int64_t)w * share;
+            const int64_t pos = share_start(w, share, rem);
             int32_t seg = a.B;
             if (pos < W) {
-                const int32_t* Fs = a.B <= FUSE_MAX_B ? sF : F;
-                int32_t lo = 0, hi = a.B - 1;  // largest b with F[b] <= pos
+                const int32_t* Ts = a.B <= FUSE_MAX_B ? sT : T;
+                int32_t lo = 0, hi = a.B - 1;  // largest b with T[b] <= pos
                 while (lo < hi) {
                     const int32_t mid = (lo + hi + 1) >> 1;
-                    if (Fs[mid] <= pos) lo = mid; else hi = mid - 1;
+                    if (Ts[mid] <= pos) lo = mid; else hi = mid - 1;
                 }
                 seg = lo;
             }
@@ -225,6 +232,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         }
         if (t == 0) {
             a.plan[PLAN_SHARE] = (int32_t)share;
+            a.plan[PLAN_SHARE_REM] = (int32_t)rem;
             a.plan[PLAN_TOTAL] = (int32_t)W;
             a.plan[PLAN_NWG] = a.nwg;
             a.plan[PLAN_EXT_COUNT] = 0;

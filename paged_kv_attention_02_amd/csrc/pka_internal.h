@@ -12,11 +12,12 @@ namespace pka {
 // Layout of the int32 `plan` array of a pka_batch.
 enum : int32_t {
     PLAN_STATUS = 0,     // sticky PKA_DEV_* flags of save_kv / attention (atomic OR)
-    PLAN_SHARE = 1,      // decode: tokens of the flattened batch per workgroup
-    PLAN_TOTAL = 2,      // decode: sum of L_b
+    PLAN_SHARE = 1,      // decode: tiles per workgroup (q; the first PLAN_SHARE_REM take q + 1)
+    PLAN_TOTAL = 2,      // decode: sum over requests of ceil(L_b / DEC_TILE)
     PLAN_NWG = 3,        // decode: workgroups the partition was made for
     PLAN_EXT_COUNT = 4,  // extend: number of (request, query tile) items
     PLAN_EXT_TQ = 5,     // extend: query tokens per item
+    PLAN_SHARE_REM = 6,  // decode: workgroups whose share is one tile longer
     PLAN_MDST = 16,      // PKA_DEV_* flags of each metadata workgroup (MD_SLOTS words)
     PLAN_HDR = 80,
 };
@@ -31,16 +32,31 @@ constexpr int64_t FUSE_MAX_ITEMS = (int64_t)MD_SLOTS * 1024 * FUSE_PER_THREAD;
 
 // Tokens per decode tile (two MFMA row blocks of 16 tokens).
 constexpr int DEC_TILE = 32;
-// Smallest share of the flattened token range given to one workgroup.
-constexpr int DEC_MIN_SHARE = 64;
+// Smallest share of the flattened tile range given to one workgroup (tiles).
+constexpr int DEC_MIN_SHARE = 2;
+// Decode shares: workgroup w takes tiles [share_start(w), share_start(w + 1))
+// of the requests' tiles laid end to end, q tiles each and one more for the
+// first r workgroups.
+__host__ __device__ inline int64_t share_start(int64_t w, int64_t q, int64_t r) {
+    return w * q + (w < r ? w : r);
+}
+// the workgroup whose share holds tile t
+__host__ __device__ inline int64_t share_of(int64_t t, int64_t q, int64_t r) {
+    const int64_t big = r * (q + 1);
+    return t < big ? t / (q + 1) : r + (t - big) / q;
+}
 // Upper bound of decode workgroups (persistent grid).
 constexpr int DEC_MAX_WG = 2048;
 // Most query tokens per request on the decode path (speculative verify).
 constexpr int DEC_MAX_Q = 16;
 
-// plan offsets that depend on the batch size
+// plan offsets that depend on the batch size: the token prefix F[b] = sum of
+// L over requests before b, the tile prefix T[b] = sum of ceil(L / DEC_TILE)
+// (the decode partition cuts it), then the first request of each decode
+// workgroup
 __host__ __device__ inline int64_t plan_seg_prefix(int32_t /*B*/) { return PLAN_HDR; }
-__host__ __device__ inline int64_t plan_wg_seg(int32_t B) { return PLAN_HDR + (int64_t)B + 1; }
+__host__ __device__ inline int64_t plan_tile_prefix(int32_t B) { return PLAN_HDR + (int64_t)B + 1; }
+__host__ __device__ inline int64_t plan_wg_seg(int32_t B) { return PLAN_HDR + 2 * ((int64_t)B + 1); }
 __host__ __device__ inline int64_t plan_ext_items(int32_t B) {
     return plan_wg_seg(B) + DEC_MAX_WG;
 }
