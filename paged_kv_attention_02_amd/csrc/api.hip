@@ -22,9 +22,10 @@ struct pka_ctx {
     int32_t G;
     int32_t qgroups;     // ceil(G / 16): decode waves per KV head
     int32_t page_shift;
-    int32_t wpb;         // decode waves per workgroup
+    int32_t wpb;         // decode waves per share (KV-head units of one share in a workgroup)
     int32_t ext_tq;      // extend query tokens per work item
-    std::atomic<int32_t> nwg{0};  // decode workgroups (from the device's CU count)
+    std::atomic<int32_t> nwg{0};  // decode shares (from the device's CU count)
+    std::atomic<int32_t> spw{0};  // decode shares per workgroup
 };
 
 namespace {
@@ -50,22 +51,44 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t elem_bytes(pka_dtype t) { return t == PKA_F32 ? 4 : t == PKA_BF16 ? 2 : 1; }
 
-// Decode workgroups: exactly one resident round (every workgroup on the
-// device at once, so the equal tile shares finish together), from the
-// device's CU count and the kernel's occupancy.  Queried once per context.
-pka_status decode_wgs(const pka_ctx* ctx, int32_t* out) {
-    int32_t v = ctx->nwg.load(std::memory_order_relaxed);
+// Decode shares: exactly one resident round (every workgroup on the device
+// at once, so the equal tile shares finish together), from the device's CU
+// count and the kernel's occupancy.  With fewer than 8 waves per share, the
+// MFMA kernel packs 8 / wpb shares into one 8-wave workgroup when that keeps
+// as many waves resident (the two waves on each SIMD are then balanced
+// against each other).  Queried once per context.
+int32_t decode_wpb(const pka_ctx* ctx) {
+    // the fp32 kernel is built for workgroups of at most 4 waves
+    return ctx->cfg.kv_dtype == PKA_F32 ? std::min(ctx->wpb, 4) : ctx->wpb;
+}
+
+pka_status decode_wgs(const pka_ctx* ctx, int32_t* out, int32_t* spw_out = nullptr) {
+    int32_t v = ctx->nwg.load(std::memory_order_acquire);
+    int32_t spw = ctx->spw.load(std::memory_order_relaxed);
     if (v <= 0) {
         int dev = 0, cus = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_fail(e, "querying the device");
-        int per_cu = pka::decode_blocks_per_cu(ctx->cfg.kv_dtype, ctx->dk, ctx->dv, ctx->wpb);
+        const pka_dtype kv = ctx->cfg.kv_dtype;
+        const int wpb = decode_wpb(ctx);
+        int per_cu = pka::decode_blocks_per_cu(kv, ctx->dk, ctx->dv, wpb);  // shares per CU
+        spw = 1;
+        if (kv != PKA_F32 && wpb < 8) {
+            const int packed = pka::decode_blocks_per_cu(kv, ctx->dk, ctx->dv, 8);
+            if (packed >= 1 && packed * 8 >= per_cu * wpb) {
+                spw = 8 / wpb;
+                per_cu = packed * spw;
+            }
+        }
         if (per_cu < 1) per_cu = 1;
         v = std::min<int32_t>(pka::DEC_MAX_WG, std::max(1, cus * per_cu));
-        const_cast<pka_ctx*>(ctx)->nwg.store(v, std::memory_order_relaxed);
+        pka_ctx* c = const_cast<pka_ctx*>(ctx);
+        c->spw.store(spw, std::memory_order_relaxed);
+        c->nwg.store(v, std::memory_order_release);
     }
     *out = v;
+    if (spw_out) *spw_out = spw;
     return PKA_OK;
 }
 
@@ -127,6 +150,7 @@ pka::AttnArgs attn_args(const pka_ctx* ctx, const pka_batch* md, const void* q, 
     a.qgroups = ctx->qgroups;
     a.page_shift = ctx->page_shift;
     a.num_pages = c.num_pages;
+    a.spw = 1;
     const float k_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f;
     a.scale_log2 = c.scale * 1.4426950408889634f * k_scale;
     a.v_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f;
@@ -160,14 +184,15 @@ pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     const int32_t qslots = decode_qslots(md->mode, md->num_q_tokens);
     if (write_new && qslots != 1)
         return fail(PKA_ERR_INVALID_ARG, "the fused cache write serves decode batches only");
-    int32_t nwg = 0;
-    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+    int32_t nwg = 0, spw = 1;
+    if ((s = decode_wgs(ctx, &nwg, &spw)) != PKA_OK) return s;
     const int64_t need = decode_ws_bytes(ctx, md->batch, nwg, qslots);
     if (!workspace || (int64_t)workspace_bytes < need || !aligned16(workspace))
         return fail(PKA_ERR_WORKSPACE, "decode needs %lld workspace bytes (16-byte aligned), got %zu",
                     (long long)need, workspace_bytes);
     pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
     a.nwg = nwg;
+    a.spw = spw;
     a.qslots = qslots;
     a.ws_o = (float*)workspace;
     a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * qslots * ctx->cfg.num_q_heads * ctx->dv;
@@ -181,7 +206,7 @@ pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, c
         a.v_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f);
     }
     hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
-                                      ctx->wpb, (hipStream_t)stream);
+                                      decode_wpb(ctx), (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
 }
 

@@ -314,15 +314,35 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     using S = DecodeShape<DK, DV, FP8>;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, j = lane >> 4;
-    const int wpb = blockDim.x >> 6;
-    const int unit = blockIdx.y * wpb + (threadIdx.x >> 6);
+    // a workgroup holds a.spw shares of wpb waves (one KV-head unit each)
+    const int waves = blockDim.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wpb = waves / a.spw;
+    const int unit = blockIdx.y * wpb + wv % wpb;
     const int g = unit / a.qgroups;
     const int h0 = g * a.G + (unit % a.qgroups) * 16;
     const int nh = min(16, a.G - (unit % a.qgroups) * 16);
+
+    // this wave's LDS: the K tile, then the queries of the next unit; after
+    // the waves' regions, one progress word per wave
+    extern __shared__ __attribute__((aligned(1024))) uint8_t dec_lds[];
+    uint8_t* const kst = dec_lds + wv * S::WAVE_LDS;
+    uint8_t* const qbuf = kst + S::KTILE;
+    int32_t* const prog = (int32_t*)(dec_lds + waves * S::WAVE_LDS);
+    // Waves wv and wv ^ 4 of an 8-wave workgroup share a SIMD, and the one
+    // with the higher priority gets the larger part of the memory pipeline
+    // (equal priorities favour the older wave, ~8% on the Llama-shaped
+    // batch).  Both serve the same number of tiles, so each step the wave
+    // that is behind its partner, or level with it and younger, takes the
+    // higher priority; the pair then ends together.  The words are read
+    // without synchronisation: a stale value only shifts a priority.
+    const bool pair = waves == 8;
+    int32_t nst = 0;  // tiles computed so far
+    if (pair) __hip_atomic_store(prog + wv, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (g >= a.Hkv) return;
 
     const int32_t* plan = a.plan;
-    const int32_t w = blockIdx.x;
+    const int32_t w = blockIdx.x * a.spw + wv / wpb;
     const int32_t nwg = plan[PLAN_NWG];
     if (w >= nwg) return;
     // this workgroup's share: tiles [start, end) of the requests' tiles laid
@@ -341,10 +361,6 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * DK * S::ESZ;
     const uint8_t* vbase = (const uint8_t*)a.v_pool + (int64_t)g * DV * S::ESZ;
     const int tok = lane & 31;  // tile token whose slot this lane looks up
-    // this wave's LDS: the K tile, then the queries of the next unit
-    extern __shared__ __attribute__((aligned(1024))) uint8_t dec_lds[];
-    uint8_t* const kst = dec_lds + (threadIdx.x >> 6) * S::WAVE_LDS;
-    uint8_t* const qbuf = kst + S::KTILE;
 
     // The wave's work is one stream of 32-position tiles.  A unit is one
     // 16-column pass over one piece (the part of a request inside this
@@ -537,10 +553,21 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile cur, its queries and nx's slots landed
         asm volatile("" ::: "memory");       // LDS reads stay after the wait
         if (cur.t0 == cur.lo) take_q();      // cur opens its unit
+        int32_t other = 0;
+        if (pair) {
+            ++nst;
+            __hip_atomic_store(prog + wv, nst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            other = __hip_atomic_load(prog + (wv ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
         f32x4_t st[2];
         tile_scores<DK, DV, FP8>(kst, qop, st, j);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the K reads are done ...
         asm volatile("" ::: "memory");       // ... before the direct loads refill the tile
+        if (pair) {
+            const int32_t o = __builtin_amdgcn_readfirstlane(other);
+            if (o > nst || (o == nst && wv >= 4)) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         if (nx.seg < a.B) {
             const bool opens = nx.t0 == nx.lo;  // nx is the first tile of its unit
             if (opens) new_token(nx);
@@ -579,14 +606,15 @@ template <int DK, int DV, bool MQ>
 __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
     constexpr int EPK = DK / 64, EPV = DV / 64;  // key and value dims per lane
     const int lane = threadIdx.x & 63;
-    const int wpb = blockDim.x >> 6;
-    const int unit = blockIdx.y * wpb + (threadIdx.x >> 6);
+    const int wv = threadIdx.x >> 6;
+    const int wpb = (blockDim.x >> 6) / a.spw;
+    const int unit = blockIdx.y * wpb + wv % wpb;
     const int g = unit / a.qgroups;
     const int h0 = g * a.G + (unit % a.qgroups) * 16;
     const int nh = min(16, a.G - (unit % a.qgroups) * 16);
     if (g >= a.Hkv) return;
     const int32_t* plan = a.plan;
-    const int32_t w = blockIdx.x;
+    const int32_t w = blockIdx.x * a.spw + wv / wpb;
     if (w >= plan[PLAN_NWG]) return;
     const int64_t shq = plan[PLAN_SHARE], shr = plan[PLAN_SHARE_REM], W = plan[PLAN_TOTAL];  // in tiles
     const int64_t start = share_start(w, shq, shr);
@@ -686,10 +714,10 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
 
 // Log-sum-exp merge of the partials of requests that were split across
 // workgroups: out = sum_c e^(lse_c - M) o_c / sum_c e^(lse_c - M) and
-// lse = M + ln(sum_c e^(lse_c - M)).  One wave per (request, head): lanes
-// first take one partial each (max and normaliser by wave reductions), then
-// lanes take head dims and sweep the partials with several loads in flight.
-// D: the value (output) width.
+// lse = M + ln(sum_c e^(lse_c - M)).  One wave per (request, head, query
+// row; grid z = query rows): lanes first take one partial each (max and
+// normaliser by wave reductions), then lanes take head dims and sweep the
+// partials with several loads in flight.  D: the value (output) width.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     constexpr int EPL = D / 64;
@@ -717,7 +745,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     }
     const int64_t lstride = (int64_t)a.qslots * a.Hq;  // per partial
     const int64_t ostride = lstride * D;
-    for (int32_t qi = 0; qi < nq; ++qi) {
+    const int32_t qi = blockIdx.z;
+    if (qi >= nq) return;
+    {
         const float* lse_col = a.ws_lse + ((b + w0) * a.qslots + qi) * a.Hq + h;
         const float* o_col = a.ws_o + (((b + w0) * a.qslots + qi) * a.Hq + h) * D;
 
@@ -788,24 +818,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
     }
 }
 
-// Dynamic LDS of a decode workgroup of wpb waves.
+// Dynamic LDS of a decode workgroup of `waves` waves: their regions and one
+// progress word each.
 template <int DK, int DV, bool FP8>
-size_t decode_lds_bytes(int wpb) {
-    return (size_t)wpb * DecodeShape<DK, DV, FP8>::WAVE_LDS;
+size_t decode_lds_bytes(int waves) {
+    return (size_t)waves * (DecodeShape<DK, DV, FP8>::WAVE_LDS + 4);
 }
 
 template <int DK, int DV>
 hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb, hipStream_t s) {
     const int units = a.Hkv * a.qgroups;
-    const dim3 grid(a.nwg, units / wpb);
-    const dim3 block(64 * wpb);
+    const int waves = wpb * a.spw;
+    const dim3 grid((a.nwg + a.spw - 1) / a.spw, units / wpb);
+    const dim3 block(64 * waves);
     const bool mq = a.qslots > 1;
     if (kv == PKA_BF16) {
-        const size_t lds = decode_lds_bytes<DK, DV, false>(wpb);
+        const size_t lds = decode_lds_bytes<DK, DV, false>(waves);
         if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true>), grid, block, lds, s, a);
         else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false>), grid, block, lds, s, a);
     } else if (kv == PKA_FP8_E4M3FN) {
-        const size_t lds = decode_lds_bytes<DK, DV, true>(wpb);
+        const size_t lds = decode_lds_bytes<DK, DV, true>(waves);
         if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true>), grid, block, lds, s, a);
         else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false>), grid, block, lds, s, a);
     } else {
@@ -814,7 +846,7 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 mgrid(a.B, (a.Hq + 3) / 4);
+    const dim3 mgrid(a.B, (a.Hq + 3) / 4, a.qslots);
     if (q == PKA_BF16)
         hipLaunchKernelGGL((decode_merge_kernel<DV, true>), mgrid, dim3(256), 0, s, a);
     else
@@ -823,26 +855,26 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
 }
 
 template <int DK, int DV>
-int blocks_per_cu_d(pka_dtype kv, int wpb) {
+int blocks_per_cu_d(pka_dtype kv, int waves) {
     int n = 0;
     hipError_t e;
     if (kv == PKA_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, false, false>, 64 * wpb,
-                                                         decode_lds_bytes<DK, DV, false>(wpb));
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, false, false>, 64 * waves,
+                                                         decode_lds_bytes<DK, DV, false>(waves));
     else if (kv == PKA_FP8_E4M3FN)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, true, false>, 64 * wpb,
-                                                         decode_lds_bytes<DK, DV, true>(wpb));
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, true, false>, 64 * waves,
+                                                         decode_lds_bytes<DK, DV, true>(waves));
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<DK, DV, false>, 64 * wpb, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<DK, DV, false>, 64 * waves, 0);
     return e == hipSuccess ? n : 0;
 }
 
 }  // namespace
 
-int decode_blocks_per_cu(pka_dtype kv, int DK, int DV, int wpb) {
-    if (DK == 128 && DV == 128) return blocks_per_cu_d<128, 128>(kv, wpb);
-    if (DK == 64 && DV == 64) return blocks_per_cu_d<64, 64>(kv, wpb);
-    if (DK == 192 && DV == 128) return blocks_per_cu_d<192, 128>(kv, wpb);
+int decode_blocks_per_cu(pka_dtype kv, int DK, int DV, int waves) {
+    if (DK == 128 && DV == 128) return blocks_per_cu_d<128, 128>(kv, waves);
+    if (DK == 64 && DV == 64) return blocks_per_cu_d<64, 64>(kv, waves);
+    if (DK == 192 && DV == 128) return blocks_per_cu_d<192, 128>(kv, waves);
     return 0;
 }
 

@@ -129,7 +129,8 @@ struct AttnArgs {
     int32_t qgroups;  // ceil(G / 16): waves per KV head
     int32_t page_shift;
     int32_t num_pages;
-    int32_t nwg;
+    int32_t nwg;       // decode shares (the partition's workgroup count)
+    int32_t spw;       // decode shares per workgroup (its waves = spw * units per share)
     float scale_log2;  // scale * log2(e) * k_scale
     float v_scale;
     // decode partial slots per (request, workgroup): 1, or up to DEC_MAX_Q
@@ -149,12 +150,14 @@ struct AttnArgs {
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 // DK: key (and query) head width; DV: value (and output) head width.
 hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, const SaveArgs& a, hipStream_t s);
-hipError_t launch_decode(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a,
-                         int waves_per_wg, hipStream_t s);
+// wpb: waves per share (KV-head units of one share in a workgroup); a
+// workgroup holds a.spw shares, 64 * wpb * a.spw threads.
+hipError_t launch_decode(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, int wpb,
+                         hipStream_t s);
 hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, hipStream_t s);
 
-// Decode workgroups of `wpb` waves that fit on one compute unit at once.
-int decode_blocks_per_cu(pka_dtype kv, int DK, int DV, int wpb);
+// Decode workgroups of `waves` waves that fit on one compute unit at once.
+int decode_blocks_per_cu(pka_dtype kv, int DK, int DV, int waves);
 
 // Query tokens per extend item for a dtype pair.
 int extend_tq(pka_dtype q, pka_dtype kv, int G, int page_size);

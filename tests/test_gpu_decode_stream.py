@@ -7,7 +7,8 @@ wave cross many units (pieces of requests, column passes) in a row.
   writes its request's new row first);
 - query-head groups of 24 and 48 (waves with 16- and 8-column passes) on the
   decode path and for speculative verify;
-- one long request surrounded by tiny ones (a share holding both).
+- one long request surrounded by tiny ones (a share holding both);
+- KV-head counts that pack 1 to 8 shares into one workgroup.
 
 Outputs are checked against the fp64 oracle (bf16: max-abs 2e-2, rel-RMS 5e-3;
 fp8: 5e-2, 2e-2; lse within 4e-3), pools byte for byte after the fused write.
@@ -101,3 +102,16 @@ def test_verify_groups_with_uneven_passes(hq, hkv):
 def test_long_request_among_tiny_ones():
     lens = [3, 1, 2] * 20 + [9000] + [1, 4, 2] * 20
     _run(DEC.replace(batch=len(lens), page_size=16, seed=146), seq_lens=lens, name="long among tiny")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("hq,hkv", [(3, 3), (12, 6), (16, 8), (32, 16), (24, 12)])
+def test_workgroup_layouts(hq, hkv, kv):
+    """KV-head counts giving 1, 2, 4 and 8 units per share and odd counts: the
+    MFMA kernel packs 8 / units-per-share shares into one 8-wave workgroup
+    (waves wv and wv ^ 4 then balance each other); the fp32 kernel runs
+    workgroups of at most 4 waves."""
+    qd = "f32" if kv == "f32" else "bf16"
+    _run(DEC.replace(batch=9, num_q_heads=hq, num_kv_heads=hkv, q_dtype=qd, kv_dtype=kv,
+                     seq_len_kind="uniform", seq_len_args=(1, 1200), seed=147),
+         name=f"decode {hq}/{hkv} {kv}")
