@@ -224,6 +224,80 @@ def bench_decode_kernel(spec, iters: int, warm: int = 10):
     return out
 
 
+def bench_verify(spec, iters: int, warm: int = 10):
+    """Speculative verify (target_verify batches, n chained draft tokens per
+    request) through both paths the dispatch can take: the decode path
+    (speculative attention mode decode: the split-K multi-query decode kernel
+    + merge) and the extend path (mode prefill).  Two copies of pools and
+    metadata are used alternately.  GB/s counts each cached token's K and V
+    once."""
+    import torch
+    import workloads
+    import paged_kv_attention_02_amd as pka
+    from tests.gpu_problem import GpuProblem
+    layout = workloads.make_layout(spec)
+    values = workloads.make_values(layout, device="cuda")
+    probs = []
+    for _ in range(2):
+        p = GpuProblem(layout, values)
+        p.mode = "target_verify"
+        p.md = pka.Batch(p.ctx, "target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages)
+        p.metadata_step()
+        probs.append(p)
+    torch.cuda.synchronize()
+    kvb = kv_bytes(layout)
+    n = sorted(set(int(x) for x in layout.extend_lens))
+    out = {"workload": spec.name, "kv_tokens": layout.total_tokens, "q_tokens": layout.num_q_tokens,
+           "draft_tokens_per_request": n[0] if len(n) == 1 else n}
+    for path, mode in (("decode_path", "decode"), ("extend_path", "prefill")):
+        call = lambda i, m=mode: probs[i % 2].attention_step(save=False, spec_mode=m, lse=False)
+        ms = time_events(call, iters, warm=warm)
+        out[path] = {"ms": round(ms, 4), "kv_read_GBps": round(kvb / ms / 1e6, 1),
+                     "frac_hbm_peak": round(kvb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    for p in probs:
+        assert p.md.status() == 0, "device status flags set"
+    del probs
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_graph_step(spec, iters: int):
+    """The headline step (metadata + forward with the cache write) captured
+    once per copy of pools and metadata in a HIP graph and replayed
+    alternately, against the same steps launched eagerly."""
+    import torch
+    import workloads
+    from tests.gpu_problem import GpuProblem
+    layout = workloads.make_layout(spec)
+    values = workloads.make_values(layout, device="cuda")
+    probs = [GpuProblem(layout, values), GpuProblem(layout, values)]
+    graphs = []
+    for p in probs:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            p.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            p.step()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    ms_graph = time_events(lambda i: graphs[i % 2].replay(), iters, warm=10)
+    ms_eager = time_events(lambda i: probs[i % 2].step(), iters, warm=10)
+    for p in probs:
+        assert p.md.status() == 0, "device status flags set"
+    kvb = kv_bytes(layout)
+    out = {"workload": spec.name, "ms_per_step_graph": round(ms_graph, 4),
+           "ms_per_step_eager": round(ms_eager, 4),
+           "kv_read_GBps_graph": round(kvb / ms_graph / 1e6, 1),
+           "kv_read_GBps_eager": round(kvb / ms_eager / 1e6, 1)}
+    del graphs, probs
+    torch.cuda.empty_cache()
+    return out
+
+
 # Untimed extend calls before timing: the matrix cores' clock takes ~10 ms of
 # sustained MFMA load to settle (the first 20 calls run ~12% slower).
 EXTEND_WARM = 20
@@ -305,7 +379,7 @@ def main():
                     help="skip the extend / other decode figures and the clock and power sampling")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--only", choices=["extend", "extend_fp8", "qwen3_235b_decode", "long_fp8_decode", "copy", "gemm",
-                                       "asym_extend", "asym_decode"], default=None,
+                                       "asym_extend", "asym_decode", "verify", "graph"], default=None,
                     help="run one extra leg alone (for profiling) and print its figures")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -334,6 +408,10 @@ def main():
             res = bench_extend(args.steps, gpu_state=False, spec=workloads.EXTRA["asym_extend"])
         elif args.only == "asym_decode":
             res = bench_decode_kernel(workloads.EXTRA["asym_decode"], args.steps)
+        elif args.only == "verify":
+            res = bench_verify(workloads.EXTRA["llama3_8b_verify"], args.steps)
+        elif args.only == "graph":
+            res = bench_graph_step(workloads.WORKLOADS["llama3_8b_decode"], args.steps)
         else:
             res = bench_decode_kernel(workloads.WORKLOADS[args.only], args.steps)
         print(json.dumps(res), flush=True)
@@ -419,6 +497,17 @@ def main():
         log(f"extend, 192/128 widths: {result['asym_extend']}")
         result["asym_decode"] = bench_decode_kernel(workloads.EXTRA["asym_decode"], args.steps)
         log(f"decode, 192/128 widths: {result['asym_decode']}")
+        # speculative verify through the decode path and the extend path
+        result["verify"] = {}
+        for n_draft in (4, 8):
+            vs = workloads.EXTRA["llama3_8b_verify"]
+            vs = vs.replace(name=vs.name.replace("_n4", f"_n{n_draft}"), new_len_args=(n_draft, n_draft),
+                            prefix_len_args=(512 - n_draft, 4096 - n_draft))
+            result["verify"][f"n{n_draft}"] = bench_verify(vs, args.steps)
+            log(f"verify, {n_draft} draft tokens: {result['verify'][f'n{n_draft}']}")
+        # the headline step replayed from a HIP graph
+        result["graph_step"] = bench_graph_step(spec, args.steps)
+        log(f"step from a HIP graph: {result['graph_step']}")
 
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")

@@ -105,6 +105,11 @@ EXTRA = {
     "asym_decode": Spec("asym_decode_bf16_b64_h16_dk192_dv128_p128", "decode", 64, 16, 16, 192, 128,
                         "bf16", "bf16", seed=13, seq_len_kind="uniform",
                         seq_len_args=(512, 8192), v_head_dim=128),
+    # Speculative verify on the Llama-shaped cache: 64 requests, each with 4
+    # chained draft tokens (topk = 1) on a cached prefix uniform in
+    # [508, 4092] (contexts of 512 ... 4096 tokens, as the decode batch).
+    "llama3_8b_verify": Spec("verify_bf16_b64_g4_d128_p16_n4", "extend", 64, 32, 8, 128, 16, "bf16",
+                             "bf16", seed=14, new_len_args=(4, 4), prefix_len_args=(508, 4092)),
 }
 
 
