@@ -59,13 +59,39 @@ def extend_flops(layout) -> float:
     return 2.0 * (spec.head_dim + spec.value_dim) * spec.num_q_heads * pairs
 
 
+def code_tokens(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed: a
+    change to comments or layout alone leaves the kernel, and this, the same."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            k = text.find("*/", i + 2)
+            i = n if k < 0 else k + 2
+            out.append(" ")
+        elif c in "\"'":
+            k = i + 1
+            while k < n and text[k] != c:
+                k += 2 if text[k] == "\\" else 1
+            out.append(text[i:k + 1])
+            i = k + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash(*names) -> str:
-    """Hash of kernel sources plus the build flags (what decides the code)."""
+    """Hash of the kernel sources' code (comments and layout aside) plus the
+    build flags: what decides the compiled kernels."""
     from paged_kv_attention_02_amd import build as pkb
     h = hashlib.sha256(" ".join(pkb.HIPCC_FLAGS).encode())
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_attention_02_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_attention_02_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,11 +4,10 @@
 // ("sglang-101 s4.2 --attention-backend", section "Two backends in one
 // server"; "[SGLang] Hybrid Attention", introduction).  The kernel is split-K
 // flash decoding: the batch's 32-token tiles, laid end to end, are cut into
-// one share per workgroup (equal to within a tile); each wave of a workgroup
-// serves one KV head (16 query heads of its group at most) over that share
-// with an online softmax, and a share that covers only part of a request
-// leaves an fp32 partial (output and log-sum-exp) that a merge kernel
-// combines.
+// shares equal to within a tile, one or more per workgroup; each wave serves
+// one KV head (16 query heads of its group at most) over one share with an
+// online softmax, and a share that covers only part of a request leaves an
+// fp32 partial (output and log-sum-exp) that a merge kernel combines.
 //
 // gfx950 mapping of the MFMA variant (bf16 or fp8 e4m3fn cache):
 //   S^T[token, head]  = K[token, :] . Q^T        v_mfma_f32_16x16x32_bf16
@@ -332,10 +331,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     // Waves wv and wv ^ 4 of an 8-wave workgroup share a SIMD, and the one
     // with the higher priority gets the larger part of the memory pipeline
     // (equal priorities favour the older wave, ~8% on the Llama-shaped
-    // batch).  Both serve the same number of tiles, so each step the wave
-    // that is behind its partner, or level with it and younger, takes the
-    // higher priority; the pair then ends together.  The words are read
-    // without synchronisation: a stale value only shifts a priority.
+    // batch).  Partners serve about the same number of tiles (the same share,
+    // or shares one tile apart), so each step the wave that is behind its
+    // partner, or level with it and younger, takes the higher priority; the
+    // pair then ends together.  The words are read without synchronisation:
+    // a stale value only shifts a priority.
     const bool pair = waves == 8;
     int32_t nst = 0;  // tiles computed so far
     if (pair) __hip_atomic_store(prog + wv, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -345,8 +345,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const int32_t w = blockIdx.x * a.spw + wv / wpb;
     const int32_t nwg = plan[PLAN_NWG];
     if (w >= nwg) return;
-    // this workgroup's share: tiles [start, end) of the requests' tiles laid
-    // end to end
+    // this wave's share: tiles [start, end) of the requests' tiles laid end
+    // to end
     const int64_t shq = plan[PLAN_SHARE], shr = plan[PLAN_SHARE_REM];
     const int64_t W = plan[PLAN_TOTAL];
     const int64_t start = share_start(w, shq, shr);
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
 
     // The wave's work is one stream of 32-position tiles.  A unit is one
     // 16-column pass over one piece (the part of a request inside this
-    // workgroup's tile share); units follow each other in request order, and
+    // wave's tile share); units follow each other in request order, and
     // the loads of a unit's first tile and its queries go out while the
     // previous unit's last tile is computed, so a request boundary costs no
     // extra round trip to memory.

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         // either path): every request is laid out as its ceil(L / DEC_TILE)
         // tiles, the requests end to end, and that tile range [0, W) is cut
         // into nwg shares of q or q + 1 tiles (at least DEC_MIN_SHARE);
-        // workgroup w starts in the request that holds its first tile.
+        // share w starts in the request that holds its first tile.
         // Cutting at tile boundaries leaves no partial tile except a
         // request's last, so the shares differ by at most one tile of work.
         int64_t share = W / a.nwg, rem = W % a.nwg;

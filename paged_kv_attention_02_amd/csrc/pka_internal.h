@@ -34,18 +34,18 @@ constexpr int64_t FUSE_MAX_ITEMS = (int64_t)MD_SLOTS * 1024 * FUSE_PER_THREAD;
 constexpr int DEC_TILE = 32;
 // Smallest share of the flattened tile range given to one workgroup (tiles).
 constexpr int DEC_MIN_SHARE = 2;
-// Decode shares: workgroup w takes tiles [share_start(w), share_start(w + 1))
-// of the requests' tiles laid end to end, q tiles each and one more for the
-// first r workgroups.
+// Decode shares: share w is tiles [share_start(w), share_start(w + 1)) of the
+// requests' tiles laid end to end, q tiles each and one more for the first r
+// shares.
 __host__ __device__ inline int64_t share_start(int64_t w, int64_t q, int64_t r) {
     return w * q + (w < r ? w : r);
 }
-// the workgroup whose share holds tile t
+// the share that holds tile t
 __host__ __device__ inline int64_t share_of(int64_t t, int64_t q, int64_t r) {
     const int64_t big = r * (q + 1);
     return t < big ? t / (q + 1) : r + (t - big) / q;
 }
-// Upper bound of decode workgroups (persistent grid).
+// Upper bound of decode shares (persistent grid).
 constexpr int DEC_MAX_WG = 2048;
 // Most query tokens per request on the decode path (speculative verify).
 constexpr int DEC_MAX_Q = 16;
