@@ -125,8 +125,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
     }
     __syncthreads();
     if (a.fuse_gather) {
-        // kv_indices[i] and out_cache_loc[j]: find the request by binary search
-        // over the LDS prefixes (largest b with prefix[b] <= i).
+        // kv_indices[i] and out_cache_loc[j].  Each thread takes U consecutive
+        // items of its workgroup's slice per round: one binary search over the
+        // LDS prefixes finds the request of the first (largest b with
+        // prefix[b] <= i), the next items step forward from there.  Both
+        // kinds of page-table reads go out before any store, so the two
+        // gathers cost one round trip to memory.  With more than one
+        // workgroup the lead one takes no slice (it builds the plan meanwhile).
         auto find = [&](const int32_t* pre, int32_t i) {
             int32_t lo = 0, hi = a.B - 1;
             while (lo < hi) {
@@ -135,59 +140,46 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             }
             return lo;
         };
-        // this workgroup's slice of the pages and of the new tokens, with
-        // FUSE_PER_THREAD independent lookups per thread in flight
         constexpr int U = FUSE_PER_THREAD;
-        const int32_t nblk = gridDim.x;
+        const int32_t g0 = gridDim.x > 1 ? 1 : 0;
+        const int32_t nblk = gridDim.x - g0, gblk = blk - g0;
         const int32_t npages = (int32_t)min((int64_t)sP[a.B], a.max_kv_pages);
         const int32_t pchunk = (npages + nblk - 1) / nblk;
-        const int32_t p_lo = blk * pchunk, p_hi = min(npages, p_lo + pchunk);
-        for (int32_t i0 = p_lo + t; i0 < p_hi; i0 += U * SCAN_THREADS) {
-            int32_t pg[U];
-            #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < p_hi) {
-                    const int32_t b = find(sP, i);
-                    pg[u] = a.page_table[(int64_t)b * a.pt_stride + (i - sP[b])];
-                }
-            }
-            #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < p_hi) {
-                    if (pg[u] < 0 || pg[u] >= a.num_pages) {
-                        flags |= PKA_DEV_BAD_PAGE;
-                        pg[u] = min(max(pg[u], 0), a.num_pages - 1);
-                    }
-                    a.kv_indices[i] = pg[u];
-                }
-            }
-        }
+        const int32_t p_lo = gblk * pchunk, p_hi = gblk < 0 ? p_lo : min(npages, p_lo + pchunk);
         const int32_t nnew = min(sQ[a.B], a.N);
         const int32_t qchunk = (nnew + nblk - 1) / nblk;
-        const int32_t q_lo = blk * qchunk, q_hi = min(nnew, q_lo + qchunk);
-        for (int32_t i0 = q_lo + t; i0 < q_hi; i0 += U * SCAN_THREADS) {
-            int32_t pg[U], pos[U];
+        const int32_t q_lo = gblk * qchunk, q_hi = gblk < 0 ? q_lo : min(nnew, q_lo + qchunk);
+        auto clamp_page = [&](int32_t pg) {
+            if (pg < 0 || pg >= a.num_pages) {
+                flags |= PKA_DEV_BAD_PAGE;
+                pg = min(max(pg, 0), a.num_pages - 1);
+            }
+            return pg;
+        };
+        for (int32_t k0 = U * t; k0 < max(p_hi - p_lo, q_hi - q_lo); k0 += U * SCAN_THREADS) {
+            int32_t pg[U], qpg[U], pos[U];
+            const int32_t i0 = p_lo + k0, j0 = q_lo + k0;
+            int32_t bp = i0 < p_hi ? find(sP, i0) : 0;
+            int32_t bq = j0 < q_hi ? find(sQ, j0) : 0;
             #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < q_hi) {
-                    const int32_t b = find(sQ, i);
-                    pos[u] = sLen[b] - (sQ[b + 1] - sQ[b]) + (i - sQ[b]);
-                    pg[u] = a.page_table[(int64_t)b * a.pt_stride + (pos[u] >> a.page_shift)];
+                const int32_t i = i0 + u;
+                if (i < p_hi) {
+                    while (sP[bp + 1] <= i) ++bp;
+                    pg[u] = a.page_table[(int64_t)bp * a.pt_stride + (i - sP[bp])];
+                }
+                const int32_t jq = j0 + u;
+                if (jq < q_hi) {
+                    while (sQ[bq + 1] <= jq) ++bq;
+                    pos[u] = sLen[bq] - (sQ[bq + 1] - sQ[bq]) + (jq - sQ[bq]);
+                    qpg[u] = a.page_table[(int64_t)bq * a.pt_stride + (pos[u] >> a.page_shift)];
                 }
             }
             #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int32_t i = i0 + u * SCAN_THREADS;
-                if (i < q_hi) {
-                    if (pg[u] < 0 || pg[u] >= a.num_pages) {
-                        flags |= PKA_DEV_BAD_PAGE;
-                        pg[u] = min(max(pg[u], 0), a.num_pages - 1);
-                    }
-                    a.out_cache_loc[i] = (pg[u] << a.page_shift) | (pos[u] & (P - 1));
-                }
+                if (i0 + u < p_hi) a.kv_indices[i0 + u] = clamp_page(pg[u]);
+                if (j0 + u < q_hi)
+                    a.out_cache_loc[j0 + u] = (clamp_page(qpg[u]) << a.page_shift) | (pos[u] & (P - 1));
             }
         }
     }
@@ -363,9 +355,10 @@ hipError_t launch_metadata(const MetaArgs& a, hipStream_t s) {
     // lookups of each kind
     int nblk = 1;
     if (a.fuse_gather) {
+        // the lead workgroup, plus the gather slices
         const int64_t items = std::max<int64_t>(a.max_kv_pages, a.N);
-        nblk = (int)std::min<int64_t>(MD_SLOTS, std::max<int64_t>(1, (items + SCAN_THREADS * FUSE_PER_THREAD - 1) /
-                                                                      (SCAN_THREADS * FUSE_PER_THREAD)));
+        const int64_t per = (int64_t)SCAN_THREADS * FUSE_PER_THREAD;
+        nblk = (int)std::min<int64_t>(MD_SLOTS, 1 + (items + per - 1) / per);
     }
     hipLaunchKernelGGL(md_scan_kernel, dim3(nblk), dim3(SCAN_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();

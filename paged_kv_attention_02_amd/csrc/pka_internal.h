@@ -80,7 +80,7 @@ struct MetaArgs {
     int64_t max_kv_pages;
     int32_t page_shift;
     int32_t num_pages;
-    int32_t nwg;       // decode workgroups
+    int32_t nwg;       // decode shares
     int32_t ext_tq;    // extend query tokens per item
     int32_t is_decode;
     int32_t fuse_gather;  // B <= FUSE_MAX_B: md_scan also writes kv_indices / out_cache_loc
