@@ -183,10 +183,11 @@ pka_status pka_save_kv(const pka_ctx* ctx, const pka_batch* md, const void* k_ne
  * verify pass sent down the decode path, "[SGLang] Hybrid Attention",
  * section on _select_backend), each request carries n_b = extend_lens[b]
  * query rows (0 <= n_b <= 16); row i sits at position L_b - n_b + i and sees
- * keys 0 .. L_b - n_b + i, the cache being read once for all of them.  Rows
- * of a request with n_b > 16 beyond the 16th are not computed and
+ * keys 0 .. L_b - n_b + i, the cache being read once per 16 (row, query
+ * head) pairs of a KV head (once for all rows when n_b * G <= 16).  Rows of
+ * a request with n_b > 16 beyond the 16th are not computed and
  * PKA_DEV_BAD_LENGTH is raised.  The workspace then holds up to 16 partial
- * rows per (request, workgroup): pka_batch_sizes sizes it by mode. */
+ * rows per (request, share of the split): pka_batch_sizes sizes it by mode. */
 pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* q,
                            const void* k_pool, const void* v_pool, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);
