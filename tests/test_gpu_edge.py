@@ -101,6 +101,17 @@ def test_extend_page_sizes(P):
     run_and_check(BASE_EXT.replace(page_size=P))
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("P", [2, 32, 256])
+def test_other_page_sizes(P, kv):
+    """Page sizes outside the workloads' (2, 32, 256): decode (pages smaller
+    than, equal to and larger than a 32-token tile) and extend (pages
+    smaller and larger than a 64-key tile)."""
+    run_and_check(BASE_DEC.replace(batch=7, page_size=P, kv_dtype=kv, seq_len_kind="uniform",
+                                   seq_len_args=(1, 900), seed=29))
+    run_and_check(BASE_EXT.replace(page_size=P, kv_dtype=kv, seed=30))
+
+
 def test_extend_ragged_new_and_prefix():
     lens_new = [1, 0, 33, 64, 65, 130, 7]
     prefix = [0, 5, 0, 63, 64, 1, 300]
