@@ -280,6 +280,7 @@ def bench_verify(spec, iters: int, warm: int = 10):
         ms = time_events(call, iters, warm=warm)
         out[path] = {"ms": round(ms, 4), "kv_read_GBps": round(kvb / ms / 1e6, 1),
                      "frac_hbm_peak": round(kvb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    out["metadata_ms"] = round(time_events(lambda i: probs[i % 2].metadata_step(), iters, warm=warm), 4)
     for p in probs:
         assert p.md.status() == 0, "device status flags set"
     del probs
@@ -351,6 +352,7 @@ def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16", spe
            "TFLOPs": round(tf, 1), "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
            "frac_mfma_peak": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
            "ms_per_call": time_per_call(call, iters), "warmup_calls": warm,
+           "metadata_ms": round(time_events(lambda i: prob.metadata_step(), iters), 4),
            "variant": f"extend_mfma_kernel<Dk {spec.head_dim}, Dv {spec.value_dim}, scale>0, "
                       f"page {spec.page_size}{' >= 64' if spec.page_size >= 64 else ' < 64'}, "
                       f"{spec.kv_dtype} cache>"}

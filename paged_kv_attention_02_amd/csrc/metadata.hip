@@ -240,21 +240,51 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         __shared__ int32_t s_count;
         if (t == 0) s_count = 0;
         __syncthreads();
-        // pass 1: count (serial over requests in chunks, tiles in parallel)
-        for (int32_t b = 0; b < a.B; ++b) {
-            const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
-            const int32_t tiles = (q1 - q0 + tq - 1) / tq;
-            for (int32_t i = t; i < tiles; i += SCAN_THREADS) {
-                const int32_t slot = s_count + i;
-                if (slot < cap) {
-                    items[2 * slot] = b;
-                    items[2 * slot + 1] = i;
-                }
+        if (a.B <= FUSE_MAX_B) {
+            // pass 1: every request's first item (exclusive prefix of its
+            // tile count, from the LDS query prefix), then the items filled
+            // in parallel, each finding its request by binary search
+            __shared__ int32_t sI[FUSE_MAX_B + 1];
+            for (int32_t base = 0; base < a.B; base += SCAN_THREADS) {
+                const int32_t b = base + t;
+                int64_t x[1] = {b < a.B ? (sQ[b + 1] - sQ[b] + tq - 1) / tq : 0};
+                const int64_t own = x[0];
+                block_scan<1>(x, sh);
+                if (b < a.B) sI[b] = s_count + (int32_t)(x[0] - own);
+                __syncthreads();
+                if (t == SCAN_THREADS - 1) s_count += (int32_t)x[0];
+                __syncthreads();
             }
+            if (t == 0) sI[a.B] = s_count;
             __syncthreads();
-            if (t == 0) s_count += tiles;
-            __syncthreads();
+            const int32_t total = (int32_t)min((int64_t)s_count, cap);
+            for (int32_t slot = t; slot < total; slot += SCAN_THREADS) {
+                int32_t lo = 0, hi = a.B - 1;  // largest b with sI[b] <= slot
+                while (lo < hi) {
+                    const int32_t mid = (lo + hi + 1) >> 1;
+                    if (sI[mid] <= slot) lo = mid; else hi = mid - 1;
+                }
+                items[2 * slot] = lo;
+                items[2 * slot + 1] = slot - sI[lo];
+            }
+        } else {
+            // pass 1 for large batches: serial over requests, tiles in parallel
+            for (int32_t b = 0; b < a.B; ++b) {
+                const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
+                const int32_t tiles = (q1 - q0 + tq - 1) / tq;
+                for (int32_t i = t; i < tiles; i += SCAN_THREADS) {
+                    const int32_t slot = s_count + i;
+                    if (slot < cap) {
+                        items[2 * slot] = b;
+                        items[2 * slot + 1] = i;
+                    }
+                }
+                __syncthreads();
+                if (t == 0) s_count += tiles;
+                __syncthreads();
+            }
         }
+        __syncthreads();
         int32_t count = s_count;
         if (count > cap) { flags |= PKA_DEV_CAPACITY; count = (int32_t)cap; }
         // sort by weight (descending) with a bitonic sort in LDS when small
