@@ -13,6 +13,8 @@
  *                      up to 16 causal query tokens for speculative verify)
  *   pka_attn_extend    a causal block of new tokens against prefix + itself
  *   pka_forward        ForwardMode-keyed dispatch between the two paths
+ *   pka_forward_with_metadata  metadata + forward in one call (one decode
+ *                      launch builds both for bf16 / fp8 decode batches)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -218,6 +220,27 @@ pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_
                        const pka_batch* md, const void* q, const void* k_new, const void* v_new,
                        int save_kv, void* k_pool, void* v_pool, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* pka_init_metadata followed by pka_forward, as one call: builds the batch's
+ * metadata into md from seq_lens / extend_lens / page_table (same arguments
+ * and results as pka_init_metadata) and runs the forward pass on it (same
+ * arguments and results as pka_forward).  The pages build the metadata once
+ * per batch and then run the forward ("sglang-101 s4.2 --attention-backend",
+ * section "What an attention backend is"); for a DECODE batch with a bf16 or
+ * fp8 cache and at most 512 requests both happen in the decode launch
+ * itself: every workgroup scans seq_lens and reads page ids straight from
+ * the page table, and the metadata arrays are written on the side, bit-equal
+ * to what pka_init_metadata writes (two launches: decode, merge).  Other
+ * batches launch pka_init_metadata's kernels, then pka_forward's.  All
+ * arguments are checked before anything is enqueued; on error nothing is. */
+pka_status pka_forward_with_metadata(const pka_ctx* ctx, pka_forward_mode mode,
+                                     pka_spec_attn_mode spec_mode, const int32_t* seq_lens,
+                                     const int32_t* extend_lens, const int32_t* page_table,
+                                     int32_t page_table_stride, int32_t page_table_cols,
+                                     pka_batch* md, const void* q, const void* k_new,
+                                     const void* v_new, int save_kv, void* k_pool, void* v_pool,
+                                     void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Synchronise `stream` and read the sticky device status word of a batch:
  * 0 = clean, else a bitwise OR of PKA_DEV_* flags. */

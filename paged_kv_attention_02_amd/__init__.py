@@ -81,6 +81,9 @@ SIGNATURES = {
     "pka_select_path": (ctypes.c_int, [ctypes.c_int, ctypes.c_int]),
     "pka_forward": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, ctypes.POINTER(BatchStruct),
                                    _VP, _VP, _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "pka_forward_with_metadata": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, _VP, _VP, _VP, _I32,
+                                                 _I32, ctypes.POINTER(BatchStruct), _VP, _VP, _VP,
+                                                 ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "pka_read_status": (ctypes.c_int, [ctypes.POINTER(BatchStruct), ctypes.POINTER(_I32), _VP]),
     "pka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pka_last_error": (ctypes.c_char_p, []),
@@ -201,9 +204,7 @@ class Batch:
     def num_q_tokens(self) -> int:
         return self.s.num_q_tokens
 
-    def init(self, seq_lens, extend_lens, page_table, stream=None):
-        """Build the index buffers from device int32 seq_lens [B], extend_lens
-        [B] (None for decode) and page_table [B, cols] (row stride >= cols)."""
+    def _check_inputs(self, seq_lens, extend_lens, page_table):
         import torch
         for name, t in (("seq_lens", seq_lens), ("extend_lens", extend_lens),
                         ("page_table", page_table)):
@@ -214,6 +215,11 @@ class Batch:
         if seq_lens.numel() != self.batch or page_table.shape[0] != self.batch:
             raise ValueError("seq_lens / page_table rows must match the batch size")
         self._keep = (seq_lens, extend_lens, page_table)
+
+    def init(self, seq_lens, extend_lens, page_table, stream=None):
+        """Build the index buffers from device int32 seq_lens [B], extend_lens
+        [B] (None for decode) and page_table [B, cols] (row stride >= cols)."""
+        self._check_inputs(seq_lens, extend_lens, page_table)
         _check(lib().pka_init_metadata(self.ctx.handle, seq_lens.data_ptr(), _ptr(extend_lens),
                                        page_table.data_ptr(), page_table.stride(0),
                                        page_table.shape[1], ctypes.byref(self.s), _stream(stream)))
@@ -295,3 +301,24 @@ def forward(ctx: Context, mode: str, md: Batch, q, k_new, v_new, k_pool, v_pool,
                              _ptr(q), _ptr(k_new), _ptr(v_new), int(bool(save_kv_cache)),
                              _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), wp, wb,
                              _stream(stream)))
+
+
+def forward_with_metadata(ctx: Context, mode: str, md: Batch, seq_lens, extend_lens, page_table, q,
+                          k_new, v_new, k_pool, v_pool, out, lse=None, save_kv_cache: bool = True,
+                          spec_mode: str = "prefill", workspace=None, stream=None):
+    """md.init(seq_lens, extend_lens, page_table) followed by forward(...), as
+    one library call (one decode launch builds both for bf16 / fp8 decode
+    batches)."""
+    if mode != "idle":
+        md._check_inputs(seq_lens, extend_lens, page_table)
+        _attn_common(ctx, md, q, k_pool, v_pool, out, lse)
+        if save_kv_cache:
+            _check_rows(ctx, k_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "k_new")
+            _check_rows(ctx, v_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "v_new", value=True)
+    wp, wb = _ws(md.workspace if workspace is None else workspace)
+    _check(lib().pka_forward_with_metadata(
+        ctx.handle, MODES[mode], SPEC_MODES[spec_mode], _ptr(seq_lens), _ptr(extend_lens),
+        _ptr(page_table), 0 if page_table is None else page_table.stride(0),
+        0 if page_table is None else page_table.shape[1], ctypes.byref(md.s), _ptr(q), _ptr(k_new),
+        _ptr(v_new), int(bool(save_kv_cache)), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), wp,
+        wb, _stream(stream)))

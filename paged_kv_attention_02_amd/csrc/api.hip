@@ -26,6 +26,7 @@ struct pka_ctx {
     int32_t ext_tq;      // extend query tokens per work item
     std::atomic<int32_t> nwg{0};  // decode shares (from the device's CU count)
     std::atomic<int32_t> spw{0};  // decode shares per workgroup
+    std::atomic<int32_t> md_fits{-1};  // decode with in-kernel metadata keeps the occupancy (-1: unknown)
 };
 
 namespace {
@@ -169,15 +170,15 @@ pka_status check_attn(const pka_ctx* ctx, const pka_batch* md, const void* q, co
 }
 
 
-// Decode launch; with write_new the new tokens k_new / v_new are written by
-// the decode kernel itself (bf16 and fp8 caches).
-pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, const void* k_pool,
+// Validated arguments of a decode launch (nothing is enqueued); with
+// write_new the new tokens k_new / v_new are written by the decode kernel
+// itself (bf16 and fp8 caches).  The caller skips idle and empty batches.
+pka_status decode_args(const pka_ctx* ctx, const pka_batch* md, const void* q, const void* k_pool,
                        const void* v_pool, void* out, float* lse, void* workspace,
-                       size_t workspace_bytes, void* stream, bool write_new, const void* k_new,
-                       const void* v_new) {
+                       size_t workspace_bytes, bool write_new, const void* k_new, const void* v_new,
+                       pka::AttnArgs* args) {
     pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
     if (s != PKA_OK) return s;
-    if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
     if (write_new && (!k_new || !v_new)) return fail(PKA_ERR_INVALID_ARG, "null K/V pointer");
     if (write_new && (!aligned16(k_new) || !aligned16(v_new)))
         return fail(PKA_ERR_INVALID_ARG, "K/V rows must be 16-byte aligned");
@@ -205,9 +206,112 @@ pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, c
         a.k_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f);
         a.v_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f);
     }
+    *args = a;
+    return PKA_OK;
+}
+
+pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, const void* k_pool,
+                       const void* v_pool, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream, bool write_new, const void* k_new,
+                       const void* v_new) {
+    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
+    if (s != PKA_OK) return s;
+    if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
+    pka::AttnArgs a;
+    if ((s = decode_args(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, write_new,
+                         k_new, v_new, &a)) != PKA_OK)
+        return s;
     hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
                                       decode_wpb(ctx), (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
+}
+
+// Validated metadata arguments (nothing is enqueued); the caller skips idle
+// and empty batches.
+pka_status meta_args(const pka_ctx* ctx, const int32_t* seq_lens, const int32_t* extend_lens,
+                     const int32_t* page_table, int32_t page_table_stride, int32_t page_table_cols,
+                     const pka_batch* md, pka::MetaArgs* out) {
+    pka_status s = check_batch(ctx, md);
+    if (s != PKA_OK) return s;
+    if (!seq_lens || !page_table) return fail(PKA_ERR_INVALID_ARG, "null seq_lens or page_table");
+    if (md->mode != PKA_MODE_DECODE && !extend_lens)
+        return fail(PKA_ERR_INVALID_ARG, "extend-like batches need extend_lens");
+    if (page_table_cols < 1 || page_table_stride < page_table_cols)
+        return fail(PKA_ERR_INVALID_ARG, "page table stride %d / cols %d", page_table_stride, page_table_cols);
+    pka::MetaArgs a{};
+    a.seq_lens = seq_lens;
+    a.extend_lens = md->mode == PKA_MODE_DECODE ? nullptr : extend_lens;
+    a.page_table = page_table;
+    a.pt_stride = page_table_stride;
+    a.pt_cols = page_table_cols;
+    a.B = md->batch;
+    a.N = md->num_q_tokens;
+    a.max_kv_pages = md->max_kv_pages;
+    a.page_shift = ctx->page_shift;
+    a.num_pages = ctx->cfg.num_pages;
+    int32_t nwg = 0;
+    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+    a.nwg = nwg;
+    a.ext_tq = ctx->ext_tq;
+    a.is_decode = md->mode == PKA_MODE_DECODE;
+    a.fuse_gather = md->batch <= pka::FUSE_MAX_B && md->max_kv_pages <= pka::FUSE_MAX_ITEMS &&
+                    md->num_q_tokens <= pka::FUSE_MAX_ITEMS;
+    a.kv_indptr = md->kv_indptr;
+    a.kv_indices = md->kv_indices;
+    a.kv_last_page_len = md->kv_last_page_len;
+    a.qo_indptr = md->qo_indptr;
+    a.out_cache_loc = md->out_cache_loc;
+    a.plan = md->plan;
+    *out = a;
+    return PKA_OK;
+}
+
+// Checks of pka_forward that need no launch: modes, buffers, the metadata's
+// mode, the decode workspace and the new K/V rows.  Sets *path.
+pka_status forward_checks(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
+                          const pka_batch* md, const void* q, const void* k_new, const void* v_new,
+                          int save_kv, void* k_pool, void* v_pool, void* out, void* workspace,
+                          size_t workspace_bytes, pka_path* path) {
+    if (mode < PKA_MODE_EXTEND || mode > PKA_MODE_DRAFT_EXTEND)
+        return fail(PKA_ERR_INVALID_ARG, "unknown forward mode %d", (int)mode);
+    if (spec_mode != PKA_SPEC_PREFILL && spec_mode != PKA_SPEC_DECODE)
+        return fail(PKA_ERR_INVALID_ARG, "unknown speculative attention mode %d", (int)spec_mode);
+    *path = pka_select_path(mode, spec_mode);
+    if (*path == PKA_PATH_NONE) return PKA_OK;
+    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
+    if (s != PKA_OK) return s;
+    if (md->mode != mode)
+        return fail(PKA_ERR_INVALID_ARG, "metadata was built for mode %d, forward called with %d",
+                    (int)md->mode, (int)mode);
+    if (*path == PKA_PATH_DECODE) {
+        int32_t nwg = 0;
+        if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+        if (!workspace ||
+            (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg, decode_qslots(md->mode, md->num_q_tokens)))
+            return fail(PKA_ERR_WORKSPACE, "decode workspace too small");
+    }
+    if (save_kv && md->num_q_tokens > 0) {
+        if (!k_new || !v_new) return fail(PKA_ERR_INVALID_ARG, "null K/V pointer");
+        if (!aligned16(k_new) || !aligned16(v_new))
+            return fail(PKA_ERR_INVALID_ARG, "K/V rows must be 16-byte aligned");
+    }
+    return PKA_OK;
+}
+
+// Whether a decode batch can build its metadata inside the decode kernel:
+// bf16 / fp8 cache, at most DEC_MD_MAX_B requests, and the kernel keeps the
+// plain decode kernel's occupancy (the partition assumes one resident round).
+bool decode_md_ok(const pka_ctx* ctx, const pka_batch* md) {
+    if (ctx->cfg.kv_dtype == PKA_F32 || md->mode != PKA_MODE_DECODE || md->batch > pka::DEC_MD_MAX_B)
+        return false;
+    int32_t v = ctx->md_fits.load(std::memory_order_acquire);
+    if (v < 0) {
+        int32_t nwg = 0, spw = 1;
+        if (decode_wgs(ctx, &nwg, &spw) != PKA_OK) return false;
+        v = pka::decode_md_fits(ctx->cfg.kv_dtype, ctx->dk, ctx->dv, decode_wpb(ctx) * spw) ? 1 : 0;
+        const_cast<pka_ctx*>(ctx)->md_fits.store(v, std::memory_order_release);
+    }
+    return v == 1;
 }
 
 }  // namespace
@@ -317,35 +421,10 @@ pka_status pka_init_metadata(const pka_ctx* ctx, const int32_t* seq_lens,
     pka_status s = check_batch(ctx, md);
     if (s != PKA_OK) return s;
     if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
-    if (!seq_lens || !page_table) return fail(PKA_ERR_INVALID_ARG, "null seq_lens or page_table");
-    if (md->mode != PKA_MODE_DECODE && !extend_lens)
-        return fail(PKA_ERR_INVALID_ARG, "extend-like batches need extend_lens");
-    if (page_table_cols < 1 || page_table_stride < page_table_cols)
-        return fail(PKA_ERR_INVALID_ARG, "page table stride %d / cols %d", page_table_stride, page_table_cols);
-    pka::MetaArgs a{};
-    a.seq_lens = seq_lens;
-    a.extend_lens = md->mode == PKA_MODE_DECODE ? nullptr : extend_lens;
-    a.page_table = page_table;
-    a.pt_stride = page_table_stride;
-    a.pt_cols = page_table_cols;
-    a.B = md->batch;
-    a.N = md->num_q_tokens;
-    a.max_kv_pages = md->max_kv_pages;
-    a.page_shift = ctx->page_shift;
-    a.num_pages = ctx->cfg.num_pages;
-    int32_t nwg = 0;
-    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
-    a.nwg = nwg;
-    a.ext_tq = ctx->ext_tq;
-    a.is_decode = md->mode == PKA_MODE_DECODE;
-    a.fuse_gather = md->batch <= pka::FUSE_MAX_B && md->max_kv_pages <= pka::FUSE_MAX_ITEMS &&
-                    md->num_q_tokens <= pka::FUSE_MAX_ITEMS;
-    a.kv_indptr = md->kv_indptr;
-    a.kv_indices = md->kv_indices;
-    a.kv_last_page_len = md->kv_last_page_len;
-    a.qo_indptr = md->qo_indptr;
-    a.out_cache_loc = md->out_cache_loc;
-    a.plan = md->plan;
+    pka::MetaArgs a;
+    if ((s = meta_args(ctx, seq_lens, extend_lens, page_table, page_table_stride, page_table_cols, md,
+                       &a)) != PKA_OK)
+        return s;
     hipError_t e = pka::launch_metadata(a, (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "metadata launch");
 }
@@ -413,24 +492,11 @@ pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_
                        const pka_batch* md, const void* q, const void* k_new, const void* v_new,
                        int save_kv, void* k_pool, void* v_pool, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream) {
-    if (mode < PKA_MODE_EXTEND || mode > PKA_MODE_DRAFT_EXTEND)
-        return fail(PKA_ERR_INVALID_ARG, "unknown forward mode %d", (int)mode);
-    if (spec_mode != PKA_SPEC_PREFILL && spec_mode != PKA_SPEC_DECODE)
-        return fail(PKA_ERR_INVALID_ARG, "unknown speculative attention mode %d", (int)spec_mode);
-    const pka_path path = pka_select_path(mode, spec_mode);
-    if (path == PKA_PATH_NONE) return PKA_OK;
-    pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
-    if (s != PKA_OK) return s;
-    if (md->mode != mode)
-        return fail(PKA_ERR_INVALID_ARG, "metadata was built for mode %d, forward called with %d",
-                    (int)md->mode, (int)mode);
-    if (path == PKA_PATH_DECODE) {  // check the workspace before anything is enqueued
-        int32_t nwg = 0;
-        if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
-        if (!workspace ||
-            (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg, decode_qslots(md->mode, md->num_q_tokens)))
-            return fail(PKA_ERR_WORKSPACE, "decode workspace too small");
-    }
+    // everything is checked before anything is enqueued
+    pka_path path;
+    pka_status s = forward_checks(ctx, mode, spec_mode, md, q, k_new, v_new, save_kv, k_pool, v_pool,
+                                  out, workspace, workspace_bytes, &path);
+    if (s != PKA_OK || path == PKA_PATH_NONE) return s;
     // bf16 / fp8 decode writes the new tokens inside the decode kernel (one
     // launch less); other paths (and verify batches on the decode path) write
     // them first with the save_kv kernel
@@ -446,14 +512,58 @@ pka_status pka_forward(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_
     return pka_attn_extend(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, stream);
 }
 
+pka_status pka_forward_with_metadata(const pka_ctx* ctx, pka_forward_mode mode,
+                                     pka_spec_attn_mode spec_mode, const int32_t* seq_lens,
+                                     const int32_t* extend_lens, const int32_t* page_table,
+                                     int32_t page_table_stride, int32_t page_table_cols,
+                                     pka_batch* md, const void* q, const void* k_new,
+                                     const void* v_new, int save_kv, void* k_pool, void* v_pool,
+                                     void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    pka_path path;
+    pka_status s = forward_checks(ctx, mode, spec_mode, md, q, k_new, v_new, save_kv, k_pool, v_pool,
+                                  out, workspace, workspace_bytes, &path);
+    if (s != PKA_OK || path == PKA_PATH_NONE) return s;
+    if (md->batch == 0) return PKA_OK;
+    pka::MetaArgs m;
+    if ((s = meta_args(ctx, seq_lens, extend_lens, page_table, page_table_stride, page_table_cols, md,
+                       &m)) != PKA_OK)
+        return s;
+    if (path == PKA_PATH_DECODE && decode_md_ok(ctx, md)) {
+        // one decode launch builds the metadata, writes the new tokens and
+        // attends; then the merge
+        pka::AttnArgs a;
+        if ((s = decode_args(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, save_kv != 0,
+                             k_new, v_new, &a)) != PKA_OK)
+            return s;
+        hipError_t e = pka::launch_decode_md(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a, m,
+                                             decode_wpb(ctx), (hipStream_t)stream);
+        return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
+    }
+    hipError_t e = pka::launch_metadata(m, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "metadata launch");
+    return pka_forward(ctx, mode, spec_mode, md, q, k_new, v_new, save_kv, k_pool, v_pool, out, lse,
+                       workspace, workspace_bytes, stream);
+}
+
 pka_status pka_read_status(const pka_batch* md, int32_t* status, void* stream) {
     if (!md || !status || !md->plan) return fail(PKA_ERR_INVALID_ARG, "null batch or status");
+    if (md->batch < 0) return fail(PKA_ERR_INVALID_ARG, "negative batch size");
     int32_t words[pka::PLAN_MDST + pka::MD_SLOTS];
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     if (e == hipSuccess) e = hipMemcpy(words, md->plan, sizeof words, hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "reading the status words");
     int32_t v = words[pka::PLAN_STATUS];
     for (int i = 0; i < pka::MD_SLOTS; ++i) v |= words[pka::PLAN_MDST + i];
+    // the per-share page flags of the partition the plan was last built for
+    const int32_t nwg = std::min<int32_t>(std::max<int32_t>(words[pka::PLAN_NWG], 0), pka::DEC_MAX_WG);
+    if (nwg > 0 && md->batch > 0) {
+        int32_t share[pka::DEC_MAX_WG];
+        e = hipMemcpy(share, md->plan + pka::plan_share_flags(md->batch), nwg * sizeof(int32_t),
+                      hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(e, "reading the status words");
+        for (int i = 0; i < nwg; ++i) v |= share[i];
+    }
     *status = v;
     return PKA_OK;
 }

@@ -82,13 +82,13 @@ __device__ inline void emit_rows(const f32x4_t (&O)[D / 16], float inv, int j, E
     emit(v, 4 * CPL * j);
 }
 
-// Cache write of one request's new token for KV head g, fused into decode:
-// K on lanes 0..31, V on lanes 32..63, 8 elements per lane (bf16 copy or
-// bf16 -> fp8 quantisation).  The store is waited for before the wave reads
-// the pool, so the wave's own later load of that slot sees it.
+// Cache write of one request's new token (query row qr, pool slot `slot`)
+// for KV head g, fused into decode: K on lanes 0..31, V on lanes 32..63, 8
+// elements per lane (bf16 copy or bf16 -> fp8 quantisation).  The store is
+// waited for before the wave reads the pool, so the wave's own later load of
+// that slot sees it.
 template <int DK, int DV, bool FP8>
-__device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int g, int lane) {
-    const int32_t slot = a.out_cache_loc[qr];
+__device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int32_t slot, int g, int lane) {
     if (slot < 0 || slot >= a.pool_slots) {
         if (lane == 0) atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_PAGE);
         return;
@@ -303,13 +303,134 @@ __device__ inline void tile_update(const VTile<DK, DV, FP8>& T, const f32x4_t (&
     }
 }
 
+// LDS of a decode kernel that builds its own metadata, after the waves'
+// regions: the page, token and tile prefixes of the batch ([B + 1] int32
+// each), the scan's wave totals and one flag word.
+__host__ __device__ inline size_t md_prefix_bytes(int32_t B) { return ((3 * ((size_t)B + 1) * 4 + 7) / 8) * 8; }
+__host__ __device__ inline size_t md_lds_bytes(int32_t B) { return md_prefix_bytes(B) + 3 * 8 * 8 + 8; }
+
+// Per-request prefixes of a decode batch, built by the whole workgroup into
+// LDS from the clamped lengths (the same clamping and sums as the metadata
+// kernel, so the partition and every page id agree with it): sP = pages
+// (kv_indptr), sF = tokens, sT = decode tiles, each [B + 1] from 0.  Returns
+// the tile total and the OR of the clamping flags in every thread.
+__device__ inline void md_prefixes(const MetaArgs& m, uint8_t* base, int64_t& W, int32_t& flags_out) {
+    int32_t* const sP = (int32_t*)base;
+    int32_t* const sF = sP + (m.B + 1);
+    int32_t* const sT = sF + (m.B + 1);
+    int64_t* const wsum = (int64_t*)(base + md_prefix_bytes(m.B));  // [3][8]
+    int32_t* const sflag = (int32_t*)(wsum + 24);
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6, nw = blockDim.x >> 6;
+    if (t == 0) {
+        sP[0] = sF[0] = sT[0] = 0;
+        *sflag = 0;
+    }
+    int64_t carry[3] = {0, 0, 0};
+    int32_t flags = 0;
+    for (int32_t b0 = 0; b0 < m.B; b0 += blockDim.x) {
+        const int32_t b = b0 + t;
+        int64_t x[3] = {0, 0, 0};  // pages, tokens, tiles
+        if (b < m.B) {
+            int64_t L = m.seq_lens[b], n = 1, pages = 0;
+            flags |= md_clamp_request(L, n, pages, m.page_shift, m.pt_cols);
+            x[0] = pages;
+            x[1] = L;
+            x[2] = (L + DEC_TILE - 1) / DEC_TILE;
+        }
+        #pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int64_t y[3];
+            #pragma unroll
+            for (int v = 0; v < 3; ++v) y[v] = __shfl_up(x[v], off);
+            if (lane >= off) {
+                #pragma unroll
+                for (int v = 0; v < 3; ++v) x[v] += y[v];
+            }
+        }
+        if (lane == 63) {
+            #pragma unroll
+            for (int v = 0; v < 3; ++v) wsum[8 * v + wv] = x[v];
+        }
+        __syncthreads();
+        int64_t before[3] = {carry[0], carry[1], carry[2]};
+        for (int k = 0; k < nw; ++k) {
+            #pragma unroll
+            for (int v = 0; v < 3; ++v) {
+                const int64_t s = wsum[8 * v + k];
+                if (k < wv) before[v] += s;
+                carry[v] += s;
+            }
+        }
+        if (b < m.B) {
+            const int64_t cp = before[0] + x[0], cL = before[1] + x[1], cT = before[2] + x[2];
+            if (cp > m.max_kv_pages || cL > INT32_MAX) flags |= PKA_DEV_CAPACITY;
+            sP[b + 1] = (int32_t)min(cp, (int64_t)INT32_MAX);
+            sF[b + 1] = (int32_t)min(cL, (int64_t)INT32_MAX);
+            sT[b + 1] = (int32_t)min(cT, (int64_t)INT32_MAX);
+        }
+        __syncthreads();  // the wave totals are rewritten next round
+    }
+    if (flags) atomicOr(sflag, flags);
+    __syncthreads();
+    flags_out = *sflag;
+    W = min(carry[2], (int64_t)INT32_MAX);
+}
+
+// The batch-wide metadata outputs, written by one wave from its workgroup's
+// LDS prefixes: kv_indptr, qo_indptr (request b's query row is b),
+// kv_last_page_len, the plan's prefixes and partition words, and the status
+// words (clamping flags; the per-share page flags are written by the shares).
+__device__ inline void md_write_batch(const MetaArgs& m, const uint8_t* base, int64_t W, int32_t flags) {
+    const int32_t* const sP = (const int32_t*)base;
+    const int32_t* const sF = sP + (m.B + 1);
+    const int32_t* const sT = sF + (m.B + 1);
+    int32_t* const F = m.plan + plan_seg_prefix(m.B);
+    int32_t* const T = m.plan + plan_tile_prefix(m.B);
+    const int lane = threadIdx.x & 63;
+    for (int32_t b = lane; b <= m.B; b += 64) {
+        m.kv_indptr[b] = sP[b];
+        m.qo_indptr[b] = b;
+        F[b] = sF[b];
+        T[b] = sT[b];
+        if (b < m.B) {
+            const int32_t L = sF[b + 1] - sF[b], pages = sP[b + 1] - sP[b];
+            m.kv_last_page_len[b] = L - ((pages - 1) << m.page_shift);
+        }
+    }
+    for (int i = lane; i < MD_SLOTS; i += 64) m.plan[PLAN_MDST + i] = i == 0 ? flags : 0;
+    if (lane == 0) {
+        int64_t q, r;
+        decode_shares(W, m.nwg, q, r);
+        m.plan[PLAN_STATUS] = 0;
+        m.plan[PLAN_SHARE] = (int32_t)q;
+        m.plan[PLAN_SHARE_REM] = (int32_t)r;
+        m.plan[PLAN_TOTAL] = (int32_t)W;
+        m.plan[PLAN_NWG] = m.nwg;
+        m.plan[PLAN_EXT_COUNT] = 0;
+        m.plan[PLAN_EXT_TQ] = m.ext_tq;
+    }
+}
+
+typedef __attribute__((address_space(3))) const int32_t lds_i32_t;
+
 // MQ: several query tokens per request (speculative verify on the decode
 // path).  Columns are then (query token i, head h) pairs of the request, 16
 // per pass of the wave over its share; token i of a request with n query
 // tokens sits at position L - n + i and sees keys 0 .. L - n + i.  Partials
 // of token i go to slot (b + w) * qslots + i.
-template <int DK, int DV, bool FP8, bool MQ>
-__global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
+//
+// MD: the kernel builds the batch's metadata itself (decode batches of at
+// most DEC_MD_MAX_B requests, m set).  Every workgroup scans the lengths into
+// LDS and its waves read page ids straight from the page table; workgroup 0
+// writes the batch-wide arrays, and the wave of each share that serves unit 0
+// writes the share's first request and its page flags (kv_indices and the
+// new tokens' slots are left to the merge, so no store waits in the tile
+// stream: stores count in vmcnt like loads).  The partition and the page ids
+// are those the metadata kernel would produce, so the outputs are
+// bit-identical to running it first.
+template <int DK, int DV, bool FP8, bool MQ, bool MD>
+__global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m) {
+    static_assert(!(MQ && MD), "metadata is built in-kernel for one query per request only");
     using S = DecodeShape<DK, DV, FP8>;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, j = lane >> 4;
@@ -339,22 +460,93 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     const bool pair = waves == 8;
     int32_t nst = 0;  // tiles computed so far
     if (pair) __hip_atomic_store(prog + wv, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // MD: the metadata area, 8-byte aligned after the progress words
+    uint8_t* const md_lds = dec_lds + ((waves * (S::WAVE_LDS + 4) + 7) & ~7);
+    int64_t W_md = 0;
+    int32_t len_flags = 0;
+    if constexpr (MD) md_prefixes(m, md_lds, W_md, len_flags);
+    lds_i32_t* const sP = (lds_i32_t*)md_lds;  // MD: the LDS prefixes
+    lds_i32_t* const sF = sP + (a.B + 1);
+    lds_i32_t* const sT = sF + (a.B + 1);
     if (g >= a.Hkv) return;
 
     const int32_t* plan = a.plan;
     const int32_t w = blockIdx.x * a.spw + wv / wpb;
-    const int32_t nwg = plan[PLAN_NWG];
+    const int32_t nwg = MD ? a.nwg : plan[PLAN_NWG];
     if (w >= nwg) return;
     // this wave's share: tiles [start, end) of the requests' tiles laid end
     // to end
-    const int64_t shq = plan[PLAN_SHARE], shr = plan[PLAN_SHARE_REM];
-    const int64_t W = plan[PLAN_TOTAL];
+    int64_t shq, shr, W;
+    if constexpr (MD) {
+        W = W_md;
+        decode_shares(W, nwg, shq, shr);
+    } else {
+        shq = plan[PLAN_SHARE];
+        shr = plan[PLAN_SHARE_REM];
+        W = plan[PLAN_TOTAL];
+    }
     const int64_t start = share_start(w, shq, shr);
-    if (start >= W) return;
+    // MD: the wave of unit 0 records its share (first request, page flags)
+    // and wave 0 of workgroup 0 the batch-wide arrays, as each wave leaves:
+    // nothing in this launch reads them, and a store issued earlier would
+    // hold up the next vmcnt wait for a tile
+    const bool md_rec = MD && unit == 0;
+    int32_t pflags = 0;  // MD: a page id outside the pool was clamped
+    int32_t seg;
+    auto md_close = [&]() {
+        if (md_rec) {
+            const bool bad = __ballot(pflags != 0) != 0;
+            if (lane == 0) {
+                m.plan[plan_share_flags(a.B) + w] = bad ? PKA_DEV_BAD_PAGE : 0;
+                m.plan[plan_wg_seg(a.B) + w] = start < W ? seg : a.B;
+            }
+        }
+        if (MD && blockIdx.x == 0 && blockIdx.y == 0 && wv == 0) md_write_batch(m, md_lds, W, len_flags);
+    };
+    if constexpr (MD) {
+        seg = a.B;
+        if (start < W) {
+            int32_t lo = 0, hi = a.B - 1;  // largest b with T[b] <= start
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) >> 1;
+                if (__builtin_amdgcn_readfirstlane(sT[mid]) <= start) lo = mid; else hi = mid - 1;
+            }
+            seg = lo;
+        }
+    }
+    if (start >= W) {
+        md_close();
+        return;
+    }
     const int64_t end = min(share_start(w + 1, shq, shr), W);
     const int32_t* F = plan + plan_seg_prefix(a.B);
     const int32_t* T = plan + plan_tile_prefix(a.B);
-    int32_t seg = plan[plan_wg_seg(a.B) + w];
+    if constexpr (!MD) seg = plan[plan_wg_seg(a.B) + w];
+    // request prefixes: tokens F, tiles T, pages (the request's first entry
+    // of kv_indices)
+    auto Fat = [&](int32_t i) -> int32_t {
+        if constexpr (MD) return __builtin_amdgcn_readfirstlane(sF[i]);
+        else return load_uniform(F, i);
+    };
+    auto Tat = [&](int32_t i) -> int32_t {
+        if constexpr (MD) return __builtin_amdgcn_readfirstlane(sT[i]);
+        else return load_uniform(T, i);
+    };
+    auto Pat = [&](int32_t i) -> int32_t {
+        if constexpr (MD) return __builtin_amdgcn_readfirstlane(sP[i]);
+        else return load_uniform(a.kv_indptr, i);
+    };
+    // MD: the page id at page k of request sg from the page table, clamped
+    // into the pool
+    const int32_t P = 1 << a.page_shift;
+    auto table_page = [&](int32_t sg, int32_t k) {
+        int32_t pg = m.page_table[(int64_t)sg * m.pt_stride + k];
+        if (pg < 0 || pg >= a.num_pages) {
+            pflags = 1;
+            pg = min(max(pg, 0), a.num_pages - 1);
+        }
+        return pg;
+    };
 
     // one pool slot, all KV heads
     const int64_t krow = (int64_t)a.Hkv * DK * S::ESZ, vrow = (int64_t)a.Hkv * DV * S::ESZ;
@@ -381,8 +573,12 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     };
     auto rows_of = [&](int32_t sg) {
         Rows r;
-        r.L = load_uniform(F, sg + 1) - load_uniform(F, sg);
-        if constexpr (MQ) {
+        r.L = Fat(sg + 1) - Fat(sg);
+        if constexpr (MD) {
+            r.q0 = sg;
+            r.nq = 1;
+            r.pfx = r.L - 1;
+        } else if constexpr (MQ) {
             r.q0 = load_uniform(a.qo_indptr, sg);
             const int32_t nb = load_uniform(a.qo_indptr, sg + 1) - r.q0;
             r.nq = min(nb, a.qslots);
@@ -397,10 +593,10 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     // first non-empty piece from request sg on (seg = a.B: the share is done)
     auto open_piece = [&](int32_t sg, It& it) {
         for (; sg < a.B; ++sg) {
-            const int32_t t0 = load_uniform(T, sg), t1 = load_uniform(T, sg + 1);
+            const int32_t t0 = Tat(sg), t1 = Tat(sg + 1);
             if (t0 >= end) break;
             // token range of the piece: whole tiles, up to the request's end
-            const int32_t L = load_uniform(F, sg + 1) - load_uniform(F, sg);
+            const int32_t L = Fat(sg + 1) - Fat(sg);
             const int32_t lo = (int32_t)(max(start, (int64_t)t0) - t0) * DEC_TILE;
             const int32_t hi = end >= t1 ? L : (int32_t)(end - t0) * DEC_TILE;
             if (hi <= lo) continue;
@@ -414,7 +610,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
             it.lo = lo;
             it.hi = hi;
             it.c0 = 0;
-            it.pb = load_uniform(a.kv_indptr, sg);
+            it.pb = Pat(sg);
             it.t0 = lo;
             return;
         }
@@ -435,10 +631,13 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
         }
     };
     // pool slot of tile token `tok`; positions past the piece repeat its last
-    // token (loaded, never counted)
+    // token (loaded, never counted).  MD: the page id comes from the page
+    // table.
     auto slot_for = [&](const It& it) {
         const int32_t pos = it.t0 + tok;
-        return slot_of(a, it.pb, pos < it.hi ? pos : it.hi - 1);
+        const int32_t pc = pos < it.hi ? pos : it.hi - 1;
+        if constexpr (MD) return (table_page(it.seg, pc >> a.page_shift) << a.page_shift) | (pc & (P - 1));
+        else return slot_of(a, it.pb, pc);
     };
     // this lane's column of a unit: query token qi, head h
     struct Col {
@@ -473,17 +672,28 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
     };
     // the piece holding a request's last position writes its new token first
     auto new_token = [&](const It& u) {
-        if constexpr (!MQ) {
+        if constexpr (MD) {
+            const Rows r = rows_of(u.seg);
+            if (a.k_new && u.hi == r.L) {
+                const int32_t pos = r.L - 1;
+                int32_t pg = load_uniform(m.page_table, (int64_t)u.seg * m.pt_stride + (pos >> a.page_shift));
+                pg = min(max(pg, 0), a.num_pages - 1);  // flagged where the tile reads it
+                write_new_token<DK, DV, FP8>(a, r.q0, (pg << a.page_shift) | (pos & (P - 1)), g, lane);
+            }
+        } else if constexpr (!MQ) {
             if (a.k_new) {
                 const Rows r = rows_of(u.seg);
-                if (u.hi == r.L) write_new_token<DK, DV, FP8>(a, r.q0, g, lane);
+                if (u.hi == r.L) write_new_token<DK, DV, FP8>(a, r.q0, a.out_cache_loc[r.q0], g, lane);
             }
         }
     };
 
     It cur, nx, nn;
     open_piece(seg, cur);
-    if (cur.seg >= a.B) return;
+    if (cur.seg >= a.B) {
+        md_close();
+        return;
+    }
     new_token(cur);
     VTile<DK, DV, FP8> A, Bt;
     {
@@ -597,6 +807,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a) {
         if (!step(A, Bt)) break;
         if (!step(Bt, A)) break;
     }
+    md_close();
 }
 
 // fp32 cache: a plain VALU variant with the same work partition (lanes over
@@ -718,12 +929,32 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
 // row; grid z = query rows): lanes first take one partial each (max and
 // normaliser by wave reductions), then lanes take head dims and sweep the
 // partials with several loads in flight.  D: the value (output) width.
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
+//
+// MD: the decode kernel built the metadata in-kernel; the merge writes what
+// it left out: kv_indices (the gridDim.y workgroups of request b take equal
+// slices of its pages, clamped into the pool as the decode kernel read them)
+// and the request's new-token slot in out_cache_loc.
+template <int D, bool OUT_BF16, bool MD>
+__global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a, MetaArgs m) {
     constexpr int EPL = D / 64;
     constexpr int UNROLL = 8;
     const int lane = threadIdx.x & 63;
     const int32_t b = blockIdx.x;
+    if constexpr (MD) {
+        const int32_t p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
+        const int32_t* row = m.page_table + (int64_t)b * m.pt_stride;
+        const int32_t chunk = (p1 - p0 + gridDim.y - 1) / gridDim.y;
+        const int32_t i0 = p0 + blockIdx.y * chunk, i1 = min(p1, i0 + chunk);
+        for (int32_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
+            const int32_t pg = min(max(row[i - p0], 0), a.num_pages - 1);
+            if (i < m.max_kv_pages) m.kv_indices[i] = pg;
+        }
+        if (blockIdx.y == 0 && threadIdx.x == 0) {
+            const int32_t last = a.kv_last_page_len[b];  // position L - 1 is in page p1 - p0 - 1
+            const int32_t pg = min(max(row[p1 - p0 - 1], 0), a.num_pages - 1);
+            m.out_cache_loc[b] = (pg << a.page_shift) | (last - 1);
+        }
+    }
     const int32_t h = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (h >= a.Hq) return;
     const int32_t* plan = a.plan;
@@ -819,10 +1050,32 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a) {
 }
 
 // Dynamic LDS of a decode workgroup of `waves` waves: their regions and one
-// progress word each.
+// progress word each; with in-kernel metadata, the 8-byte aligned metadata
+// area of a batch of B requests after them.
 template <int DK, int DV, bool FP8>
 size_t decode_lds_bytes(int waves) {
     return (size_t)waves * (DecodeShape<DK, DV, FP8>::WAVE_LDS + 4);
+}
+template <int DK, int DV, bool FP8>
+size_t decode_md_lds_bytes(int waves, int32_t B) {
+    return ((decode_lds_bytes<DK, DV, FP8>(waves) + 7) & ~(size_t)7) + md_lds_bytes(B);
+}
+
+// The merge after a decode launch (md: after the decode kernel that built
+// the metadata; the merge then writes kv_indices and out_cache_loc).
+template <int DV>
+hipError_t launch_merge(pka_dtype q, const AttnArgs& a, const MetaArgs* md, hipStream_t s) {
+    const dim3 mgrid(a.B, (a.Hq + 3) / 4, a.qslots);
+    const MetaArgs none{};
+    if (md && q == PKA_BF16)
+        hipLaunchKernelGGL((decode_merge_kernel<DV, true, true>), mgrid, dim3(256), 0, s, a, *md);
+    else if (md)
+        hipLaunchKernelGGL((decode_merge_kernel<DV, false, true>), mgrid, dim3(256), 0, s, a, *md);
+    else if (q == PKA_BF16)
+        hipLaunchKernelGGL((decode_merge_kernel<DV, true, false>), mgrid, dim3(256), 0, s, a, none);
+    else
+        hipLaunchKernelGGL((decode_merge_kernel<DV, false, false>), mgrid, dim3(256), 0, s, a, none);
+    return hipGetLastError();
 }
 
 template <int DK, int DV>
@@ -832,41 +1085,71 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
     const dim3 grid((a.nwg + a.spw - 1) / a.spw, units / wpb);
     const dim3 block(64 * waves);
     const bool mq = a.qslots > 1;
+    const MetaArgs none{};
     if (kv == PKA_BF16) {
         const size_t lds = decode_lds_bytes<DK, DV, false>(waves);
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true>), grid, block, lds, s, a);
-        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false>), grid, block, lds, s, a);
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true, false>), grid, block, lds, s, a, none);
+        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false, false>), grid, block, lds, s, a, none);
     } else if (kv == PKA_FP8_E4M3FN) {
         const size_t lds = decode_lds_bytes<DK, DV, true>(waves);
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true>), grid, block, lds, s, a);
-        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false>), grid, block, lds, s, a);
+        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true, false>), grid, block, lds, s, a, none);
+        else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false, false>), grid, block, lds, s, a, none);
     } else {
         if (mq) hipLaunchKernelGGL((decode_f32_kernel<DK, DV, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((decode_f32_kernel<DK, DV, false>), grid, block, 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 mgrid(a.B, (a.Hq + 3) / 4, a.qslots);
-    if (q == PKA_BF16)
-        hipLaunchKernelGGL((decode_merge_kernel<DV, true>), mgrid, dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((decode_merge_kernel<DV, false>), mgrid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_merge<DV>(q, a, nullptr, s);
+}
+
+template <int DK, int DV>
+hipError_t launch_decode_md_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, const MetaArgs& m, int wpb,
+                              hipStream_t s) {
+    const int units = a.Hkv * a.qgroups;
+    const int waves = wpb * a.spw;
+    const dim3 grid((a.nwg + a.spw - 1) / a.spw, units / wpb);
+    const dim3 block(64 * waves);
+    if (kv == PKA_BF16) {
+        const size_t lds = decode_md_lds_bytes<DK, DV, false>(waves, a.B);
+        hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false, true>), grid, block, lds, s, a, m);
+    } else if (kv == PKA_FP8_E4M3FN) {
+        const size_t lds = decode_md_lds_bytes<DK, DV, true>(waves, a.B);
+        hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false, true>), grid, block, lds, s, a, m);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge<DV>(q, a, &m, s);
+}
+
+template <typename K>
+int occupancy(K kernel, int waves, size_t lds) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 64 * waves, lds);
+    return e == hipSuccess ? n : 0;
 }
 
 template <int DK, int DV>
 int blocks_per_cu_d(pka_dtype kv, int waves) {
-    int n = 0;
-    hipError_t e;
     if (kv == PKA_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, false, false>, 64 * waves,
-                                                         decode_lds_bytes<DK, DV, false>(waves));
-    else if (kv == PKA_FP8_E4M3FN)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<DK, DV, true, false>, 64 * waves,
-                                                         decode_lds_bytes<DK, DV, true>(waves));
-    else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_f32_kernel<DK, DV, false>, 64 * waves, 0);
-    return e == hipSuccess ? n : 0;
+        return occupancy(decode_mfma_kernel<DK, DV, false, false, false>, waves, decode_lds_bytes<DK, DV, false>(waves));
+    if (kv == PKA_FP8_E4M3FN)
+        return occupancy(decode_mfma_kernel<DK, DV, true, false, false>, waves, decode_lds_bytes<DK, DV, true>(waves));
+    return occupancy(decode_f32_kernel<DK, DV, false>, waves, 0);
+}
+
+// the in-kernel metadata variant at the largest batch it takes
+template <int DK, int DV>
+int blocks_per_cu_md_d(pka_dtype kv, int waves) {
+    if (kv == PKA_BF16)
+        return occupancy(decode_mfma_kernel<DK, DV, false, false, true>, waves,
+                         decode_md_lds_bytes<DK, DV, false>(waves, DEC_MD_MAX_B));
+    if (kv == PKA_FP8_E4M3FN)
+        return occupancy(decode_mfma_kernel<DK, DV, true, false, true>, waves,
+                         decode_md_lds_bytes<DK, DV, true>(waves, DEC_MD_MAX_B));
+    return 0;
 }
 
 }  // namespace
@@ -878,11 +1161,27 @@ int decode_blocks_per_cu(pka_dtype kv, int DK, int DV, int waves) {
     return 0;
 }
 
+bool decode_md_fits(pka_dtype kv, int DK, int DV, int waves) {
+    int md = 0;
+    if (DK == 128 && DV == 128) md = blocks_per_cu_md_d<128, 128>(kv, waves);
+    else if (DK == 64 && DV == 64) md = blocks_per_cu_md_d<64, 64>(kv, waves);
+    else if (DK == 192 && DV == 128) md = blocks_per_cu_md_d<192, 128>(kv, waves);
+    return md > 0 && md == decode_blocks_per_cu(kv, DK, DV, waves);
+}
+
 hipError_t launch_decode(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, int wpb,
                          hipStream_t s) {
     if (DK == 128 && DV == 128) return launch_decode_d<128, 128>(q, kv, a, wpb, s);
     if (DK == 64 && DV == 64) return launch_decode_d<64, 64>(q, kv, a, wpb, s);
     if (DK == 192 && DV == 128) return launch_decode_d<192, 128>(q, kv, a, wpb, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_md(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a,
+                            const MetaArgs& m, int wpb, hipStream_t s) {
+    if (DK == 128 && DV == 128) return launch_decode_md_d<128, 128>(q, kv, a, m, wpb, s);
+    if (DK == 64 && DV == 64) return launch_decode_md_d<64, 64>(q, kv, a, m, wpb, s);
+    if (DK == 192 && DV == 128) return launch_decode_md_d<192, 128>(q, kv, a, m, wpb, s);
     return hipErrorInvalidValue;
 }
 

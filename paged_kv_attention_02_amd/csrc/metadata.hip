@@ -84,16 +84,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         if (b < a.B) {
             L = a.seq_lens[b];
             n = a.is_decode ? 1 : a.extend_lens[b];
-            if (L < 1) { flags |= PKA_DEV_BAD_LENGTH; L = 1; }
-            if (n < 0) { flags |= PKA_DEV_BAD_LENGTH; n = 0; }
-            if (n > L) { flags |= PKA_DEV_BAD_LENGTH; n = L; }
-            pages = (L + P - 1) >> a.page_shift;
-            if (pages > a.pt_cols) {
-                flags |= PKA_DEV_TABLE_SHORT;
-                pages = a.pt_cols;
-                L = (int64_t)a.pt_cols << a.page_shift;
-                if (n > L) n = L;
-            }
+            flags |= md_clamp_request(L, n, pages, a.page_shift, a.pt_cols);
         }
         // pages, new tokens, tokens, decode tiles
         int64_t x[4] = {pages, n, L, (L + DEC_TILE - 1) / DEC_TILE};
@@ -202,13 +193,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         // share w starts in the request that holds its first tile.
         // Cutting at tile boundaries leaves no partial tile except a
         // request's last, so the shares differ by at most one tile of work.
-        int64_t share = W / a.nwg, rem = W % a.nwg;
-        if (share < DEC_MIN_SHARE) {
-            share = DEC_MIN_SHARE;
-            rem = 0;
-        }
+        int64_t share, rem;
+        decode_shares(W, a.nwg, share, rem);
         int32_t* wg_seg = a.plan + plan_wg_seg(a.B);
+        int32_t* share_flags = a.plan + plan_share_flags(a.B);
         for (int32_t w = t; w < a.nwg; w += SCAN_THREADS) {
+            share_flags[w] = 0;
             const int64_t pos = share_start(w, share, rem);
             int32_t seg = a.B;
             if (pos < W) {

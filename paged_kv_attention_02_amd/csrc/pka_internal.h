@@ -52,13 +52,15 @@ constexpr int DEC_MAX_Q = 16;
 
 // plan offsets that depend on the batch size: the token prefix F[b] = sum of
 // L over requests before b, the tile prefix T[b] = sum of ceil(L / DEC_TILE)
-// (the decode partition cuts it), then the first request of each decode
-// workgroup
+// (the decode partition cuts it), the first request of each decode share,
+// then one PKA_DEV_* word per decode share (written by the decode kernel that
+// builds its own metadata; zeroed by the metadata kernel)
 __host__ __device__ inline int64_t plan_seg_prefix(int32_t /*B*/) { return PLAN_HDR; }
 __host__ __device__ inline int64_t plan_tile_prefix(int32_t B) { return PLAN_HDR + (int64_t)B + 1; }
 __host__ __device__ inline int64_t plan_wg_seg(int32_t B) { return PLAN_HDR + 2 * ((int64_t)B + 1); }
+__host__ __device__ inline int64_t plan_share_flags(int32_t B) { return plan_wg_seg(B) + DEC_MAX_WG; }
 __host__ __device__ inline int64_t plan_ext_items(int32_t B) {
-    return plan_wg_seg(B) + DEC_MAX_WG;
+    return plan_share_flags(B) + DEC_MAX_WG;
 }
 // extend items (request, query tile of tq tokens): at most ceil(N / tq) + B
 __host__ __device__ inline int64_t plan_ext_capacity(int32_t B, int32_t N, int32_t tq) {
@@ -66,6 +68,40 @@ __host__ __device__ inline int64_t plan_ext_capacity(int32_t B, int32_t N, int32
 }
 __host__ __device__ inline int64_t plan_elems(int32_t B, int32_t N, int32_t tq) {
     return plan_ext_items(B) + 2 * plan_ext_capacity(B, N, tq);
+}
+
+// Decode batches up to this size may build their metadata inside the decode
+// kernel (every workgroup scans the lengths into LDS).
+constexpr int DEC_MD_MAX_B = 512;
+
+// Clamp one request's lengths the way every metadata builder does: L >= 1,
+// 0 <= n <= L, and no more pages than the page table has columns.  Returns the
+// PKA_DEV_* flags of what was clamped; `pages` = ceil(L / page size).
+__host__ __device__ inline int32_t md_clamp_request(int64_t& L, int64_t& n, int64_t& pages,
+                                                    int32_t page_shift, int32_t pt_cols) {
+    int32_t flags = 0;
+    if (L < 1) { flags |= PKA_DEV_BAD_LENGTH; L = 1; }
+    if (n < 0) { flags |= PKA_DEV_BAD_LENGTH; n = 0; }
+    if (n > L) { flags |= PKA_DEV_BAD_LENGTH; n = L; }
+    pages = (L + (1 << page_shift) - 1) >> page_shift;
+    if (pages > pt_cols) {
+        flags |= PKA_DEV_TABLE_SHORT;
+        pages = pt_cols;
+        L = (int64_t)pt_cols << page_shift;
+        if (n > L) n = L;
+    }
+    return flags;
+}
+
+// Decode shares of W tiles over nwg workgroups: q tiles each (at least
+// DEC_MIN_SHARE) and one more for the first r.
+__host__ __device__ inline void decode_shares(int64_t W, int32_t nwg, int64_t& q, int64_t& r) {
+    q = W / nwg;
+    r = W % nwg;
+    if (q < DEC_MIN_SHARE) {
+        q = DEC_MIN_SHARE;
+        r = 0;
+    }
 }
 
 // --------------------------------------------------------------- launch --
@@ -154,6 +190,12 @@ hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, const SaveArgs& a, hipStr
 // workgroup holds a.spw shares, 64 * wpb * a.spw threads.
 hipError_t launch_decode(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, int wpb,
                          hipStream_t s);
+// Decode (one query per request, bf16 / fp8 cache) that builds the batch's
+// metadata itself from m.seq_lens and m.page_table, then the merge.
+hipError_t launch_decode_md(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a,
+                            const MetaArgs& m, int wpb, hipStream_t s);
+// Whether that kernel keeps the occupancy of the plain decode kernel.
+bool decode_md_fits(pka_dtype kv, int DK, int DV, int waves);
 hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, hipStream_t s);
 
 // Decode workgroups of `waves` waves that fit on one compute unit at once.

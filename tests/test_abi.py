@@ -145,3 +145,35 @@ def test_calls_refuse_bad_arguments_without_touching_the_device():
     assert st == -1
     for s in (0, -1, -2, -3, -4):
         assert lib.pka_status_string(s)
+
+
+def test_forward_with_metadata_refuses_before_any_launch():
+    """The one-call entry point checks the forward's and the metadata's
+    arguments before it enqueues anything."""
+    lib = pka.lib()
+    ctx = pka.Context(32, 8, 128, 16, 100)
+    fake = 1 << 20  # aligned, never dereferenced: validation fails first
+    f = lib.pka_forward_with_metadata
+    md = pka.BatchStruct(0, 4, 40, 40, fake, fake, fake, fake, fake, fake)  # extend metadata
+    # unknown modes
+    assert f(ctx.handle, 9, 0, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None, 0, None) == -1
+    assert f(ctx.handle, 0, 5, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None, 0, None) == -1
+    # IDLE needs no buffers
+    assert f(ctx.handle, 2, 0, None, None, None, 0, 0, ctypes.byref(md), None, None, None, 1,
+             None, None, None, None, None, 0, None) == 0
+    # metadata built for another mode
+    assert f(ctx.handle, 3, 0, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None, 0, None) == -1
+    # an extend batch needs extend_lens; a bad page-table shape is refused
+    assert f(ctx.handle, 0, 0, fake, None, fake, 3, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None, 0, None) == -1
+    assert f(ctx.handle, 0, 0, fake, fake, fake, 2, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None, 0, None) == -1
+    # the cache write needs its rows
+    assert f(ctx.handle, 0, 0, fake, fake, fake, 3, 3, ctypes.byref(md), fake, None, fake, 1,
+             fake, fake, fake, None, None, 0, None) == -1
+    assert f(ctx.handle, 0, 0, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake + 4, fake, 1,
+             fake, fake, fake, None, None, 0, None) == -1
+    assert b"extend_lens" in lib.pka_last_error() or lib.pka_last_error()

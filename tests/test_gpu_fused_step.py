@@ -1,0 +1,221 @@
+"""pka_forward_with_metadata: metadata and forward in one call, through the C ABI.
+
+For a bf16 / fp8 decode batch of up to 512 requests the decode kernel builds
+the metadata itself (every workgroup scans the lengths, waves read page ids
+from the page table, the metadata arrays are written on the side).  Whatever
+the path, the call must leave exactly what pka_init_metadata followed by
+pka_forward leaves: metadata arrays, pools and outputs bit-identical, and the
+outputs within the gates of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.oracle_ref import LSE_ATOL, TOL, errors, oracle_full, raw_np
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_attention_02_amd as pka
+    from tests.gpu_problem import GpuProblem
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    print(f"\n[case] {request.node.name}", flush=True)
+
+
+W = workloads.WORKLOADS
+MD_ARRAYS = ("kv_indptr", "kv_indices", "kv_last_page_len", "qo_indptr", "out_cache_loc")
+
+CASES = {
+    "llama_b9_p16": W["llama3_8b_decode"].replace(batch=9, seq_len_args=(1, 900), seed=81),
+    "qwen_b7_p1": W["qwen3_235b_decode"].replace(batch=7, seq_len_kind="uniform", seq_len_args=(1, 1200), seed=82),
+    "fp8_b6_p64": W["long_fp8_decode"].replace(batch=6, seq_len_args=(1, 2500), seed=83),
+    "llama_b64_short_p16": W["llama3_8b_decode"].replace(batch=64, seq_len_args=(1, 70), seed=84),
+    "d64_p4": W["llama3_8b_decode"].replace(batch=5, head_dim=64, page_size=4, seq_len_args=(1, 500), seed=85),
+    "asym_p128": W["llama3_8b_decode"].replace(batch=5, num_q_heads=16, num_kv_heads=16, head_dim=192,
+                                               v_head_dim=128, page_size=128, seq_len_args=(1, 700), seed=86),
+    "b300_tiny_p2": W["llama3_8b_decode"].replace(batch=300, page_size=2, seq_len_args=(1, 5), seed=87),
+    "b512_p16": W["llama3_8b_decode"].replace(batch=512, seq_len_args=(1, 60), seed=88),
+    # beyond the in-kernel limit: metadata kernel, then the forward
+    "b600_fallback": W["llama3_8b_decode"].replace(batch=600, seq_len_args=(1, 40), seed=89),
+    "tiny_f32_fallback": W["tiny_decode"],
+    "extend_b3": W["llama3_8b_extend"].replace(batch=3, new_len_args=(1, 200), prefix_len_args=(0, 300), seed=90),
+}
+
+
+def _md_arrays(prob):
+    L = prob.layout
+    n = {"kv_indptr": L.batch + 1, "kv_indices": L.kv_pages, "kv_last_page_len": L.batch,
+         "qo_indptr": L.batch + 1, "out_cache_loc": L.num_q_tokens}
+    return {k: getattr(prob.md, k)[:n[k]].clone() for k in MD_ARRAYS}
+
+
+def _scrub(prob):
+    """Overwrite every output the step must produce."""
+    for k in MD_ARRAYS + ("plan",):
+        getattr(prob.md, k).fill_(-7)
+    prob.out.fill_(float("nan"))
+    prob.lse.fill_(float("nan"))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_one_call_equals_metadata_then_forward(name):
+    spec = CASES[name]
+    layout = workloads.make_layout(spec)
+    values = workloads.make_values(layout, device="cuda")
+    # reference: the two calls, on pools that hold only the prefix
+    ref = GpuProblem(layout, values, prefix_only=True)
+    ref.step()
+    torch.cuda.synchronize()
+    assert ref.md.status() == 0
+    # the one call, on fresh pools and scrubbed outputs
+    prob = GpuProblem(layout, values, prefix_only=True)
+    _scrub(prob)
+    prob.fused_step()
+    torch.cuda.synchronize()
+    assert prob.md.status() == 0
+    got, want = _md_arrays(prob), _md_arrays(ref)
+    for k in MD_ARRAYS:
+        assert torch.equal(got[k], want[k]), k
+    # the oracle's metadata too
+    ext = None if spec.mode == "decode" else layout.extend_lens
+    omd = oracle.metadata(layout.seq_lens, ext, layout.page_table, spec.page_size, layout.num_pages)
+    for k, v in omd.items():
+        assert np.array_equal(got[k].cpu().numpy()[:v.size], v), k
+    # the plan: the attention paths read it, so pka_attn_decode on it must agree
+    assert torch.equal(prob.k_pool.view(torch.uint8) if spec.kv_dtype == "fp8" else prob.k_pool.view(torch.int16),
+                       ref.k_pool.view(torch.uint8) if spec.kv_dtype == "fp8" else ref.k_pool.view(torch.int16))
+    assert np.array_equal(raw_np(prob.v_pool), raw_np(ref.v_pool), equal_nan=spec.kv_dtype == "f32")
+    assert torch.equal(prob.out, ref.out), "outputs differ from metadata + forward"
+    assert torch.equal(prob.lse, ref.lse)
+    want_out, want_lse = oracle_full(layout, values)
+    max_abs, rel = errors(prob.out_np(), want_out)
+    tol_abs, tol_rel = TOL[spec.kv_dtype]
+    print(f"[parity] {name}: max_abs={max_abs:.3e} rel_rms={rel:.3e}", flush=True)
+    assert max_abs <= tol_abs and rel <= tol_rel
+    np.testing.assert_allclose(prob.lse_np(), want_lse, rtol=0, atol=LSE_ATOL)
+
+
+def test_plan_serves_a_later_decode_call():
+    """Metadata left by the one-call path serves the plain decode call of
+    another layer: same result as the step itself."""
+    layout = workloads.make_layout(CASES["llama_b9_p16"])
+    prob = GpuProblem(layout)
+    prob.fused_step(save=False)
+    torch.cuda.synchronize()
+    first = prob.out.clone()
+    prob.out.fill_(float("nan"))
+    pka.attn_decode(prob.ctx, prob.md, prob.values.q, prob.k_pool, prob.v_pool, prob.out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, prob.out)
+    assert prob.md.status() == 0
+
+
+def test_without_the_cache_write_reads_the_pool_as_is():
+    layout = workloads.make_layout(CASES["fp8_b6_p64"])
+    ref = GpuProblem(layout)
+    ref.metadata_step()
+    ref.attention_step(save=False)
+    prob = GpuProblem(layout, ref.values)
+    prob.fused_step(save=False)
+    torch.cuda.synchronize()
+    assert torch.equal(prob.out, ref.out)
+    assert torch.equal(prob.lse, ref.lse)
+
+
+def test_bad_page_ids_are_clamped_and_flagged():
+    spec = CASES["llama_b9_p16"].replace(batch=3, seq_len_kind="uniform", seq_len_args=(20, 60))
+    layout = workloads.make_layout(spec)
+    prob = GpuProblem(layout)
+    bad = prob.page_table.clone()
+    bad[1, 0] = layout.num_pages + 5
+    bad[2, 1] = -3
+    prob.fused_step(page_table=bad)
+    torch.cuda.synchronize()
+    assert prob.md.status() & 2  # PKA_DEV_BAD_PAGE
+    kvi = prob.md.kv_indices.cpu().numpy()
+    ptr = prob.md.kv_indptr.cpu().numpy()
+    assert kvi[ptr[1]] == layout.num_pages - 1 and kvi[ptr[2] + 1] == 0
+    assert np.all(np.isfinite(prob.out_np()))
+    # a clean call afterwards clears the flags
+    prob.fused_step()
+    assert prob.md.status() == 0
+
+
+def test_lengths_beyond_the_page_table_are_flagged():
+    spec = CASES["llama_b9_p16"].replace(batch=2, seq_len_kind="uniform", seq_len_args=(20, 40))
+    layout = workloads.make_layout(spec)
+    prob = GpuProblem(layout)
+    lens = prob.seq_lens.clone()
+    lens[0] = layout.page_table.shape[1] * spec.page_size + 100
+    prob.fused_step(save=False, seq_lens=lens)
+    assert prob.md.status() & 4  # PKA_DEV_TABLE_SHORT
+    lens[0] = 0
+    prob.fused_step(save=False, seq_lens=lens)
+    assert prob.md.status() & 1  # PKA_DEV_BAD_LENGTH
+
+
+def test_full_size_llama_batch_is_bit_identical():
+    layout = workloads.make_layout(W["llama3_8b_decode"])
+    values = workloads.make_values(layout, device="cuda")
+    ref = GpuProblem(layout, values, prefix_only=True)
+    ref.step()
+    prob = GpuProblem(layout, values, prefix_only=True)
+    _scrub(prob)
+    prob.fused_step()
+    torch.cuda.synchronize()
+    assert prob.md.status() == 0
+    for k in MD_ARRAYS:
+        assert torch.equal(_md_arrays(prob)[k], _md_arrays(ref)[k]), k
+    assert torch.equal(prob.out, ref.out)
+    assert torch.equal(prob.k_pool.view(torch.int16), ref.k_pool.view(torch.int16))
+    assert torch.equal(prob.v_pool.view(torch.int16), ref.v_pool.view(torch.int16))
+
+
+def test_graph_replays_of_the_one_call_step():
+    spec = CASES["llama_b9_p16"]
+    layout = workloads.make_layout(spec)
+    prob = GpuProblem(layout)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        prob.fused_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        prob.fused_step()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    P = spec.page_size
+    grow = torch.tensor([1 <= int(L) % P <= P - 2 for L in layout.seq_lens], device="cuda")
+    for r in range(3):
+        prob.values.q.copy_(torch.randn(prob.values.q.shape, generator=gen, device="cuda").to(prob.values.q.dtype))
+        if r > 0:
+            prob.seq_lens += grow.to(torch.int32)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_lse = prob.out.clone(), prob.lse.clone()
+        assert prob.md.status() == 0
+        prob.step()  # metadata kernel + forward, eagerly
+        torch.cuda.synchronize()
+        assert torch.equal(got, prob.out), f"replay {r}"
+        assert torch.equal(got_lse, prob.lse)
+
+
+def test_idle_and_empty_launch_nothing():
+    layout = workloads.make_layout(CASES["llama_b9_p16"])
+    prob = GpuProblem(layout)
+    prob.out.fill_(1.5)
+    before = prob.out.clone()
+    pka.forward_with_metadata(prob.ctx, "idle", prob.md, None, None, None, None, None, None,
+                              None, None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(before, prob.out)
