@@ -376,10 +376,66 @@ __device__ inline void md_prefixes(const MetaArgs& m, uint8_t* base, int64_t& W,
     W = min(carry[2], (int64_t)INT32_MAX);
 }
 
-// The batch-wide metadata outputs, written by one wave from its workgroup's
-// LDS prefixes: kv_indptr, qo_indptr (request b's query row is b),
-// kv_last_page_len, the plan's prefixes and partition words, and the status
-// words (clamping flags; the per-share page flags are written by the shares).
+// Batches of at most 64 requests: every wave builds the prefixes itself in
+// registers, lane b holding the sums through request b (inclusive), so
+// neither LDS nor a barrier is needed.  `flags` is the OR of the clamping
+// flags over the batch.
+struct MdWave {
+    int32_t P, F, T;  // pages, tokens, tiles through request `lane`
+};
+__device__ inline MdWave md_prefixes_wave(const MetaArgs& m, int32_t& flags_out) {
+    const int lane = threadIdx.x & 63;
+    int64_t L = 0, n = 1, pages = 0;
+    int32_t flags = 0;
+    if (lane < m.B) {
+        L = m.seq_lens[lane];
+        flags = md_clamp_request(L, n, pages, m.page_shift, m.pt_cols);
+    }
+    int64_t x[3] = {pages, L, (L + DEC_TILE - 1) / DEC_TILE};
+    #pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int64_t y[3];
+        #pragma unroll
+        for (int v = 0; v < 3; ++v) y[v] = __shfl_up(x[v], off);
+        if (lane >= off) {
+            #pragma unroll
+            for (int v = 0; v < 3; ++v) x[v] += y[v];
+        }
+    }
+    if (lane < m.B && (x[0] > m.max_kv_pages || x[1] > INT32_MAX)) flags |= PKA_DEV_CAPACITY;
+    int32_t all = 0;
+    #pragma unroll
+    for (int bit = 1; bit <= PKA_DEV_CAPACITY; bit <<= 1)
+        if (__ballot((flags & bit) != 0)) all |= bit;
+    flags_out = __builtin_amdgcn_readfirstlane(all);
+    MdWave r;
+    r.P = (int32_t)min(x[0], (int64_t)INT32_MAX);
+    r.F = (int32_t)min(x[1], (int64_t)INT32_MAX);
+    r.T = (int32_t)min(x[2], (int64_t)INT32_MAX);
+    return r;
+}
+
+// The plan's partition and status words of a batch built in-kernel.
+__device__ inline void md_write_plan_words(const MetaArgs& m, int64_t W, int32_t flags) {
+    const int lane = threadIdx.x & 63;
+    for (int i = lane; i < MD_SLOTS; i += 64) m.plan[PLAN_MDST + i] = i == 0 ? flags : 0;
+    if (lane == 0) {
+        int64_t q, r;
+        decode_shares(W, m.nwg, q, r);
+        m.plan[PLAN_STATUS] = 0;
+        m.plan[PLAN_SHARE] = (int32_t)q;
+        m.plan[PLAN_SHARE_REM] = (int32_t)r;
+        m.plan[PLAN_TOTAL] = (int32_t)W;
+        m.plan[PLAN_NWG] = m.nwg;
+        m.plan[PLAN_EXT_COUNT] = 0;
+        m.plan[PLAN_EXT_TQ] = m.ext_tq;
+    }
+}
+
+// The batch-wide metadata outputs, written by one wave: kv_indptr, qo_indptr
+// (request b's query row is b), kv_last_page_len, the plan's prefixes, and
+// the partition and status words (clamping flags; the per-share page flags
+// are written by the shares).  From the workgroup's LDS prefixes ...
 __device__ inline void md_write_batch(const MetaArgs& m, const uint8_t* base, int64_t W, int32_t flags) {
     const int32_t* const sP = (const int32_t*)base;
     const int32_t* const sF = sP + (m.B + 1);
@@ -397,18 +453,28 @@ __device__ inline void md_write_batch(const MetaArgs& m, const uint8_t* base, in
             m.kv_last_page_len[b] = L - ((pages - 1) << m.page_shift);
         }
     }
-    for (int i = lane; i < MD_SLOTS; i += 64) m.plan[PLAN_MDST + i] = i == 0 ? flags : 0;
+    md_write_plan_words(m, W, flags);
+}
+// ... or from the wave's register prefixes (at most 64 requests)
+__device__ inline void md_write_batch(const MetaArgs& m, const MdWave& r, int64_t W, int32_t flags) {
+    int32_t* const F = m.plan + plan_seg_prefix(m.B);
+    int32_t* const T = m.plan + plan_tile_prefix(m.B);
+    const int lane = threadIdx.x & 63;
+    // every lane takes part in the shuffles (a lane reading an inactive one gets nothing)
+    const int32_t Fu = __shfl_up(r.F, 1), Pu = __shfl_up(r.P, 1);
+    const int32_t F0 = lane ? Fu : 0, P0 = lane ? Pu : 0;
     if (lane == 0) {
-        int64_t q, r;
-        decode_shares(W, m.nwg, q, r);
-        m.plan[PLAN_STATUS] = 0;
-        m.plan[PLAN_SHARE] = (int32_t)q;
-        m.plan[PLAN_SHARE_REM] = (int32_t)r;
-        m.plan[PLAN_TOTAL] = (int32_t)W;
-        m.plan[PLAN_NWG] = m.nwg;
-        m.plan[PLAN_EXT_COUNT] = 0;
-        m.plan[PLAN_EXT_TQ] = m.ext_tq;
+        m.kv_indptr[0] = m.qo_indptr[0] = 0;
+        F[0] = T[0] = 0;
     }
+    if (lane < m.B) {
+        m.kv_indptr[lane + 1] = r.P;
+        m.qo_indptr[lane + 1] = lane + 1;
+        F[lane + 1] = r.F;
+        T[lane + 1] = r.T;
+        m.kv_last_page_len[lane] = (r.F - F0) - ((r.P - P0 - 1) << m.page_shift);
+    }
+    md_write_plan_words(m, W, flags);
 }
 
 typedef __attribute__((address_space(3))) const int32_t lds_i32_t;
@@ -462,9 +528,19 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     if (pair) __hip_atomic_store(prog + wv, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     // MD: the metadata area, 8-byte aligned after the progress words
     uint8_t* const md_lds = dec_lds + ((waves * (S::WAVE_LDS + 4) + 7) & ~7);
+    // MD: prefixes in registers (at most 64 requests) or in LDS
+    const bool md_reg = MD && a.B <= 64;
     int64_t W_md = 0;
     int32_t len_flags = 0;
-    if constexpr (MD) md_prefixes(m, md_lds, W_md, len_flags);
+    MdWave mw{};
+    if constexpr (MD) {
+        if (md_reg) {
+            mw = md_prefixes_wave(m, len_flags);
+            W_md = __builtin_amdgcn_readlane(mw.T, a.B - 1);
+        } else {
+            md_prefixes(m, md_lds, W_md, len_flags);
+        }
+    }
     lds_i32_t* const sP = (lds_i32_t*)md_lds;  // MD: the LDS prefixes
     lds_i32_t* const sF = sP + (a.B + 1);
     lds_i32_t* const sT = sF + (a.B + 1);
@@ -501,11 +577,17 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
                 m.plan[plan_wg_seg(a.B) + w] = start < W ? seg : a.B;
             }
         }
-        if (MD && blockIdx.x == 0 && blockIdx.y == 0 && wv == 0) md_write_batch(m, md_lds, W, len_flags);
+        if (MD && blockIdx.x == 0 && blockIdx.y == 0 && wv == 0) {
+            if (md_reg) md_write_batch(m, mw, W, len_flags);
+            else md_write_batch(m, md_lds, W, len_flags);
+        }
     };
     if constexpr (MD) {
         seg = a.B;
-        if (start < W) {
+        if (start < W && md_reg) {
+            // largest b with T[b] <= start: T[0] = 0, T[b] = lane b - 1's sum
+            seg = __builtin_popcountll(__ballot(lane < a.B - 1 && mw.T <= start));
+        } else if (start < W) {
             int32_t lo = 0, hi = a.B - 1;  // largest b with T[b] <= start
             while (lo < hi) {
                 const int32_t mid = (lo + hi + 1) >> 1;
@@ -525,15 +607,18 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     // request prefixes: tokens F, tiles T, pages (the request's first entry
     // of kv_indices)
     auto Fat = [&](int32_t i) -> int32_t {
-        if constexpr (MD) return __builtin_amdgcn_readfirstlane(sF[i]);
+        if constexpr (MD) return md_reg ? (i ? __builtin_amdgcn_readlane(mw.F, i - 1) : 0)
+                                        : __builtin_amdgcn_readfirstlane(sF[i]);
         else return load_uniform(F, i);
     };
     auto Tat = [&](int32_t i) -> int32_t {
-        if constexpr (MD) return __builtin_amdgcn_readfirstlane(sT[i]);
+        if constexpr (MD) return md_reg ? (i ? __builtin_amdgcn_readlane(mw.T, i - 1) : 0)
+                                        : __builtin_amdgcn_readfirstlane(sT[i]);
         else return load_uniform(T, i);
     };
     auto Pat = [&](int32_t i) -> int32_t {
-        if constexpr (MD) return __builtin_amdgcn_readfirstlane(sP[i]);
+        if constexpr (MD) return md_reg ? (i ? __builtin_amdgcn_readlane(mw.P, i - 1) : 0)
+                                        : __builtin_amdgcn_readfirstlane(sP[i]);
         else return load_uniform(a.kv_indptr, i);
     };
     // MD: the page id at page k of request sg from the page table, clamped
@@ -1058,6 +1143,7 @@ size_t decode_lds_bytes(int waves) {
 }
 template <int DK, int DV, bool FP8>
 size_t decode_md_lds_bytes(int waves, int32_t B) {
+    if (B <= 64) return decode_lds_bytes<DK, DV, FP8>(waves);  // prefixes in registers
     return ((decode_lds_bytes<DK, DV, FP8>(waves) + 7) & ~(size_t)7) + md_lds_bytes(B);
 }
 
