@@ -230,8 +230,9 @@ def cpu_baseline(layout, values, budget_s: float = 20.0):
 
 
 def bench_decode_kernel(spec, iters: int, warm: int = 10):
-    """Kernel-level decode figure for one workload (attn_decode alone), on two
-    copies of pools and metadata used alternately (as for the headline batch)."""
+    """Decode figures for one workload on two copies of pools and metadata
+    used alternately (as for the headline batch): attn_decode alone on
+    prebuilt metadata, and the whole step as one call and as two."""
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
@@ -242,11 +243,20 @@ def bench_decode_kernel(spec, iters: int, warm: int = 10):
         p.attention_step(save=True)
     torch.cuda.synchronize()
     ms = time_events(lambda i: probs[i % 2].attention_step(save=False, lse=False), iters, warm=warm)
+    # the whole step (metadata, cache write, decode, merge) as one call and
+    # as two (init_metadata, then forward)
+    ms_step = time_events(lambda i: probs[i % 2].fused_step(), iters, warm=warm)
+    ms_two = time_events(lambda i: probs[i % 2].step(), iters, warm=warm)
+    for p in probs:
+        assert p.md.status() == 0, "device status flags set"
     nbytes = decode_algorithmic_bytes(layout)
+    kvb = kv_bytes(layout)
     out = {"workload": layout.spec.name, "kv_tokens": layout.total_tokens,
-           "ms": round(ms, 4), "kv_read_GBps": round(kv_bytes(layout) / ms / 1e6, 1),
+           "ms": round(ms, 4), "kv_read_GBps": round(kvb / ms / 1e6, 1),
            "algorithmic_GBps": round(nbytes / ms / 1e6, 1),
-           "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+           "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+           "step_ms": round(ms_step, 4), "step_kv_read_GBps": round(kvb / ms_step / 1e6, 1),
+           "two_call_step_ms": round(ms_two, 4)}
     del probs
     torch.cuda.empty_cache()
     return out

@@ -161,8 +161,12 @@ def test_lengths_beyond_the_page_table_are_flagged():
     assert prob.md.status() & 1  # PKA_DEV_BAD_LENGTH
 
 
-def test_full_size_llama_batch_is_bit_identical():
-    layout = workloads.make_layout(W["llama3_8b_decode"])
+@pytest.mark.parametrize("name", ["llama3_8b_decode", "qwen3_235b_decode", "long_fp8_decode"])
+def test_full_size_batches_are_bit_identical(name):
+    """The full-size decode batches (64 requests: prefixes in registers; 128:
+    in LDS; 16 fp8 requests at 32k-128k tokens) through one call and through
+    two calls leave identical metadata, pools and outputs."""
+    layout = workloads.make_layout(W[name])
     values = workloads.make_values(layout, device="cuda")
     ref = GpuProblem(layout, values, prefix_only=True)
     ref.step()
@@ -174,8 +178,11 @@ def test_full_size_llama_batch_is_bit_identical():
     for k in MD_ARRAYS:
         assert torch.equal(_md_arrays(prob)[k], _md_arrays(ref)[k]), k
     assert torch.equal(prob.out, ref.out)
-    assert torch.equal(prob.k_pool.view(torch.int16), ref.k_pool.view(torch.int16))
-    assert torch.equal(prob.v_pool.view(torch.int16), ref.v_pool.view(torch.int16))
+    assert torch.equal(prob.lse, ref.lse)
+    raw = torch.uint8 if layout.spec.kv_dtype == "fp8" else torch.int16
+    assert torch.equal(prob.k_pool.view(raw), ref.k_pool.view(raw))
+    assert torch.equal(prob.v_pool.view(raw), ref.v_pool.view(raw))
+    print(f"[fused] {name}: bit-identical to metadata + forward", flush=True)
 
 
 def test_graph_replays_of_the_one_call_step():
