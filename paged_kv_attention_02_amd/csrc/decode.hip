@@ -541,8 +541,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             md_prefixes(m, md_lds, W_md, len_flags);
         }
     }
-    lds_i32_t* const sP = (lds_i32_t*)md_lds;  // MD: the LDS prefixes
-    lds_i32_t* const sF = sP + (a.B + 1);
+    lds_i32_t* const sF = (lds_i32_t*)md_lds + (a.B + 1);  // MD, LDS path: token and tile prefixes
     lds_i32_t* const sT = sF + (a.B + 1);
     if (g >= a.Hkv) return;
 
@@ -604,8 +603,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     const int32_t* F = plan + plan_seg_prefix(a.B);
     const int32_t* T = plan + plan_tile_prefix(a.B);
     if constexpr (!MD) seg = plan[plan_wg_seg(a.B) + w];
-    // request prefixes: tokens F, tiles T, pages (the request's first entry
-    // of kv_indices)
+    // request prefixes: tokens F, tiles T
     auto Fat = [&](int32_t i) -> int32_t {
         if constexpr (MD) return md_reg ? (i ? __builtin_amdgcn_readlane(mw.F, i - 1) : 0)
                                         : __builtin_amdgcn_readfirstlane(sF[i]);
@@ -615,11 +613,6 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         if constexpr (MD) return md_reg ? (i ? __builtin_amdgcn_readlane(mw.T, i - 1) : 0)
                                         : __builtin_amdgcn_readfirstlane(sT[i]);
         else return load_uniform(T, i);
-    };
-    auto Pat = [&](int32_t i) -> int32_t {
-        if constexpr (MD) return md_reg ? (i ? __builtin_amdgcn_readlane(mw.P, i - 1) : 0)
-                                        : __builtin_amdgcn_readfirstlane(sP[i]);
-        else return load_uniform(a.kv_indptr, i);
     };
     // MD: the page id at page k of request sg from the page table, clamped
     // into the pool
@@ -695,7 +688,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             it.lo = lo;
             it.hi = hi;
             it.c0 = 0;
-            it.pb = Pat(sg);
+            it.pb = MD ? 0 : load_uniform(a.kv_indptr, sg);  // MD reads the page table instead
             it.t0 = lo;
             return;
         }
