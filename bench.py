@@ -300,6 +300,20 @@ def bench_verify(spec, iters: int, warm: int = 10):
     return out
 
 
+def bench_verify_drafts(iters: int):
+    """bench_verify on the Llama-shaped verify batch with 4 and 8 chained
+    draft tokens per request (contexts of 512-4096 tokens)."""
+    import workloads
+    out = {}
+    for n_draft in (4, 8):
+        vs = workloads.EXTRA["llama3_8b_verify"]
+        vs = vs.replace(name=vs.name.replace("_n4", f"_n{n_draft}"), new_len_args=(n_draft, n_draft),
+                        prefix_len_args=(512 - n_draft, 4096 - n_draft))
+        out[f"n{n_draft}"] = bench_verify(vs, iters)
+        log(f"verify, {n_draft} draft tokens: {out[f'n{n_draft}']}")
+    return out
+
+
 def bench_graph_step(spec, iters: int):
     """The headline step (one forward_with_metadata call with the cache
     write) captured once per copy of pools and metadata in a HIP graph and
@@ -449,7 +463,7 @@ def main():
         elif args.only == "asym_decode":
             res = bench_decode_kernel(workloads.EXTRA["asym_decode"], args.steps)
         elif args.only == "verify":
-            res = bench_verify(workloads.EXTRA["llama3_8b_verify"], args.steps)
+            res = bench_verify_drafts(args.steps)
         elif args.only == "graph":
             res = bench_graph_step(workloads.WORKLOADS["llama3_8b_decode"], args.steps)
         else:
@@ -556,13 +570,7 @@ def main():
         result["asym_decode"] = bench_decode_kernel(workloads.EXTRA["asym_decode"], args.steps)
         log(f"decode, 192/128 widths: {result['asym_decode']}")
         # speculative verify through the decode path and the extend path
-        result["verify"] = {}
-        for n_draft in (4, 8):
-            vs = workloads.EXTRA["llama3_8b_verify"]
-            vs = vs.replace(name=vs.name.replace("_n4", f"_n{n_draft}"), new_len_args=(n_draft, n_draft),
-                            prefix_len_args=(512 - n_draft, 4096 - n_draft))
-            result["verify"][f"n{n_draft}"] = bench_verify(vs, args.steps)
-            log(f"verify, {n_draft} draft tokens: {result['verify'][f'n{n_draft}']}")
+        result["verify"] = bench_verify_drafts(args.steps)
         # the headline step replayed from a HIP graph
         result["graph_step"] = bench_graph_step(spec, args.steps)
         log(f"step from a HIP graph: {result['graph_step']}")

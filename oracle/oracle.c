@@ -17,6 +17,13 @@
  * head h / (Hq/Hkv)) and bottom-right causal alignment for extend (query i
  * of a request with prefix p sees keys 0..p+i).
  *
+ * Parity unpinned by the pages for two conventions: the head grouping
+ * (contiguous groups) and the causal alignment (bottom-right) are readings,
+ * not printed there.  The tests pin the oracle to them through torch's CPU
+ * scaled-dot-product attention with explicit head repetition and an explicit
+ * boolean mask, and through the grouping and causal-edit invariants; that
+ * fixes the arithmetic, not the reading.
+ *
  * Everything is fp64 with an explicit per-token page gather and a two-pass
  * softmax (max first, then exponentials); no blocking, no online softmax.
  *

@@ -26,6 +26,7 @@ struct pka_ctx {
     int32_t ext_tq;      // extend query tokens per work item
     std::atomic<int32_t> nwg{0};  // decode shares (from the device's CU count)
     std::atomic<int32_t> spw{0};  // decode shares per workgroup
+    std::atomic<int32_t> packed8{0};  // 8-wave decode workgroups resident per CU
     std::atomic<int32_t> md_fits{-1};  // decode with in-kernel metadata keeps the occupancy (-1: unknown)
 };
 
@@ -85,6 +86,8 @@ pka_status decode_wgs(const pka_ctx* ctx, int32_t* out, int32_t* spw_out = nullp
         if (per_cu < 1) per_cu = 1;
         v = std::min<int32_t>(pka::DEC_MAX_WG, std::max(1, cus * per_cu));
         pka_ctx* c = const_cast<pka_ctx*>(ctx);
+        c->packed8.store(kv != PKA_F32 ? pka::decode_blocks_per_cu(kv, ctx->dk, ctx->dv, 8) : 0,
+                         std::memory_order_relaxed);
         c->spw.store(spw, std::memory_order_relaxed);
         c->nwg.store(v, std::memory_order_release);
     }
@@ -103,6 +106,47 @@ bool is_extend_like(pka_forward_mode m) {
 int32_t decode_qslots(pka_forward_mode m, int32_t num_q_tokens) {
     if (m == PKA_MODE_DECODE) return 1;
     return std::max(1, std::min<int32_t>(pka::DEC_MAX_Q, num_q_tokens));
+}
+
+// Waves per head group on the decode path.  A verify batch whose query
+// columns (tokens x heads of a group) need several 16-column passes gives
+// them to up to DEC_MAX_CSPLIT waves of one workgroup that read the same
+// tiles side by side, instead of one wave reading them once per pass.  The
+// split follows the average tokens per request; a request with fewer
+// leaves the surplus waves idle over its tiles.  bf16 / fp8 caches only.
+int32_t decode_csplit(const pka_ctx* ctx, const pka_batch* md) {
+    if (ctx->cfg.kv_dtype == PKA_F32 || md->batch <= 0) return 1;
+    const int32_t qslots = decode_qslots(md->mode, md->num_q_tokens);
+    if (qslots <= 1) return 1;
+    const int32_t nq = std::min<int32_t>(qslots, (md->num_q_tokens + md->batch - 1) / md->batch);
+    const int32_t passes = (nq * std::min<int32_t>(ctx->G, 16) + 15) / 16;
+    return std::max<int32_t>(1, std::min<int32_t>(passes, pka::DEC_MAX_CSPLIT));
+}
+
+// Launch shape of a decode call with column split cs: waves per share in a
+// workgroup (wpb) and shares per workgroup (spw).  A share then needs cs
+// times the waves, so the partition is cut into nwg / cs shares
+// (batch_shares) and all of them stay resident at once.
+void decode_shape(const pka_ctx* ctx, int32_t cs, int32_t base_spw, int* wpb, int* spw) {
+    if (cs <= 1) {
+        *wpb = decode_wpb(ctx);
+        *spw = base_spw;
+        return;
+    }
+    const int units = ctx->cfg.num_kv_heads * ctx->qgroups * cs;
+    int w = 8;
+    while (units % w) w >>= 1;
+    *wpb = w;
+    *spw = w < 8 && ctx->packed8.load(std::memory_order_relaxed) >= 1 ? 8 / w : 1;
+}
+
+// Decode shares of a batch's partition (one resident round of the launch that
+// will serve it) and, for the plain launch shape, shares per workgroup.  The
+// metadata and the decode call derive it from the same batch sizes.
+pka_status batch_shares(const pka_ctx* ctx, const pka_batch* md, int32_t* nwg, int32_t* spw = nullptr) {
+    pka_status s = decode_wgs(ctx, nwg, spw);
+    if (s == PKA_OK) *nwg = std::max<int32_t>(1, *nwg / decode_csplit(ctx, md));
+    return s;
 }
 
 int64_t decode_ws_bytes(const pka_ctx* ctx, int32_t B, int32_t nwg, int32_t qslots) {
@@ -152,6 +196,7 @@ pka::AttnArgs attn_args(const pka_ctx* ctx, const pka_batch* md, const void* q, 
     a.page_shift = ctx->page_shift;
     a.num_pages = c.num_pages;
     a.spw = 1;
+    a.csplit = 1;
     const float k_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f;
     a.scale_log2 = c.scale * 1.4426950408889634f * k_scale;
     a.v_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f;
@@ -176,7 +221,7 @@ pka_status check_attn(const pka_ctx* ctx, const pka_batch* md, const void* q, co
 pka_status decode_args(const pka_ctx* ctx, const pka_batch* md, const void* q, const void* k_pool,
                        const void* v_pool, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, bool write_new, const void* k_new, const void* v_new,
-                       pka::AttnArgs* args) {
+                       pka::AttnArgs* args, int* wpb_out) {
     pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
     if (s != PKA_OK) return s;
     if (write_new && (!k_new || !v_new)) return fail(PKA_ERR_INVALID_ARG, "null K/V pointer");
@@ -186,14 +231,17 @@ pka_status decode_args(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     if (write_new && qslots != 1)
         return fail(PKA_ERR_INVALID_ARG, "the fused cache write serves decode batches only");
     int32_t nwg = 0, spw = 1;
-    if ((s = decode_wgs(ctx, &nwg, &spw)) != PKA_OK) return s;
+    if ((s = batch_shares(ctx, md, &nwg, &spw)) != PKA_OK) return s;
     const int64_t need = decode_ws_bytes(ctx, md->batch, nwg, qslots);
     if (!workspace || (int64_t)workspace_bytes < need || !aligned16(workspace))
         return fail(PKA_ERR_WORKSPACE, "decode needs %lld workspace bytes (16-byte aligned), got %zu",
                     (long long)need, workspace_bytes);
     pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
+    int wpb = 1, sp = 1;
+    a.csplit = decode_csplit(ctx, md);  // 1 unless several query rows per request
+    decode_shape(ctx, a.csplit, spw, &wpb, &sp);
     a.nwg = nwg;
-    a.spw = spw;
+    a.spw = sp;
     a.qslots = qslots;
     a.ws_o = (float*)workspace;
     a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * qslots * ctx->cfg.num_q_heads * ctx->dv;
@@ -207,6 +255,7 @@ pka_status decode_args(const pka_ctx* ctx, const pka_batch* md, const void* q, c
         a.v_inv = 1.0f / (c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f);
     }
     *args = a;
+    *wpb_out = wpb;
     return PKA_OK;
 }
 
@@ -218,11 +267,12 @@ pka_status decode_call(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     if (s != PKA_OK) return s;
     if (md->mode == PKA_MODE_IDLE || md->batch == 0) return PKA_OK;
     pka::AttnArgs a;
+    int wpb = 1;
     if ((s = decode_args(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, write_new,
-                         k_new, v_new, &a)) != PKA_OK)
+                         k_new, v_new, &a, &wpb)) != PKA_OK)
         return s;
-    hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
-                                      decode_wpb(ctx), (hipStream_t)stream);
+    hipError_t e = pka::launch_decode(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a, wpb,
+                                      (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
 }
 
@@ -250,7 +300,7 @@ pka_status meta_args(const pka_ctx* ctx, const int32_t* seq_lens, const int32_t*
     a.page_shift = ctx->page_shift;
     a.num_pages = ctx->cfg.num_pages;
     int32_t nwg = 0;
-    if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+    if ((s = batch_shares(ctx, md, &nwg)) != PKA_OK) return s;
     a.nwg = nwg;
     a.ext_tq = ctx->ext_tq;
     a.is_decode = md->mode == PKA_MODE_DECODE;
@@ -285,7 +335,7 @@ pka_status forward_checks(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_at
                     (int)md->mode, (int)mode);
     if (*path == PKA_PATH_DECODE) {
         int32_t nwg = 0;
-        if ((s = decode_wgs(ctx, &nwg)) != PKA_OK) return s;
+        if ((s = batch_shares(ctx, md, &nwg)) != PKA_OK) return s;
         if (!workspace ||
             (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg, decode_qslots(md->mode, md->num_q_tokens)))
             return fail(PKA_ERR_WORKSPACE, "decode workspace too small");
@@ -533,11 +583,12 @@ pka_status pka_forward_with_metadata(const pka_ctx* ctx, pka_forward_mode mode,
         // one decode launch builds the metadata, writes the new tokens and
         // attends; then the merge
         pka::AttnArgs a;
+        int wpb = 1;
         if ((s = decode_args(ctx, md, q, k_pool, v_pool, out, lse, workspace, workspace_bytes, save_kv != 0,
-                             k_new, v_new, &a)) != PKA_OK)
+                             k_new, v_new, &a, &wpb)) != PKA_OK)
             return s;
         hipError_t e = pka::launch_decode_md(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a, m,
-                                             decode_wpb(ctx), (hipStream_t)stream);
+                                             wpb, (hipStream_t)stream);
         return e == hipSuccess ? PKA_OK : hip_fail(e, "decode launch");
     }
     hipError_t e = pka::launch_metadata(m, (hipStream_t)stream);

@@ -505,9 +505,14 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wpb = waves / a.spw;
     const int unit = blockIdx.y * wpb + wv % wpb;
-    const int g = unit / a.qgroups;
-    const int h0 = g * a.G + (unit % a.qgroups) * 16;
-    const int nh = min(16, a.G - (unit % a.qgroups) * 16);
+    // unit = (KV head g, group of up to 16 of its query heads, column split
+    // ps): with MQ the csplit waves of one head group take its 16-column
+    // passes in turn (pass k goes to wave k % csplit), side by side in one
+    // workgroup, so they read the same tiles at the same time
+    const int ps = unit % a.csplit, uh = unit / a.csplit;
+    const int g = uh / a.qgroups;
+    const int h0 = g * a.G + (uh % a.qgroups) * 16;
+    const int nh = min(16, a.G - (uh % a.qgroups) * 16);
 
     // this wave's LDS: the K tile, then the queries of the next unit; after
     // the waves' regions, one progress word per wave
@@ -682,12 +687,13 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
                 const int32_t nb = load_uniform(a.qo_indptr, sg + 1) - load_uniform(a.qo_indptr, sg);
                 if (nb > a.qslots && lo == 0 && lane == 0 && unit == 0)
                     atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_LENGTH);
-                if (min(nb, a.qslots) <= 0) continue;  // no query rows
+                // no query rows, or none in this wave's passes
+                if (16 * ps >= min(nb, a.qslots) * nh) continue;
             }
             it.seg = sg;
             it.lo = lo;
             it.hi = hi;
-            it.c0 = 0;
+            it.c0 = 16 * ps;
             it.pb = MD ? 0 : load_uniform(a.kv_indptr, sg);  // MD reads the page table instead
             it.t0 = lo;
             return;
@@ -701,8 +707,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         if (cur.seg >= a.B) return;
         nx.t0 = cur.t0 + DEC_TILE;
         if (nx.t0 < cur.hi) return;
-        if (MQ && cur.c0 + 16 < rows_of(cur.seg).nq * nh) {
-            nx.c0 = cur.c0 + 16;
+        if (MQ && cur.c0 + 16 * a.csplit < rows_of(cur.seg).nq * nh) {
+            nx.c0 = cur.c0 + 16 * a.csplit;
             nx.t0 = cur.lo;
         } else {
             open_piece(cur.seg + 1, nx);
@@ -889,8 +895,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
 }
 
 // fp32 cache: a plain VALU variant with the same work partition (lanes over
-// head_dim, one token at a time, 16 columns per pass as in the MFMA variant).
-// Used for fp32 workloads.
+// head_dim, one token at a time, 16 columns per pass as in the MFMA variant;
+// its launches have csplit 1).  Used for fp32 workloads.
 template <int DK, int DV, bool MQ>
 __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
     constexpr int EPK = DK / 64, EPV = DV / 64;  // key and value dims per lane
@@ -1159,7 +1165,7 @@ hipError_t launch_merge(pka_dtype q, const AttnArgs& a, const MetaArgs* md, hipS
 
 template <int DK, int DV>
 hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb, hipStream_t s) {
-    const int units = a.Hkv * a.qgroups;
+    const int units = a.Hkv * a.qgroups * a.csplit;
     const int waves = wpb * a.spw;
     const dim3 grid((a.nwg + a.spw - 1) / a.spw, units / wpb);
     const dim3 block(64 * waves);
@@ -1185,7 +1191,7 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
 template <int DK, int DV>
 hipError_t launch_decode_md_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, const MetaArgs& m, int wpb,
                               hipStream_t s) {
-    const int units = a.Hkv * a.qgroups;
+    const int units = a.Hkv * a.qgroups * a.csplit;
     const int waves = wpb * a.spw;
     const dim3 grid((a.nwg + a.spw - 1) / a.spw, units / wpb);
     const dim3 block(64 * waves);

@@ -49,6 +49,8 @@ __host__ __device__ inline int64_t share_of(int64_t t, int64_t q, int64_t r) {
 constexpr int DEC_MAX_WG = 2048;
 // Most query tokens per request on the decode path (speculative verify).
 constexpr int DEC_MAX_Q = 16;
+// Most waves that share one head group's column passes (speculative verify).
+constexpr int DEC_MAX_CSPLIT = 4;
 
 // plan offsets that depend on the batch size: the token prefix F[b] = sum of
 // L over requests before b, the tile prefix T[b] = sum of ceil(L / DEC_TILE)
@@ -162,7 +164,8 @@ struct AttnArgs {
     int32_t Hq;
     int32_t Hkv;
     int32_t G;
-    int32_t qgroups;  // ceil(G / 16): waves per KV head
+    int32_t qgroups;  // ceil(G / 16): head groups per KV head
+    int32_t csplit;   // decode waves per head group (MQ: they take its column passes in turn)
     int32_t page_shift;
     int32_t num_pages;
     int32_t nwg;       // decode shares (the partition's workgroup count)

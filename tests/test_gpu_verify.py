@@ -71,6 +71,20 @@ def test_verify_on_decode_path(name, spec, mode):
     _check(prob, layout, values, f"{name}/{mode}")
 
 
+@pytest.mark.parametrize("name,spec", [
+    # 8 tokens x 4 heads = 32 columns: two waves per KV head take the passes
+    ("llama_n8_g4", BASE.replace(batch=64, new_len_args=(8, 8), prefix_len_args=(0, 600), seed=91)),
+    # 4 tokens x 16 heads = 64 columns: four waves per KV head, fp8 cache
+    ("fp8_n4_g16", BASE.replace(batch=9, num_q_heads=64, num_kv_heads=4, page_size=64, kv_dtype="fp8",
+                                new_len_args=(4, 4), prefix_len_args=(0, 2000), seed=92)),
+])
+def test_verify_column_passes_in_parallel_waves(name, spec):
+    """Uniform draft lengths whose columns need several 16-column passes:
+    the passes go to parallel waves of one workgroup."""
+    prob, layout, values = _verify_problem(spec)
+    _check(prob, layout, values, name)
+
+
 def test_verify_long_requests_are_split_and_merged():
     """Long contexts spread over many workgroups: every query token's rows
     come from partials, including pieces where some tokens see no key."""
