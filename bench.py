@@ -357,7 +357,11 @@ EXTEND_WARM = 20
 
 
 def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16", spec=None,
-                 warm: int = EXTEND_WARM):
+                 warm: int = EXTEND_WARM, constant: bool = False):
+    """Extend TFLOP/s on one workload.  constant: Q, K and V all 1/16 instead
+    of N(0,1) -- the same instruction stream with operand bits that barely
+    toggle, so the clock is not held down by the power limit (a diagnostic
+    beside the bf16 GEMM reference, never the headline figure)."""
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
@@ -365,7 +369,11 @@ def bench_extend(iters: int, gpu_state: bool = True, kv_dtype: str = "bf16", spe
     if kv_dtype != spec.kv_dtype:
         spec = spec.replace(name=spec.name.replace("extend_bf16", f"extend_{kv_dtype}kv"), kv_dtype=kv_dtype)
     layout = workloads.make_layout(spec)
-    prob = GpuProblem(layout)
+    values = workloads.make_values(layout, device="cuda")
+    if constant:
+        for t in (values.q, values.k_all, values.v_all):
+            t.fill_(0.0625)
+    prob = GpuProblem(layout, values)
     prob.attention_step(save=True)
     torch.cuda.synchronize()
     call = lambda i: prob.attention_step(save=False, lse=False)
@@ -556,6 +564,9 @@ def main():
         result["extend"]["frac_of_random_gemm"] = round(
             result["extend"]["TFLOPs"] / result["mfma_reference"]["random_TFLOPs"], 4)
         log(f"extend: {result['extend']}")
+        c = bench_extend(args.steps, constant=True)
+        result["extend_constant_operands"] = {k: c[k] for k in ("TFLOPs", "frac_mfma_peak", "ms", "gpu_state")}
+        log(f"extend on constant operands (power diagnostic): {result['extend_constant_operands']}")
         result["extend_fp8kv"] = bench_extend(args.steps, gpu_state=False, kv_dtype="fp8")
         log(f"extend over an fp8 cache: {result['extend_fp8kv']}")
         log(f"bf16 GEMM reference: {result['mfma_reference']}")
