@@ -40,6 +40,8 @@ CASES = {
     "d64_p4": W["llama3_8b_decode"].replace(batch=5, head_dim=64, page_size=4, seq_len_args=(1, 500), seed=85),
     "asym_p128": W["llama3_8b_decode"].replace(batch=5, num_q_heads=16, num_kv_heads=16, head_dim=192,
                                                v_head_dim=128, page_size=128, seq_len_args=(1, 700), seed=86),
+    "b1_long_p16": W["llama3_8b_decode"].replace(batch=1, seq_len_kind="fixed", seq_len_args=(20000,), seed=93),
+    "b65_p16": W["llama3_8b_decode"].replace(batch=65, seq_len_args=(1, 300), seed=94),  # first LDS-prefix size
     "b300_tiny_p2": W["llama3_8b_decode"].replace(batch=300, page_size=2, seq_len_args=(1, 5), seed=87),
     "b512_p16": W["llama3_8b_decode"].replace(batch=512, seq_len_args=(1, 60), seed=88),
     # beyond the in-kernel limit: metadata kernel, then the forward
