@@ -486,14 +486,15 @@ typedef __attribute__((address_space(3))) const int32_t lds_i32_t;
 // of token i go to slot (b + w) * qslots + i.
 //
 // MD: the kernel builds the batch's metadata itself (decode batches of at
-// most DEC_MD_MAX_B requests, m set).  Every workgroup scans the lengths into
-// LDS and its waves read page ids straight from the page table; workgroup 0
-// writes the batch-wide arrays, and the wave of each share that serves unit 0
-// writes the share's first request and its page flags (kv_indices and the
-// new tokens' slots are left to the merge, so no store waits in the tile
-// stream: stores count in vmcnt like loads).  The partition and the page ids
-// are those the metadata kernel would produce, so the outputs are
-// bit-identical to running it first.
+// most DEC_MD_MAX_B requests, m set).  Every wave scans the lengths itself in
+// registers (up to 64 requests), or every workgroup into LDS (more), and the
+// waves read page ids straight from the page table.  As the waves exit, wave
+// 0 of workgroup 0 writes the batch-wide arrays and the wave of each share
+// that serves unit 0 the share's first request and its page flags;
+// kv_indices and the new tokens' slots are left to the merge, so no store
+// waits in the tile stream (stores count in vmcnt like loads).  The
+// partition and the page ids are those the metadata kernel would produce,
+// so the outputs are bit-identical to running it first.
 template <int DK, int DV, bool FP8, bool MQ, bool MD>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m) {
     static_assert(!(MQ && MD), "metadata is built in-kernel for one query per request only");
