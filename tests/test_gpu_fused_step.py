@@ -42,6 +42,10 @@ CASES = {
                                                v_head_dim=128, page_size=128, seq_len_args=(1, 700), seed=86),
     "b1_long_p16": W["llama3_8b_decode"].replace(batch=1, seq_len_kind="fixed", seq_len_args=(20000,), seed=93),
     "b65_p16": W["llama3_8b_decode"].replace(batch=65, seq_len_args=(1, 300), seed=94),  # first LDS-prefix size
+    "p256": W["llama3_8b_decode"].replace(batch=6, page_size=256, seq_len_args=(1, 1500), seed=95),
+    "p32_fp8": W["long_fp8_decode"].replace(batch=5, page_size=32, seq_len_args=(1, 900), seed=96),
+    "g32_two_head_groups": W["llama3_8b_decode"].replace(batch=7, num_q_heads=64, num_kv_heads=2,
+                                                         seq_len_args=(1, 800), seed=97),
     "b300_tiny_p2": W["llama3_8b_decode"].replace(batch=300, page_size=2, seq_len_args=(1, 5), seed=87),
     "b512_p16": W["llama3_8b_decode"].replace(batch=512, seq_len_args=(1, 60), seed=88),
     # beyond the in-kernel limit: metadata kernel, then the forward
