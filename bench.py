@@ -229,6 +229,34 @@ def cpu_baseline(layout, values, budget_s: float = 20.0):
             "cpu": cpu_model()}
 
 
+def cpu_baseline_extend(layout, values, budget_s: float = 10.0, stride: int = 8):
+    """The oracle on a bounded sample of the extend workload: every stride-th
+    new token of whole requests, all heads, until about budget_s of work;
+    GFLOP/s with the same causal flop count as the GPU figure."""
+    from tests.oracle_ref import oracle_requests
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    spec = layout.spec
+    flops, t_total, toks, reqs = 0.0, 0.0, 0, 0
+    for b in range(layout.batch):
+        L, n = int(layout.seq_lens[b]), int(layout.extend_lens[b])
+        p = L - n
+        ts = list(range(0, n, stride))
+        t0 = time.perf_counter()
+        oracle_requests(layout, values, [b], tokens=lambda nb, ts=ts: ts, threads=threads)
+        t_total += time.perf_counter() - t0
+        flops += sum(2.0 * (spec.head_dim + spec.value_dim) * spec.num_q_heads * (p + i + 1) for i in ts)
+        toks += len(ts)
+        reqs += 1
+        if t_total >= budget_s:
+            break
+    return {"value": round(flops / t_total / 1e9, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"every {stride}th new token of {reqs} of {layout.batch} requests ({toks} query tokens, "
+                      f"all {spec.num_q_heads} heads), fp64 C oracle, {oracle.max_threads()} OpenMP threads, "
+                      f"wall {t_total:.2f} s incl. per-request cache repacking",
+            "cpu": cpu_model()}
+
+
 def bench_decode_kernel(spec, iters: int, warm: int = 10):
     """Decode figures for one workload on two copies of pools and metadata
     used alternately (as for the headline batch): attn_decode alone on
@@ -589,6 +617,14 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host cores ...")
         result["cpu_baseline"] = cpu_baseline(layout, values, args.cpu_budget)
+        result["cpu_baseline"]["gpu_speedup"] = round(result["value"] / result["cpu_baseline"]["value"], 1)
+        if not args.no_extras:
+            elayout = workloads.make_layout(workloads.WORKLOADS["llama3_8b_extend"])
+            evalues = workloads.make_values(elayout, device="cuda")
+            cb = cpu_baseline_extend(elayout, evalues, min(args.cpu_budget, 10.0))
+            cb["gpu_speedup"] = round(result["extend"]["TFLOPs"] * 1e3 / cb["value"], 1)
+            result["extend"]["cpu_baseline"] = cb
+            log(f"extend oracle: {cb}")
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
