@@ -86,7 +86,8 @@ class GpuProblem:
         self.metadata_step()
         self.attention_step(save=True)
 
-    def fused_step(self, save: bool = True, lse: bool = True, page_table=None, seq_lens=None):
+    def fused_step(self, save: bool = True, lse: bool = True, page_table=None, seq_lens=None,
+                   spec_mode: str = "prefill"):
         """The same pass as step(), through the one-call entry point
         (pka_forward_with_metadata)."""
         pt = self.page_table if page_table is None else page_table
@@ -94,7 +95,8 @@ class GpuProblem:
         pka.forward_with_metadata(self.ctx, self.mode, self.md, sl,
                                   None if self.mode == "decode" else self.extend_lens, pt,
                                   self.values.q, self.k_new, self.v_new, self.k_pool, self.v_pool,
-                                  self.out, self.lse if lse else None, save_kv_cache=save)
+                                  self.out, self.lse if lse else None, save_kv_cache=save,
+                                  spec_mode=spec_mode)
 
     def out_np(self) -> np.ndarray:
         return self.out.float().cpu().numpy().astype(np.float64)

@@ -108,6 +108,35 @@ def test_one_call_equals_metadata_then_forward(name):
     np.testing.assert_allclose(prob.lse_np(), want_lse, rtol=0, atol=LSE_ATOL)
 
 
+@pytest.mark.parametrize("spec_mode", ["decode", "prefill"])
+def test_verify_batch_in_one_call(spec_mode):
+    """A target-verify batch (8 draft tokens per request) through the one
+    call: metadata kernel, cache write and the path the speculative attention
+    mode picks, bit-identical to init_metadata + forward."""
+    spec = W["llama3_8b_extend"].replace(batch=12, new_len_args=(8, 8), prefix_len_args=(0, 700), seed=98)
+    layout = workloads.make_layout(spec)
+    values = workloads.make_values(layout, device="cuda")
+    probs = []
+    for _ in range(2):
+        p = GpuProblem(layout, values, prefix_only=True)
+        p.mode = "target_verify"
+        p.md = pka.Batch(p.ctx, "target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages)
+        probs.append(p)
+    ref, prob = probs
+    ref.metadata_step()
+    ref.attention_step(save=True, spec_mode=spec_mode)
+    _scrub(prob)
+    prob.fused_step(spec_mode=spec_mode)
+    torch.cuda.synchronize()
+    assert ref.md.status() == 0 and prob.md.status() == 0
+    for k in MD_ARRAYS:
+        assert torch.equal(_md_arrays(prob)[k], _md_arrays(ref)[k]), k
+    assert torch.equal(prob.out, ref.out) and torch.equal(prob.lse, ref.lse)
+    want, _ = oracle_full(layout, values)
+    max_abs, rel = errors(prob.out_np(), want)
+    assert max_abs <= TOL["bf16"][0] and rel <= TOL["bf16"][1]
+
+
 def test_plan_serves_a_later_decode_call():
     """Metadata left by the one-call path serves the plain decode call of
     another layer: same result as the step itself."""
