@@ -82,24 +82,36 @@ __device__ inline void emit_rows(const f32x4_t (&O)[D / 16], float inv, int j, E
     emit(v, 4 * CPL * j);
 }
 
-// Cache write of one request's new token (query row qr, pool slot `slot`)
-// for KV head g, fused into decode: K on lanes 0..31, V on lanes 32..63, 8
-// elements per lane (bf16 copy or bf16 -> fp8 quantisation).  The store is
-// waited for before the wave reads the pool, so the wave's own later load of
-// that slot sees it.
+// Cache write of one request's new token for KV head g, fused into decode,
+// in two halves.  load_new_token reads this lane's part of the row (query row
+// qr): K on lanes 0..31, V on lanes 32..63, 8 elements per lane; lanes past a
+// row's width read nothing.
+template <int DK, int DV>
+__device__ inline u32x4_t load_new_token(const AttnArgs& a, int32_t qr, int g, int lane) {
+    const bool is_v = lane >= 32;
+    const int D = is_v ? DV : DK;
+    const int e = (lane & 31) * 8;  // first element of this lane
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (e < D)
+        w = *(const u32x4_t*)((const __bf16*)(is_v ? a.v_new : a.k_new) + ((int64_t)qr * a.Hkv + g) * D + e);
+    return w;
+}
+
+// store_new_token writes it to pool slot `slot` (bf16 copy or bf16 -> fp8
+// quantisation).  Nothing waits for the store: a wave's vector memory
+// instructions reach memory in issue order, so the wave's own later load of
+// that slot (the only one in the launch) returns the new row.
 template <int DK, int DV, bool FP8>
-__device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int32_t slot, int g, int lane) {
+__device__ inline void store_new_token(const AttnArgs& a, u32x4_t w, int32_t slot, int g, int lane) {
     if (slot < 0 || slot >= a.pool_slots) {
         if (lane == 0) atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_PAGE);
         return;
     }
     const bool is_v = lane >= 32;
     const int D = is_v ? DV : DK;
-    const int e = (lane & 31) * 8;  // first element of this lane
+    const int e = (lane & 31) * 8;
     if (e < D) {
-        const int64_t src = ((int64_t)qr * a.Hkv + g) * D + e;
         const int64_t dst = ((int64_t)slot * a.Hkv + g) * D + e;
-        const u32x4_t w = *(const u32x4_t*)((const __bf16*)(is_v ? a.v_new : a.k_new) + src);
         if constexpr (FP8) {
             const float inv = is_v ? a.v_inv : a.k_inv;
             *(u32x2_t*)((uint8_t*)(is_v ? a.v_pool : a.k_pool) + dst) =
@@ -108,7 +120,6 @@ __device__ inline void write_new_token(const AttnArgs& a, int32_t qr, int32_t sl
             *(u32x4_t*)((__bf16*)(is_v ? a.v_pool : a.k_pool) + dst) = w;
         }
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the stores have completed
 }
 
 // DK: key (and query) width; DV: value (and output) width.
@@ -755,20 +766,34 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             }
         }
     };
-    // the piece holding a request's last position writes its new token first
-    auto new_token = [&](const It& u) {
-        if constexpr (MD) {
+    // The wave whose tile holds a request's last position writes the new
+    // token just before that tile's loads go out.  For 128-wide heads the row
+    // and the slot are read with the loads of the tile before (prep_new_token,
+    // waited for with them), so the store waits for nothing unless the tile
+    // is the wave's first; for the other widths they are read when the store
+    // is due, as holding them across a step would cost occupancy or spill
+    // registers.
+    constexpr bool EARLY = DK == 128;
+    struct NewTok {
+        u32x4_t w;
+        int32_t slot;
+        bool on;
+    };
+    auto prep_new_token = [&](const It& u, NewTok& t) {
+        t.on = false;
+        if constexpr (MD || !MQ) {
+            if (!a.k_new || u.seg >= a.B || u.t0 + DEC_TILE < u.hi) return;
             const Rows r = rows_of(u.seg);
-            if (a.k_new && u.hi == r.L) {
+            if (u.hi != r.L) return;
+            t.on = true;
+            t.w = load_new_token<DK, DV>(a, r.q0, g, lane);
+            if constexpr (MD) {
                 const int32_t pos = r.L - 1;
                 int32_t pg = load_uniform(m.page_table, (int64_t)u.seg * m.pt_stride + (pos >> a.page_shift));
                 pg = min(max(pg, 0), a.num_pages - 1);  // flagged where the tile reads it
-                write_new_token<DK, DV, FP8>(a, r.q0, (pg << a.page_shift) | (pos & (P - 1)), g, lane);
-            }
-        } else if constexpr (!MQ) {
-            if (a.k_new) {
-                const Rows r = rows_of(u.seg);
-                if (u.hi == r.L) write_new_token<DK, DV, FP8>(a, r.q0, a.out_cache_loc[r.q0], g, lane);
+                t.slot = (pg << a.page_shift) | (pos & (P - 1));
+            } else {
+                t.slot = a.out_cache_loc[r.q0];
             }
         }
     };
@@ -779,7 +804,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         md_close();
         return;
     }
-    new_token(cur);
+    NewTok nt;
+    prep_new_token(cur, nt);
+    if (nt.on) store_new_token<DK, DV, FP8>(a, nt.w, nt.slot, g, lane);
     VTile<DK, DV, FP8> A, Bt;
     {
         const int32_t s0 = slot_for(cur);
@@ -789,6 +816,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     fetch_q(cur);
     advance(cur, nx);
     int32_t s_nx = nx.seg < a.B ? slot_for(nx) : 0;
+    if constexpr (EARLY) prep_new_token(nx, nt);
     Rows crow = rows_of(cur.seg);  // query rows of cur's request
     Col col = column(cur, crow);
     bf16x8_t qop[S::KSTEPS];
@@ -845,7 +873,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     // before the next tile's go out, so one tile is in flight while
     // another is computed.
     auto step = [&](VTile<DK, DV, FP8>& X, VTile<DK, DV, FP8>& Y) -> bool {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile cur, its queries and nx's slots landed
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile cur, its queries, nx's new token landed
         asm volatile("" ::: "memory");       // LDS reads stay after the wait
         if (cur.t0 == cur.lo) take_q();      // cur opens its unit
         int32_t other = 0;
@@ -865,13 +893,20 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         }
         if (nx.seg < a.B) {
             const bool opens = nx.t0 == nx.lo;  // nx is the first tile of its unit
-            if (opens) new_token(nx);
+            if constexpr (EARLY) {
+                if (nt.on) store_new_token<DK, DV, FP8>(a, nt.w, nt.slot, g, lane);
+            } else {
+                NewTok t;
+                prep_new_token(nx, t);
+                if (t.on) store_new_token<DK, DV, FP8>(a, t.w, t.slot, g, lane);
+            }
             load_k<DK, DV, FP8>(kst, s_nx, kbase, krow);
             load_v(Y, s_nx, vbase, vrow, n, j);
             if (opens) fetch_q(nx);
         }
         advance(nx, nn);
         const int32_t s_nn = nn.seg < a.B ? slot_for(nn) : 0;
+        if constexpr (EARLY) prep_new_token(nn, nt);
         tile_update<DK, DV, FP8, MQ>(X, st, O, m2, lsum, col.kend - cur.t0, a.scale_log2, j);
         if (cur.t0 + DEC_TILE >= cur.hi) {  // last tile of its unit
             finish(cur);
