@@ -17,6 +17,7 @@ namespace pka {
 namespace {
 
 constexpr int SORT_MAX = 2048;  // extend items sorted in LDS (heaviest first)
+constexpr int RANK_MAX = 512;   // up to this many, by rank (no barriers) instead of bitonic
 constexpr int SCAN_THREADS = 256;  // small workgroups: cheap barriers, more of them share the gather
 
 // Inclusive block scan of NV int64 values per thread: a shuffle scan inside
@@ -227,14 +228,31 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         const int32_t tq = a.ext_tq;
         const int64_t cap = plan_ext_capacity(a.B, a.N, tq);
         int32_t* items = a.plan + plan_ext_items(a.B);
+        const bool fused = a.B <= FUSE_MAX_B;
         __shared__ int32_t s_count;
+        __shared__ int32_t sI[FUSE_MAX_B + 1];  // fused: each request's first item
+        __shared__ __align__(16) uint32_t keys[SORT_MAX];
         if (t == 0) s_count = 0;
         __syncthreads();
-        if (a.B <= FUSE_MAX_B) {
-            // pass 1: every request's first item (exclusive prefix of its
-            // tile count, from the LDS query prefix), then the items filled
-            // in parallel, each finding its request by binary search
-            __shared__ int32_t sI[FUSE_MAX_B + 1];
+        // sort key of item i = (request b, query tile ti): its weight, then
+        // the index (ties: lower index first); 0 is left for padding
+        auto key_of = [&](int32_t b, int32_t ti, int32_t i, int32_t L, int32_t n) {
+            const int32_t last = L - n + min((ti + 1) * tq, n);  // keys of the tile's last row
+            const uint32_t wgt = (uint32_t)min(last, (1 << 20) - 1);
+            return ((wgt << 11) | (uint32_t)(SORT_MAX - 1 - i)) + 1;
+        };
+        // fused: the request of item i, by binary search over sI
+        auto request_of = [&](int32_t i) {
+            int32_t lo = 0, hi = a.B - 1;  // largest b with sI[b] <= i
+            while (lo < hi) {
+                const int32_t mid = (lo + hi + 1) >> 1;
+                if (sI[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            return lo;
+        };
+        if (fused) {
+            // every request's first item (exclusive prefix of its tile
+            // count, from the LDS query prefix)
             for (int32_t base = 0; base < a.B; base += SCAN_THREADS) {
                 const int32_t b = base + t;
                 int64_t x[1] = {b < a.B ? (sQ[b + 1] - sQ[b] + tq - 1) / tq : 0};
@@ -247,18 +265,8 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
             }
             if (t == 0) sI[a.B] = s_count;
             __syncthreads();
-            const int32_t total = (int32_t)min((int64_t)s_count, cap);
-            for (int32_t slot = t; slot < total; slot += SCAN_THREADS) {
-                int32_t lo = 0, hi = a.B - 1;  // largest b with sI[b] <= slot
-                while (lo < hi) {
-                    const int32_t mid = (lo + hi + 1) >> 1;
-                    if (sI[mid] <= slot) lo = mid; else hi = mid - 1;
-                }
-                items[2 * slot] = lo;
-                items[2 * slot + 1] = slot - sI[lo];
-            }
         } else {
-            // pass 1 for large batches: serial over requests, tiles in parallel
+            // large batches: serial over requests, tiles in parallel
             for (int32_t b = 0; b < a.B; ++b) {
                 const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
                 const int32_t tiles = (q1 - q0 + tq - 1) / tq;
@@ -274,25 +282,52 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
                 __syncthreads();
             }
         }
-        __syncthreads();
         int32_t count = s_count;
         if (count > cap) { flags |= PKA_DEV_CAPACITY; count = (int32_t)cap; }
-        // sort by weight (descending) with a bitonic sort in LDS when small
-        __shared__ uint32_t keys[SORT_MAX];
-        if (count <= SORT_MAX && count > 1) {
+        if (fused && count > SORT_MAX) {
+            // too many to sort in LDS: request order
+            for (int32_t i = t; i < count; i += SCAN_THREADS) {
+                const int32_t b = request_of(i);
+                items[2 * i] = b;
+                items[2 * i + 1] = i - sI[b];
+            }
+        } else if (fused && count <= RANK_MAX) {
+            // few items: each one's place is the number of heavier keys
+            const int32_t c4 = (count + 3) & ~3;
+            for (int32_t i = t; i < c4; i += SCAN_THREADS) {
+                uint32_t key = 0;  // padding counts as lightest
+                if (i < count) {
+                    const int32_t b = request_of(i);
+                    key = key_of(b, i - sI[b], i, sLen[b], sQ[b + 1] - sQ[b]);
+                }
+                keys[i] = key;
+            }
+            __syncthreads();
+            for (int32_t i = t; i < count; i += SCAN_THREADS) {
+                const uint32_t k = keys[i];
+                int32_t r = 0;
+                for (int32_t j = 0; j < c4; j += 4) {
+                    const uint4 v = *(const uint4*)(keys + j);
+                    r += (v.x > k) + (v.y > k) + (v.z > k) + (v.w > k);
+                }
+                const int32_t b = request_of(i);
+                items[2 * r] = b;
+                items[2 * r + 1] = i - sI[b];
+            }
+        } else if (count <= SORT_MAX && count > 1) {
+            // bitonic sort in LDS (descending)
             int n2 = 1;
             while (n2 < count) n2 <<= 1;
             for (int i = t; i < n2; i += SCAN_THREADS) {
                 uint32_t key = 0;  // padding sorts last
                 if (i < count) {
-                    const int32_t b = items[2 * i], ti = items[2 * i + 1];
-                    const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
-                    const int32_t L = F[b + 1] - F[b];
-                    const int32_t n = q1 - q0;
-                    const int32_t last = L - n + min((ti + 1) * tq, n);  // keys of the tile's last row
-                    const uint32_t wgt = (uint32_t)min(last, (1 << 20) - 1);
-                    key = (wgt << 11) | (uint32_t)(SORT_MAX - 1 - i);  // ties: lower index first
-                    key = key + 1;  // keep 0 for padding
+                    if (fused) {
+                        const int32_t b = request_of(i);
+                        key = key_of(b, i - sI[b], i, sLen[b], sQ[b + 1] - sQ[b]);
+                    } else {
+                        const int32_t b = items[2 * i], ti = items[2 * i + 1];
+                        key = key_of(b, ti, i, F[b + 1] - F[b], a.qo_indptr[b + 1] - a.qo_indptr[b]);
+                    }
                 }
                 keys[i] = key;
             }
@@ -313,16 +348,24 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
                     __syncthreads();
                 }
             }
-            // rebuild the item list in sorted order
+            // the item list in sorted order (large batches stage the unsorted
+            // list through LDS first)
             for (int i = t; i < count; i += SCAN_THREADS) {
-                const uint32_t key = keys[i] - 1;
-                const int32_t src = SORT_MAX - 1 - (int32_t)(key & (SORT_MAX - 1));
-                sh[i] = ((int64_t)items[2 * src] << 32) | (uint32_t)items[2 * src + 1];
+                const int32_t src = SORT_MAX - 1 - (int32_t)((keys[i] - 1) & (SORT_MAX - 1));
+                if (fused) {
+                    const int32_t b = request_of(src);
+                    items[2 * i] = b;
+                    items[2 * i + 1] = src - sI[b];
+                } else {
+                    sh[i] = ((int64_t)items[2 * src] << 32) | (uint32_t)items[2 * src + 1];
+                }
             }
-            __syncthreads();
-            for (int i = t; i < count; i += SCAN_THREADS) {
-                items[2 * i] = (int32_t)(sh[i] >> 32);
-                items[2 * i + 1] = (int32_t)(sh[i] & 0xffffffff);
+            if (!fused) {
+                __syncthreads();
+                for (int i = t; i < count; i += SCAN_THREADS) {
+                    items[2 * i] = (int32_t)(sh[i] >> 32);
+                    items[2 * i + 1] = (int32_t)(sh[i] & 0xffffffff);
+                }
             }
         }
         if (t == 0) a.plan[PLAN_EXT_COUNT] = count;
