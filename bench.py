@@ -1,17 +1,19 @@
 """Benchmark of the paged KV attention path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch: per-batch metadata,
 the cache write of the new tokens (save_kv) and attention (split kernel +
-merge), on the Llama-3-8B-shaped decode workload (batch 64, 32/8 heads,
-head_dim 128, bf16, page size 16, seq_lens uniform in [512, 4096]), through
-the one-call entry point pka_forward_with_metadata (the decode launch builds
-the metadata itself); the same step as two calls (init_metadata, then
-forward) is reported beside it.  Inputs are resident in HBM before timing starts.  The JSON line
-reports KV bytes read per step / step time, the dominant kernel against the
-HBM roofline (HIP events on the stream the kernels run on), the oracle timed
-on the host cores, and the extend and the other decode workloads as extras.
+merge), through the one-call entry point pka_forward_with_metadata (the
+decode launch builds the metadata itself).  The headline workload is the
+largest single-GPU decode batch, Qwen3-235B-shaped (one layer on one GPU:
+batch 128, 64 query / 4 KV heads, head_dim 128, bf16, page size 1, seq_lens
+log-uniform in [2048, 32768], 1.42 M cached tokens); --workload picks another
+decode batch for the same measurement (profiling).  Inputs are resident in
+HBM before timing starts.  The JSON line reports KV bytes read per step /
+step time, the dominant launch against the HBM roofline (HIP events on the
+stream the kernels run on), the oracle timed on the host cores, and the
+other decode workloads, extend, verify and a graph-replayed step as extras.
 """
 from __future__ import annotations
 
@@ -459,16 +461,113 @@ def bench_copy(iters: int, nbytes: int = 1 << 30):
             "ms": round(ms, 4), "GBps_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}
 
 
+# The workload the headline line is quoted on: the largest single-GPU decode
+# batch (Qwen3-235B-shaped, one layer on one GPU, 1.42 M cached tokens).
+HEADLINE = "qwen3_235b_decode"
+
+
+def traffic_key(spec_name: str) -> str:
+    return "decode_" + spec_name.split("_decode")[0] + "_step"
+
+
+def bench_decode_step(spec, steps: int, warmup: int, extras: bool) -> dict:
+    """The whole step on one decode workload: per-batch metadata, the cache
+    write of the new tokens and attention (split kernel + merge), through the
+    one-call entry point pka_forward_with_metadata, on two copies of pools
+    and metadata used alternately (so the 256 MB Infinity Cache cannot serve
+    one step's KV from the previous step).  Returns the step time, the same
+    step as two calls, and the roofline record of the dominant launch."""
+    import torch
+    import workloads
+    from tests.gpu_problem import GpuProblem
+    layout = workloads.make_layout(spec)
+    log(f"workload {spec.name}: B={layout.batch} tokens={layout.total_tokens} pages={layout.kv_pages}")
+    values = workloads.make_values(layout, device="cuda")
+    probs = [GpuProblem(layout, values), GpuProblem(layout, values)]
+    torch.cuda.synchronize()
+
+    def timed_steps(step):
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    ms_step = timed_steps(lambda i: probs[i % 2].fused_step())
+    kvb = kv_bytes(layout)
+    for p in probs:
+        assert p.md.status() == 0, "device status flags set"
+    log(f"{spec.name}: step {ms_step:.4f} ms -> {kvb / ms_step / 1e6:.1f} GB/s KV read")
+    # the same step as two calls: the metadata kernel, then the forward
+    ms_two = timed_steps(lambda i: probs[i % 2].step())
+    for p in probs:
+        assert p.md.status() == 0, "device status flags set"
+    # dominant kernel: the step's decode launch (metadata built in the kernel)
+    # + the merge, HIP events on the stream they run on
+    attn_call = lambda i: probs[i % 2].fused_step(save=False, lse=False)
+    ms_attn = time_events(attn_call, steps)
+    attn_dist = time_per_call(attn_call, steps)
+    attn_state = gpu_state_under(attn_call) if extras else None
+    # the plain attn_decode call on metadata built beforehand, and the
+    # metadata kernel alone
+    ms_plain = time_events(lambda i: probs[i % 2].attention_step(save=False, lse=False), steps)
+    ms_meta = time_events(lambda i: probs[i % 2].metadata_step(), steps)
+    nbytes = decode_algorithmic_bytes(layout)
+    achieved = nbytes / (ms_attn * 1e-3) / 1e9
+    src = source_hash("decode.hip", "pka_internal.h", "fp8.h")
+    ctx = probs[0].ctx
+    variant = ctx.describe("decode", layout.batch, layout.num_q_tokens, with_metadata=True)
+    roof = {"bound": "hbm",
+            "kernel": "decode_mfma_kernel (metadata built in-kernel) + decode_merge_kernel "
+                      "(one forward_with_metadata call, no cache write)",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(traffic_key(spec.name), src),
+            "bytes_per_launch": nbytes, "ms_per_launch": round(ms_attn, 4),
+            "ms_per_launch_per_call": attn_dist,
+            "variant": variant,
+            "gpu_state": attn_state,
+            "source_hash": src}
+    if roof["traffic"]:
+        roof["traffic_over_algorithmic"] = round(roof["traffic"] / nbytes, 4)
+    log(f"{spec.name}: forward_with_metadata {ms_attn:.4f} ms -> {achieved:.1f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); attn_decode {ms_plain:.4f} ms; metadata {ms_meta:.4f} ms")
+    log(f"{spec.name}: resolved variant: {variant}")
+    out = {"layout": layout, "values": values, "ms_step": ms_step, "kv_bytes": kvb,
+           "value": kvb / (ms_step * 1e-3) / 1e9,
+           "config": {"workload": spec.name, "batch": layout.batch, "num_q_heads": spec.num_q_heads,
+                      "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+                      "page_size": spec.page_size, "kv_dtype": spec.kv_dtype,
+                      "kv_tokens": layout.total_tokens, "kv_bytes_per_step": kvb, "seed": spec.seed,
+                      "step": "forward_with_metadata(save_kv_cache=True): one decode launch builds the "
+                              "metadata, writes the new tokens and attends, then the merge",
+                      "two_call_step_ms": round(ms_two, 4),
+                      "two_call_step_GBps": round(kvb / ms_two / 1e6, 1),
+                      "attn_decode_ms": round(ms_plain, 4),
+                      "metadata_ms": round(ms_meta, 4)},
+           "roofline": roof}
+    del probs
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE,
+                    choices=["qwen3_235b_decode", "llama3_8b_decode", "long_fp8_decode", "l4_log_decode"],
+                    help="decode workload of the headline step (default: the Qwen3-235B-shaped batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extend / other decode figures and the clock and power sampling")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
-    ap.add_argument("--only", choices=["extend", "extend_fp8", "qwen3_235b_decode", "long_fp8_decode", "copy", "gemm",
+    ap.add_argument("--only", choices=["extend", "extend_fp8", "qwen3_235b_decode", "llama3_8b_decode",
+                                       "long_fp8_decode", "l4_log_decode", "copy", "gemm",
                                        "asym_extend", "asym_decode", "verify", "graph"], default=None,
                     help="run one extra leg alone (for profiling) and print its figures")
     args = ap.parse_args()
@@ -480,11 +579,11 @@ def main():
     import torch
     import workloads
     import paged_kv_attention_02_amd as pka
-    from tests.gpu_problem import GpuProblem
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pka.lib()  # fail loudly if the library is missing
+    all_specs = dict(workloads.WORKLOADS, **workloads.EXTRA)
     if args.only:
         if args.only == "copy":
             res = bench_copy(args.steps)
@@ -503,90 +602,35 @@ def main():
         elif args.only == "graph":
             res = bench_graph_step(workloads.WORKLOADS["llama3_8b_decode"], args.steps)
         else:
-            res = bench_decode_kernel(workloads.WORKLOADS[args.only], args.steps)
+            res = bench_decode_kernel(all_specs[args.only], args.steps)
         print(json.dumps(res), flush=True)
         return
 
-    spec = workloads.WORKLOADS["llama3_8b_decode"]
-    layout = workloads.make_layout(spec)
-    log(f"workload {spec.name}: B={layout.batch} tokens={layout.total_tokens} pages={layout.kv_pages}")
-    values = workloads.make_values(layout, device="cuda")
-    # two copies of the pools and metadata, used alternately, so the 256 MB
-    # Infinity Cache cannot serve one step's KV from the previous step
-    probs = [GpuProblem(layout, values), GpuProblem(layout, values)]
-    torch.cuda.synchronize()
-
-    def timed_steps(step):
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(i)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / args.steps
-
-    ms_step = timed_steps(lambda i: probs[i % 2].fused_step())
-    kvb = kv_bytes(layout)
-    value = kvb / (ms_step * 1e-3) / 1e9
-    for p in probs:
-        assert p.md.status() == 0, "device status flags set"
-    log(f"step {ms_step:.4f} ms -> {value:.1f} GB/s KV read")
-    # the same step as two calls: the metadata kernel, then the forward
-    ms_two = timed_steps(lambda i: probs[i % 2].step())
-    for p in probs:
-        assert p.md.status() == 0, "device status flags set"
-    log(f"two-call step {ms_two:.4f} ms -> {kvb / ms_two / 1e6:.1f} GB/s KV read")
-
-    # dominant kernel: the step's decode launch (metadata built in the kernel)
-    # + the merge, HIP events on the stream they run on
-    attn_call = lambda i: probs[i % 2].fused_step(save=False, lse=False)
-    ms_attn = time_events(attn_call, args.steps)
-    attn_dist = time_per_call(attn_call, args.steps)
-    attn_state = None if args.no_extras else gpu_state_under(attn_call)
-    # the plain attn_decode call on metadata built beforehand, and the
-    # metadata kernel alone
-    ms_plain = time_events(lambda i: probs[i % 2].attention_step(save=False, lse=False), args.steps)
-    ms_meta = time_events(lambda i: probs[i % 2].metadata_step(), args.steps)
-    nbytes = decode_algorithmic_bytes(layout)
-    achieved = nbytes / (ms_attn * 1e-3) / 1e9
-    src = source_hash("decode.hip", "pka_internal.h", "fp8.h")
-    roof = {"bound": "hbm",
-            "kernel": "decode_mfma_kernel (metadata built in-kernel) + decode_merge_kernel "
-                      "(one forward_with_metadata call)",
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles("decode_llama3_8b_step", src),
-            "bytes_per_launch": nbytes, "ms_per_launch": round(ms_attn, 4),
-            "ms_per_launch_per_call": attn_dist,
-            "variant": f"decode_mfma_kernel<{spec.head_dim}, {spec.kv_dtype} KV, in-kernel metadata> "
-                       "+ decode_merge_kernel",
-            "gpu_state": attn_state,
-            "source_hash": src}
-    log(f"forward_with_metadata {ms_attn:.4f} ms -> {achieved:.1f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% "
-        f"of peak); attn_decode {ms_plain:.4f} ms; metadata {ms_meta:.4f} ms")
-
+    spec = all_specs[args.workload]
+    head = bench_decode_step(spec, args.steps, args.warmup, extras=not args.no_extras)
+    layout, values = head.pop("layout"), head.pop("values")
     result = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": round(head["value"], 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_step"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": spec.name, "batch": layout.batch, "num_q_heads": spec.num_q_heads,
-                   "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
-                   "page_size": spec.page_size, "kv_tokens": layout.total_tokens,
-                   "kv_bytes_per_step": kvb, "seed": spec.seed,
-                   "step": "forward_with_metadata(save_kv_cache=True): one decode launch builds the metadata, "
-                           "writes the new tokens and attends, then the merge",
-                   "two_call_step_ms": round(ms_two, 4),
-                   "two_call_step_GBps": round(kvb / ms_two / 1e6, 1),
-                   "attn_decode_ms": round(ms_plain, 4),
-                   "metadata_ms": round(ms_meta, 4)},
-        "roofline": roof,
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
-    del probs
-    torch.cuda.empty_cache()
 
     if not args.no_extras:
+        # the other decode workloads, each as the headline step is measured
+        result["decode_workloads"] = {}
+        for wl in ("llama3_8b_decode", "long_fp8_decode", "qwen3_235b_decode", "l4_log_decode"):
+            if wl == args.workload:
+                continue
+            r = bench_decode_step(all_specs[wl], args.steps, args.warmup, extras=False)
+            r.pop("layout"), r.pop("values")
+            result["decode_workloads"][wl] = {
+                "step_ms": round(r["ms_step"], 4), "step_kv_read_GBps": round(r["value"], 1),
+                "step_frac_hbm_peak": round(r["value"] / HBM_PEAK_GBS, 4),
+                "config": r["config"], "roofline": r["roofline"]}
+            log(f"decode {wl}: {result['decode_workloads'][wl]}")
         result["extend"] = bench_extend(args.steps)
         result["mfma_reference"] = bench_gemm(min(args.steps, 20))
         result["extend"]["frac_of_random_gemm"] = round(
@@ -598,10 +642,6 @@ def main():
         result["extend_fp8kv"] = bench_extend(args.steps, gpu_state=False, kv_dtype="fp8")
         log(f"extend over an fp8 cache: {result['extend_fp8kv']}")
         log(f"bf16 GEMM reference: {result['mfma_reference']}")
-        result["decode_workloads"] = {}
-        for wl in ("qwen3_235b_decode", "long_fp8_decode"):
-            result["decode_workloads"][wl] = bench_decode_kernel(workloads.WORKLOADS[wl], args.steps)
-            log(f"decode {wl}: {result['decode_workloads'][wl]}")
         # key / value heads of different widths (192 / 128)
         result["asym_extend"] = bench_extend(args.steps, gpu_state=False,
                                              spec=workloads.EXTRA["asym_extend"])
@@ -610,8 +650,8 @@ def main():
         log(f"decode, 192/128 widths: {result['asym_decode']}")
         # speculative verify through the decode path and the extend path
         result["verify"] = bench_verify_drafts(args.steps)
-        # the headline step replayed from a HIP graph
-        result["graph_step"] = bench_graph_step(spec, args.steps)
+        # the Llama-shaped step replayed from a HIP graph
+        result["graph_step"] = bench_graph_step(workloads.WORKLOADS["llama3_8b_decode"], args.steps)
         log(f"step from a HIP graph: {result['graph_step']}")
 
     if not args.no_cpu_baseline:

@@ -250,6 +250,18 @@ pka_status pka_read_status(const pka_batch* md, int32_t* status, void* stream);
 #define PKA_DEV_TABLE_SHORT 4   /* ceil(L_b/P) > page_table_cols (clamped) */
 #define PKA_DEV_CAPACITY 8      /* pages or tokens beyond the batch capacities */
 
+/* Name the kernels and launch shape a call would resolve to for a batch of
+ * `batch` requests and `num_q_tokens` query tokens, as text in buf (len
+ * bytes, NUL-terminated); with_metadata: the batch goes through
+ * pka_forward_with_metadata.  The pages ask to read which backend was
+ * actually resolved before measuring anything ("sglang-101 s4.2
+ * --attention-backend", section "What to measure"); this is that read-out
+ * for the kernels.  Host-only: it launches nothing (it may query the current
+ * device's compute-unit count and the kernels' occupancy).  Returns
+ * PKA_ERR_INVALID_ARG if the text does not fit. */
+pka_status pka_describe(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
+                        int32_t batch, int32_t num_q_tokens, int with_metadata, char* buf, size_t len);
+
 const char* pka_status_string(pka_status s);
 const char* pka_last_error(void);
 

@@ -85,6 +85,8 @@ SIGNATURES = {
                                                  _I32, ctypes.POINTER(BatchStruct), _VP, _VP, _VP,
                                                  ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "pka_read_status": (ctypes.c_int, [ctypes.POINTER(BatchStruct), ctypes.POINTER(_I32), _VP]),
+    "pka_describe": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, _I32, _I32, ctypes.c_int,
+                                    ctypes.c_char_p, _SZ]),
     "pka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pka_last_error": (ctypes.c_char_p, []),
     "pka_version": (ctypes.c_char_p, []),
@@ -165,6 +167,14 @@ class Context:
         _check(lib().pka_batch_sizes(self.handle, MODES[mode], batch, num_q_tokens, max_kv_pages,
                                      ctypes.byref(s)))
         return s
+
+    def describe(self, mode: str, batch: int, num_q_tokens: int, spec_mode: str = "prefill",
+                 with_metadata: bool = False) -> str:
+        """The kernels and launch shape a batch of this shape resolves to."""
+        buf = ctypes.create_string_buffer(1024)
+        _check(lib().pka_describe(self.handle, MODES[mode], SPEC_MODES[spec_mode], batch,
+                                  num_q_tokens, int(bool(with_metadata)), buf, len(buf)))
+        return buf.value.decode()
 
     def pool_shape(self):
         """Shape of the K pool."""

@@ -195,6 +195,7 @@ pka::AttnArgs attn_args(const pka_ctx* ctx, const pka_batch* md, const void* q, 
     a.qgroups = ctx->qgroups;
     a.page_shift = ctx->page_shift;
     a.num_pages = c.num_pages;
+    a.pool_slots = (int64_t)c.num_pages * c.page_size;
     a.spw = 1;
     a.csplit = 1;
     const float k_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f;
@@ -364,9 +365,73 @@ bool decode_md_ok(const pka_ctx* ctx, const pka_batch* md) {
     return v == 1;
 }
 
+const char* dtype_name(pka_dtype t) { return t == PKA_F32 ? "f32" : t == PKA_BF16 ? "bf16" : "fp8 e4m3fn"; }
+
 }  // namespace
 
 extern "C" {
+
+pka_status pka_describe(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
+                        int32_t batch, int32_t num_q_tokens, int with_metadata, char* buf, size_t len) {
+    if (!ctx || !buf || len == 0) return fail(PKA_ERR_INVALID_ARG, "null context or buffer");
+    if (mode < PKA_MODE_EXTEND || mode > PKA_MODE_DRAFT_EXTEND)
+        return fail(PKA_ERR_INVALID_ARG, "unknown forward mode %d", (int)mode);
+    if (spec_mode != PKA_SPEC_PREFILL && spec_mode != PKA_SPEC_DECODE)
+        return fail(PKA_ERR_INVALID_ARG, "unknown speculative attention mode %d", (int)spec_mode);
+    if (batch < 0 || num_q_tokens < 0 || (mode == PKA_MODE_DECODE && num_q_tokens != batch))
+        return fail(PKA_ERR_INVALID_ARG, "batch %d / num_q_tokens %d", batch, num_q_tokens);
+    const pka_config& c = ctx->cfg;
+    const pka_path path = pka_select_path(mode, spec_mode);
+    pka_batch md{};
+    md.mode = mode;
+    md.batch = batch;
+    md.num_q_tokens = num_q_tokens;
+    std::string d;
+    char tmp[512];
+    if (path == PKA_PATH_NONE) {
+        d = "path none (idle batch: nothing is launched)";
+    } else if (path == PKA_PATH_DECODE) {
+        int32_t nwg = 0, base_spw = 1;
+        pka_status s = batch_shares(ctx, &md, &nwg, &base_spw);
+        if (s != PKA_OK) return s;
+        const int32_t cs = decode_csplit(ctx, &md);
+        int wpb = 1, spw = 1;
+        decode_shape(ctx, cs, base_spw, &wpb, &spw);
+        const int32_t qslots = decode_qslots(mode, num_q_tokens);
+        const bool md_in = with_metadata && decode_md_ok(ctx, &md);
+        const char* kern = c.kv_dtype == PKA_F32 ? "decode_f32_kernel" : "decode_mfma_kernel";
+        snprintf(tmp, sizeof tmp,
+                 "path decode: %s<Dk %d, Dv %d, %s cache%s%s>, page size %d, %d query heads per KV head "
+                 "(%d head group(s) of <= 16), %d shares (one resident round), %d wave(s) per share, "
+                 "%d share(s) per workgroup, %d workgroups, column split %d, %d partial row(s) per share; "
+                 "then decode_merge_kernel<Dv %d>%s",
+                 kern, ctx->dk, ctx->dv, dtype_name(c.kv_dtype), qslots > 1 ? ", several query rows" : "",
+                 md_in ? ", metadata built in-kernel" : "", c.page_size, ctx->G, ctx->qgroups, nwg, wpb, spw,
+                 (nwg + spw - 1) / spw, cs, qslots, ctx->dv,
+                 with_metadata && !md_in ? "; metadata by md_scan_kernel first" : "");
+        d = tmp;
+    } else {
+        if (c.q_dtype == PKA_F32) {
+            snprintf(tmp, sizeof tmp, "path extend: extend_f32_kernel<Dk %d, Dv %d>, %d query tokens per item",
+                     ctx->dk, ctx->dv, ctx->ext_tq);
+        } else {
+            const bool big = c.page_size >= 64;
+            const int64_t row = (int64_t)c.num_kv_heads * std::max(ctx->dk, ctx->dv) * (int64_t)elem_bytes(c.kv_dtype);
+            const bool wide = !big && (int64_t)c.num_pages * c.page_size * row > (int64_t)UINT32_MAX;
+            snprintf(tmp, sizeof tmp,
+                     "path extend: extend_mfma_kernel<Dk %d, Dv %d, scale %s 0, %s, %s cache>, %d query tokens "
+                     "x %d heads per workgroup item, 64-key tiles",
+                     ctx->dk, ctx->dv, c.scale > 0.f ? ">" : "<=",
+                     big ? "one page per key tile" : (wide ? "per-row slots, 64-bit addresses" : "per-row slots"),
+                     dtype_name(c.kv_dtype), ctx->ext_tq, ctx->G);
+        }
+        d = tmp;
+        if (with_metadata) d = "md_scan_kernel, then " + d;
+    }
+    if (d.size() + 1 > len) return fail(PKA_ERR_INVALID_ARG, "description needs %zu bytes", d.size() + 1);
+    memcpy(buf, d.c_str(), d.size() + 1);
+    return PKA_OK;
+}
 
 const char* pka_status_string(pka_status s) {
     switch (s) {

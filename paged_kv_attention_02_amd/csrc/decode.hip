@@ -157,14 +157,12 @@ struct DecodeShape {
 typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
 
 // Direct HBM -> LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_dst + 16 * i (lds_dst is wave-uniform).  The compiler does not track
-// it: the kernel waits for it with an explicit vmcnt(0) before the data is
-// read.
+// lds_dst + 16 * i (lds_dst is wave-uniform; the compiler moves it to M0).
+// The load counts in vmcnt like any other; the kernel still waits for it
+// with an explicit vmcnt(0) before the data is read.
 __device__ inline void lds_dma16(const void* src, const uint8_t* lds_dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    // one wait state between the M0 write and the LDS-DMA instruction reading it
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
-                 : "m0", "memory");
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
 // V of one 32-token tile in registers: k-slot q of lane group j holds tile
@@ -189,12 +187,15 @@ template <int DK, int DV, bool FP8>
 __device__ inline void load_k(uint8_t* kst, int32_t slot, const uint8_t* kbase, int64_t krow) {
     using S = DecodeShape<DK, DV, FP8>;
     const int lane = threadIdx.x & 63;
+    // every row's slot first, so one wait covers the cross-lane moves
+    int32_t ks[S::KDMA];
+    #pragma unroll
+    for (int q = 0; q < S::KDMA; ++q) ks[q] = __shfl(slot, (64 * q + lane) / S::KCPR);
     #pragma unroll
     for (int q = 0; q < S::KDMA; ++q) {
         const int f = 64 * q + lane;
         const int row = f / S::KCPR, pc = f % S::KCPR;
-        const int32_t ks = __shfl(slot, row);
-        lds_dma16(kbase + ks * krow + 16 * S::kswz(row, pc), kst + 1024 * q);
+        lds_dma16(kbase + ks[q] * krow + 16 * S::kswz(row, pc), kst + 1024 * q);
     }
 }
 template <int DK, int DV, bool FP8>
@@ -873,7 +874,12 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     // before the next tile's go out, so one tile is in flight while
     // another is computed.
     auto step = [&](VTile<DK, DV, FP8>& X, VTile<DK, DV, FP8>& Y) -> bool {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile cur, its queries, nx's new token landed
+        // vmcnt(0): tile cur, its queries and nx's new token landed.  With
+        // lgkmcnt(0) as well (nothing of the scalar or LDS kind is pending
+        // here), the compiler also knows the direct loads' LDS writes are
+        // done; without it, it would make every LDS wait of the step a full
+        // lgkmcnt(0).
+        __builtin_amdgcn_s_waitcnt(0x0070);
         asm volatile("" ::: "memory");       // LDS reads stay after the wait
         if (cur.t0 == cur.lo) take_q();      // cur opens its unit
         int32_t other = 0;

@@ -79,14 +79,27 @@ __device__ inline float sum_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Direct HBM -> LDS load of 16 bytes per lane: lane i's bytes land at
-// lds_dst + 16 * i (lds_dst is wave-uniform).  Issued as a plain instruction
-// the compiler does not track: the caller orders it with an explicit
-// vmcnt(0) wait and a barrier before any wave reads the destination.
+// Direct HBM -> LDS loads of 16 bytes per lane: lane i's bytes land at
+// lds_dst + 16 * i (lds_dst is wave-uniform; the compiler moves it to M0).
+// The caller orders them with an explicit vmcnt(0) wait and a barrier before
+// any wave reads the destination.  The buffer form addresses a wave-uniform
+// base (a raw buffer resource) plus a 32-bit per-lane offset; the compiler
+// counts it in vmcnt alone, so the LDS operand reads issued after it keep
+// their partial lgkmcnt waits (the global form also counts as an LDS access
+// and turns those into full waits).  The global form takes any 64-bit
+// address and serves pools beyond 4 GiB on pages of under 64 tokens.
+typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ inline void lds_dma16(const void* src, const uint8_t* lds_dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    // one wait state between the M0 write and the LDS-DMA instruction reading it
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "m0");
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (lds_void_t*)lds_dst, 16, 0, 0);
+}
+// raw buffer of `bytes` bytes from `base`: offsets at or beyond it read zero
+__device__ inline __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                             0x00020000 /* 32-bit data format */);
+}
+__device__ inline void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, const uint8_t* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_dst, 16, voff, 0, 0, 0);
 }
 
 // LDS tiles: BN keys x D dims of K or of V, rows of 16-byte chunks with no
@@ -133,14 +146,6 @@ __device__ inline int32_t load_uniform(const int32_t* p, int64_t i) {
     return ((const __attribute__((address_space(4))) int32_t*)(uintptr_t)p)[i];
 }
 
-// Direct HBM -> LDS load of 16 bytes per lane from a wave-uniform base plus
-// a 32-bit per-lane byte offset.
-__device__ inline void lds_dma16_s(const uint8_t* base, uint32_t voff, const uint8_t* lds_dst) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff),
-                 "s"(base) : "m0");
-}
-
 // Software pipeline over 64-key tiles t (per wave):
 //   top of iteration t: K(t+1) and V(t) are in LDS, the raw scores S(t) are
 //   in registers; the direct loads of K(t+2) and V(t+1) start into the
@@ -150,9 +155,11 @@ __device__ inline void lds_dma16_s(const uint8_t* base, uint32_t voff, const uin
 //   tile t+1 (independent of the softmax) are issued together, so the matrix
 //   cores run while the vector ALUs compute probabilities.
 // BIGPAGE (page size >= 64): a tile lies in one page, so its pool address is
-// a scalar and each lane only adds a fixed row offset.
+// a scalar and each lane only adds a fixed row offset.  Smaller pages gather
+// rows by slot: SLOT64 when a pool spans more than 4 GiB (64-bit addresses),
+// else 32-bit offsets from the pool's base.
 // DK: key (and query) width; DV: value (and output) width.
-template <int DK, int DV, bool POS, bool BIGPAGE, bool FP8>
+template <int DK, int DV, bool POS, bool BIGPAGE, bool FP8, bool SLOT64>
 __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void extend_mfma_kernel(AttnArgs a) {
     using TK = ExtTile<DK>;
     using TV = ExtTile<DV>;
@@ -279,14 +286,16 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 rg[j] = __builtin_nontemporal_load((const u32x4_t*)(tb + o));
             }
         } else if (lim >= BN - 1) {
+            const auto rs = raw_buffer(tb, BN * rb);
             #pragma unroll
-            for (int j = 0; j < M::NR; ++j) lds_dma16_s(tb, off[j], dst + (TT::LOADS * wave + j) * 1024);
+            for (int j = 0; j < M::NR; ++j) lds_dma16_buf(rs, off[j], dst + (TT::LOADS * wave + j) * 1024);
         } else {
+            const auto rs = raw_buffer(tb, BN * rb);
             #pragma unroll
             for (int j = 0; j < M::NR; ++j) {
                 const int r = M::row(tid, j);
                 const int ch = phys(vt, r, M::pos(tid, j));
-                lds_dma16_s(tb, (uint32_t)(min(r, lim) * rb + 16 * ch), dst + (TT::LOADS * wave + j) * 1024);
+                lds_dma16_buf(rs, (uint32_t)(min(r, lim) * rb + 16 * ch), dst + (TT::LOADS * wave + j) * 1024);
             }
         }
     };
@@ -320,10 +329,16 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
             #pragma unroll
             for (int j = 0; j < M::NR; ++j)
                 rg[j] = __builtin_nontemporal_load((const u32x4_t*)(src + (int64_t)slot[j] * rb + off[j]));
-        } else {
+        } else if constexpr (SLOT64) {
             #pragma unroll
             for (int j = 0; j < M::NR; ++j)
                 lds_dma16(src + (int64_t)slot[j] * rb + off[j], dst + (TT::LOADS * wave + j) * 1024);
+        } else {
+            // the pool from this head on fits in 32-bit offsets (checked at launch)
+            const auto rs = raw_buffer(src, (uint32_t)min(a.pool_slots * (int64_t)rb, (int64_t)UINT32_MAX));
+            #pragma unroll
+            for (int j = 0; j < M::NR; ++j)
+                lds_dma16_buf(rs, (uint32_t)slot[j] * (uint32_t)rb + off[j], dst + (TT::LOADS * wave + j) * 1024);
         }
     };
     // fp8: write one tensor's tile (registers) into LDS as bf16; each 16-byte
@@ -644,6 +659,32 @@ int extend_max_group(pka_dtype q, int /*page_size*/) {
     return EXT_COLS;
 }
 
+namespace {
+// One launch of the MFMA kernel for a (widths, scale sign, page path, cache
+// dtype) combination; the fp8 path moves tiles through registers and has no
+// 64-bit gather variant.
+template <int DK, int DV, bool POS, bool F8>
+void launch_ext_p(const AttnArgs& a, bool big, bool wide, dim3 grid, hipStream_t s) {
+    const dim3 block(64 * EXT_WAVES);
+    if (big)
+        hipLaunchKernelGGL((extend_mfma_kernel<DK, DV, POS, true, F8, false>), grid, block, 0, s, a);
+    else if (F8 || !wide)
+        hipLaunchKernelGGL((extend_mfma_kernel<DK, DV, POS, false, F8, false>), grid, block, 0, s, a);
+    else if constexpr (!F8)
+        hipLaunchKernelGGL((extend_mfma_kernel<DK, DV, POS, false, false, true>), grid, block, 0, s, a);
+}
+template <int DK, int DV>
+void launch_ext_d(const AttnArgs& a, bool pos, bool big, bool wide, bool f8, dim3 grid, hipStream_t s) {
+    if (f8) {
+        if (pos) launch_ext_p<DK, DV, true, true>(a, big, wide, grid, s);
+        else launch_ext_p<DK, DV, false, true>(a, big, wide, grid, s);
+    } else {
+        if (pos) launch_ext_p<DK, DV, true, false>(a, big, wide, grid, s);
+        else launch_ext_p<DK, DV, false, false>(a, big, wide, grid, s);
+    }
+}
+}  // namespace
+
 hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, hipStream_t s) {
     const int P = 1 << a.page_shift;
     const int tq = extend_tq(q, kv, a.G, P);
@@ -661,20 +702,15 @@ hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnAr
     const dim3 grid((unsigned)(items * a.Hkv));
     const bool pos = a.scale_log2 > 0.f;
     const bool big = P >= BN;
-#define PKA_EXT(DK_, DV_, POS_, BIG_, F8_) \
-    hipLaunchKernelGGL((extend_mfma_kernel<DK_, DV_, POS_, BIG_, F8_>), grid, dim3(64 * EXT_WAVES), 0, s, a)
-#define PKA_EXT_D(DK_, DV_, F8_)                                                                          \
-    do {                                                                                                  \
-        if (pos) { if (big) PKA_EXT(DK_, DV_, true, true, F8_); else PKA_EXT(DK_, DV_, true, false, F8_); }   \
-        else { if (big) PKA_EXT(DK_, DV_, false, true, F8_); else PKA_EXT(DK_, DV_, false, false, F8_); }     \
-    } while (0)
+    // pages under 64 tokens gather rows by slot: 32-bit offsets while every
+    // pool byte is within 4 GiB of the pool's base
+    const int64_t row_bytes = (int64_t)a.Hkv * (DK > DV ? DK : DV) * (kv == PKA_FP8_E4M3FN ? 1 : 2);
+    const bool wide = !big && a.pool_slots * row_bytes > (int64_t)UINT32_MAX;
     const bool f8 = kv == PKA_FP8_E4M3FN;
-    if (DK == 128 && DV == 128) { if (f8) PKA_EXT_D(128, 128, true); else PKA_EXT_D(128, 128, false); }
-    else if (DK == 64 && DV == 64) { if (f8) PKA_EXT_D(64, 64, true); else PKA_EXT_D(64, 64, false); }
-    else if (DK == 192 && DV == 128) { if (f8) PKA_EXT_D(192, 128, true); else PKA_EXT_D(192, 128, false); }
+    if (DK == 128 && DV == 128) launch_ext_d<128, 128>(a, pos, big, wide, f8, grid, s);
+    else if (DK == 64 && DV == 64) launch_ext_d<64, 64>(a, pos, big, wide, f8, grid, s);
+    else if (DK == 192 && DV == 128) launch_ext_d<192, 128>(a, pos, big, wide, f8, grid, s);
     else return hipErrorInvalidValue;
-#undef PKA_EXT_D
-#undef PKA_EXT
     return hipGetLastError();
 }
 
