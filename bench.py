@@ -467,7 +467,8 @@ HEADLINE = "qwen3_235b_decode"
 
 
 def traffic_key(spec_name: str) -> str:
-    return "decode_" + spec_name.split("_decode")[0] + "_step"
+    """Key of a decode workload's step launch in profiles/traffic.json."""
+    return "decode_step:" + spec_name
 
 
 def bench_decode_step(spec, steps: int, warmup: int, extras: bool) -> dict:

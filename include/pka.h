@@ -96,8 +96,12 @@ typedef enum { PKA_PATH_NONE = 0, PKA_PATH_DECODE = 1, PKA_PATH_EXTEND = 2 } pka
  *   the decode and the extend path.
  * scale multiplies q.k; k_scale / v_scale are the per-tensor fp8 scales (the
  * cached code c stands for c * scale); they must be 1 for non-fp8 caches.
- * v_head_dim is the last member so a zero-initialised config keeps the
- * equal-width behaviour. */
+ * max_q_per_request: the most query tokens one request carries in a
+ * target-verify / draft-extend batch sent down the decode path (the
+ * server's speculative draft-token count); it sizes the decode workspace's
+ * partial rows.  0 means 16, the most the decode path takes per request.
+ * v_head_dim and max_q_per_request come last so a zero-initialised tail
+ * keeps the equal-width, 16-row behaviour. */
 typedef struct {
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -110,6 +114,7 @@ typedef struct {
     float k_scale;
     float v_scale;
     int32_t v_head_dim; /* 0: same as head_dim */
+    int32_t max_q_per_request; /* 0: 16 */
 } pka_config;
 
 typedef struct pka_ctx pka_ctx;
@@ -150,7 +155,13 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out);
 void pka_destroy(pka_ctx* ctx);
 
 /* Sizes for a batch of `batch` requests, `num_q_tokens` new tokens and at
- * most `max_kv_pages` pages in total (sum of ceil(L_b / page_size)). */
+ * most `max_kv_pages` pages in total (sum of ceil(L_b / page_size)).  The
+ * decode workspace holds fp32 partial rows for one resident round of the
+ * decode launch on the current device (its compute units times the
+ * kernel's occupancy; the most the library allows, 2048 shares, if no
+ * device can be queried) and up to min(16, max_q_per_request, num_q_tokens)
+ * query rows per request for verify batches; it also covers any smaller
+ * batch of the same mode on the same device. */
 pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t batch,
                            int32_t num_q_tokens, int64_t max_kv_pages, pka_sizes* out);
 
@@ -184,12 +195,14 @@ pka_status pka_save_kv(const pka_ctx* ctx, const pka_batch* md, const void* k_ne
  * With metadata built for TARGET_VERIFY / DRAFT_EXTEND (the speculative
  * verify pass sent down the decode path, "[SGLang] Hybrid Attention",
  * section on _select_backend), each request carries n_b = extend_lens[b]
- * query rows (0 <= n_b <= 16); row i sits at position L_b - n_b + i and sees
- * keys 0 .. L_b - n_b + i, the cache being read once per 16 (row, query
- * head) pairs of a KV head (once for all rows when n_b * G <= 16).  Rows of
- * a request with n_b > 16 beyond the 16th are not computed and
- * PKA_DEV_BAD_LENGTH is raised.  The workspace then holds up to 16 partial
- * rows per (request, share of the split): pka_batch_sizes sizes it by mode. */
+ * query rows (0 <= n_b <= R, R = min(16, max_q_per_request)); row i sits at
+ * position L_b - n_b + i and sees keys 0 .. L_b - n_b + i, the cache being
+ * read once per 16 (row, query head) pairs of a KV head (once for all rows
+ * when n_b * G <= 16).  A batch with num_q_tokens > R * batch is refused
+ * (PKA_ERR_UNSUPPORTED: some request certainly has more than R rows); rows
+ * of a request beyond the R-th are not computed and PKA_DEV_BAD_LENGTH is
+ * raised.  The workspace then holds R partial rows per (request, share of
+ * the split): pka_batch_sizes sizes it by mode. */
 pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* q,
                            const void* k_pool, const void* v_pool, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream);

@@ -47,7 +47,7 @@ class Config(ctypes.Structure):
                 ("num_pages", ctypes.c_int32), ("q_dtype", ctypes.c_int),
                 ("kv_dtype", ctypes.c_int), ("scale", ctypes.c_float),
                 ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
-                ("v_head_dim", ctypes.c_int32)]
+                ("v_head_dim", ctypes.c_int32), ("max_q_per_request", ctypes.c_int32)]
 
 
 class BatchStruct(ctypes.Structure):
@@ -141,13 +141,15 @@ class Context:
     def __init__(self, num_q_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
                  num_pages: int, q_dtype: str = "bf16", kv_dtype: str = "bf16",
                  scale: Optional[float] = None, k_scale: float = 1.0, v_scale: float = 1.0,
-                 v_head_dim: Optional[int] = None):
+                 v_head_dim: Optional[int] = None, max_q_per_request: int = 0):
         """head_dim: query/key head width; v_head_dim: value/output head
-        width (None: the same as head_dim)."""
+        width (None: the same as head_dim); max_q_per_request: the most query
+        tokens a request carries in a verify batch on the decode path (0: 16)."""
         dv = head_dim if v_head_dim is None else v_head_dim
         self.cfg = Config(num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
                           DTYPES[q_dtype], DTYPES[kv_dtype],
-                          head_dim ** -0.5 if scale is None else scale, k_scale, v_scale, dv)
+                          head_dim ** -0.5 if scale is None else scale, k_scale, v_scale, dv,
+                          max_q_per_request)
         self.q_dtype, self.kv_dtype = q_dtype, kv_dtype
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         self.v_head_dim = dv
@@ -332,3 +334,4 @@ def forward_with_metadata(ctx: Context, mode: str, md: Batch, seq_lens, extend_l
         0 if page_table is None else page_table.shape[1], ctypes.byref(md.s), _ptr(q), _ptr(k_new),
         _ptr(v_new), int(bool(save_kv_cache)), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), wp,
         wb, _stream(stream)))
+

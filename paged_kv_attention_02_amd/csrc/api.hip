@@ -24,6 +24,7 @@ struct pka_ctx {
     int32_t page_shift;
     int32_t wpb;         // decode waves per share (KV-head units of one share in a workgroup)
     int32_t ext_tq;      // extend query tokens per work item
+    int32_t max_q;       // most query rows per request on the decode path (1 .. DEC_MAX_Q)
     std::atomic<int32_t> nwg{0};  // decode shares (from the device's CU count)
     std::atomic<int32_t> spw{0};  // decode shares per workgroup
     std::atomic<int32_t> packed8{0};  // 8-wave decode workgroups resident per CU
@@ -102,10 +103,10 @@ bool is_extend_like(pka_forward_mode m) {
 
 // Decode partial slots per (request, workgroup): a decode batch has one query
 // row per request; an extend-like batch sent down the decode path
-// (speculative verify) may carry up to DEC_MAX_Q rows per request.
-int32_t decode_qslots(pka_forward_mode m, int32_t num_q_tokens) {
+// (speculative verify) may carry up to ctx->max_q rows per request.
+int32_t decode_qslots(const pka_ctx* ctx, pka_forward_mode m, int32_t num_q_tokens) {
     if (m == PKA_MODE_DECODE) return 1;
-    return std::max(1, std::min<int32_t>(pka::DEC_MAX_Q, num_q_tokens));
+    return std::max(1, std::min<int32_t>(ctx->max_q, num_q_tokens));
 }
 
 // Waves per head group on the decode path.  A verify batch whose query
@@ -116,7 +117,7 @@ int32_t decode_qslots(pka_forward_mode m, int32_t num_q_tokens) {
 // leaves the surplus waves idle over its tiles.  bf16 / fp8 caches only.
 int32_t decode_csplit(const pka_ctx* ctx, const pka_batch* md) {
     if (ctx->cfg.kv_dtype == PKA_F32 || md->batch <= 0) return 1;
-    const int32_t qslots = decode_qslots(md->mode, md->num_q_tokens);
+    const int32_t qslots = decode_qslots(ctx, md->mode, md->num_q_tokens);
     if (qslots <= 1) return 1;
     const int32_t nq = std::min<int32_t>(qslots, (md->num_q_tokens + md->batch - 1) / md->batch);
     const int32_t passes = (nq * std::min<int32_t>(ctx->G, 16) + 15) / 16;
@@ -228,9 +229,13 @@ pka_status decode_args(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     if (write_new && (!k_new || !v_new)) return fail(PKA_ERR_INVALID_ARG, "null K/V pointer");
     if (write_new && (!aligned16(k_new) || !aligned16(v_new)))
         return fail(PKA_ERR_INVALID_ARG, "K/V rows must be 16-byte aligned");
-    const int32_t qslots = decode_qslots(md->mode, md->num_q_tokens);
+    const int32_t qslots = decode_qslots(ctx, md->mode, md->num_q_tokens);
     if (write_new && qslots != 1)
         return fail(PKA_ERR_INVALID_ARG, "the fused cache write serves decode batches only");
+    if (qslots > 1 && (int64_t)md->num_q_tokens > (int64_t)qslots * md->batch)
+        return fail(PKA_ERR_UNSUPPORTED,
+                    "verify batch of %d query tokens over %d requests: the decode path takes at most %d "
+                    "per request (max_q_per_request / 16)", md->num_q_tokens, md->batch, qslots);
     int32_t nwg = 0, spw = 1;
     if ((s = batch_shares(ctx, md, &nwg, &spw)) != PKA_OK) return s;
     const int64_t need = decode_ws_bytes(ctx, md->batch, nwg, qslots);
@@ -338,7 +343,7 @@ pka_status forward_checks(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_at
         int32_t nwg = 0;
         if ((s = batch_shares(ctx, md, &nwg)) != PKA_OK) return s;
         if (!workspace ||
-            (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg, decode_qslots(md->mode, md->num_q_tokens)))
+            (int64_t)workspace_bytes < decode_ws_bytes(ctx, md->batch, nwg, decode_qslots(ctx, md->mode, md->num_q_tokens)))
             return fail(PKA_ERR_WORKSPACE, "decode workspace too small");
     }
     if (save_kv && md->num_q_tokens > 0) {
@@ -397,7 +402,7 @@ pka_status pka_describe(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn
         const int32_t cs = decode_csplit(ctx, &md);
         int wpb = 1, spw = 1;
         decode_shape(ctx, cs, base_spw, &wpb, &spw);
-        const int32_t qslots = decode_qslots(mode, num_q_tokens);
+        const int32_t qslots = decode_qslots(ctx, mode, num_q_tokens);
         const bool md_in = with_metadata && decode_md_ok(ctx, &md);
         const char* kern = c.kv_dtype == PKA_F32 ? "decode_f32_kernel" : "decode_mfma_kernel";
         snprintf(tmp, sizeof tmp,
@@ -479,6 +484,8 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
     } else if (c.k_scale != 1.f || c.v_scale != 1.f) {
         return fail(PKA_ERR_INVALID_ARG, "k_scale / v_scale apply to fp8 caches only (must be 1)");
     }
+    if (c.max_q_per_request < 0)
+        return fail(PKA_ERR_INVALID_ARG, "max_q_per_request must be >= 0 (0: 16)");
     const int G = c.num_q_heads / c.num_kv_heads;
     if (G > pka::extend_max_group(c.q_dtype, c.page_size))
         return fail(PKA_ERR_UNSUPPORTED, "%d query heads per KV head (extend supports up to %d at page size %d)",
@@ -499,6 +506,7 @@ pka_status pka_create(const pka_config* cfg, pka_ctx** out) {
     while (units % wpb) wpb >>= 1;
     ctx->wpb = wpb;
     ctx->ext_tq = pka::extend_tq(c.q_dtype, c.kv_dtype, ctx->G, c.page_size);
+    ctx->max_q = c.max_q_per_request == 0 ? pka::DEC_MAX_Q : std::min<int32_t>(c.max_q_per_request, pka::DEC_MAX_Q);
     *out = ctx;
     return PKA_OK;
 }
@@ -520,12 +528,17 @@ pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t ba
     out->qo_indptr = (int64_t)batch + 1;
     out->out_cache_loc = std::max<int32_t>(num_q_tokens, 1);
     out->plan = pka::plan_elems(batch, num_q_tokens, ctx->ext_tq);
-    // split partials: only the decode path uses the workspace (an extend batch
-    // may still be routed to it by the speculative-attention dispatch)
-    out->workspace_bytes = mode == PKA_MODE_EXTEND || mode == PKA_MODE_IDLE
-                               ? 0
-                               : decode_ws_bytes(ctx, batch, pka::DEC_MAX_WG,
-                                                 decode_qslots(mode, num_q_tokens));
+    // split partials: only the decode path uses the workspace (a verify batch
+    // may be routed to it by the speculative-attention dispatch).  One
+    // resident round of the device's decode launch (without a column split:
+    // the most shares any batch of this mode can use), else the library's
+    // bound when no device answers.
+    out->workspace_bytes = 0;
+    if (mode != PKA_MODE_EXTEND && mode != PKA_MODE_IDLE) {
+        int32_t nwg = 0;
+        if (decode_wgs(ctx, &nwg) != PKA_OK) nwg = pka::DEC_MAX_WG;
+        out->workspace_bytes = decode_ws_bytes(ctx, batch, nwg, decode_qslots(ctx, mode, num_q_tokens));
+    }
     return PKA_OK;
 }
 

@@ -187,6 +187,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
+
 // DK: key (and query) head width; DV: value (and output) head width.
 hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, const SaveArgs& a, hipStream_t s);
 // wpb: waves per share (KV-head units of one share in a workgroup); a

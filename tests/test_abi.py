@@ -177,3 +177,44 @@ def test_forward_with_metadata_refuses_before_any_launch():
     assert f(ctx.handle, 0, 0, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake + 4, fake, 1,
              fake, fake, fake, None, None, 0, None) == -1
     assert b"extend_lens" in lib.pka_last_error() or lib.pka_last_error()
+
+
+def test_verify_workspace_follows_max_q_per_request():
+    """The decode path's partial rows per request: min(16, max_q_per_request,
+    num_q_tokens) for verify batches (0 means 16), one for decode batches."""
+    sizes = lambda mq, n: pka.Context(32, 8, 128, 16, 100, max_q_per_request=mq).sizes(
+        "target_verify", 8, n, 80).workspace_bytes
+    one = pka.Context(32, 8, 128, 16, 100).sizes("decode", 8, 8, 80).workspace_bytes
+    assert sizes(4, 32) == 4 * one
+    assert sizes(0, 32) == sizes(16, 32) == sizes(40, 32) == 16 * one
+    assert sizes(8, 3) == 3 * one  # never more rows than query tokens
+    assert _create(max_q_per_request=-1) == -1
+    assert _create(max_q_per_request=4) == 0
+
+
+def test_describe_names_the_extend_variant():
+    """The resolved-kernel read-out needs no device on the extend path."""
+    ctx = pka.Context(32, 8, 128, 128, 100)
+    d = ctx.describe("extend", 8, 1000, with_metadata=True)
+    assert d.startswith("md_scan_kernel, then path extend: extend_mfma_kernel<Dk 128, Dv 128")
+    assert "one page per key tile" in d and "32 query tokens x 4 heads" in d
+    small = pka.Context(32, 8, 128, 16, 100, "bf16", "fp8", 0.1, 0.01, 0.01).describe("target_verify", 4, 16)
+    assert "per-row slots" in small and "fp8 e4m3fn cache" in small
+    assert pka.Context(4, 2, 64, 1, 100, "f32", "f32").describe("extend", 2, 9).startswith(
+        "path extend: extend_f32_kernel<Dk 64, Dv 64>")
+    assert pka.Context(32, 8, 128, 16, 100).describe("idle", 4, 4).startswith("path none")
+    with pytest.raises(pka.PkaError):
+        ctx.describe("decode", 4, 5)  # decode takes one token per request
+
+
+
+def test_decode_path_refuses_verify_batches_beyond_max_q():
+    """A verify batch with more query tokens than max_q_per_request per
+    request on average certainly has a request the decode path cannot hold:
+    refused before anything is launched."""
+    lib = pka.lib()
+    ctx = pka.Context(32, 8, 128, 16, 100, max_q_per_request=4)
+    fake = 1 << 20  # aligned, never dereferenced: validation fails first
+    md = pka.BatchStruct(3, 4, 17, 40, fake, fake, fake, fake, fake, fake)  # target_verify, 17 > 4 x 4
+    st = lib.pka_attn_decode(ctx.handle, ctypes.byref(md), fake, fake, fake, fake, None, fake, 1 << 30, None)
+    assert st == -2 and b"at most 4 per request" in lib.pka_last_error()

@@ -130,3 +130,31 @@ def test_more_than_16_tokens_is_flagged():
     max_abs, rel = errors(got[rows], ref[rows])
     assert max_abs <= 2e-2 and rel <= 5e-3, (max_abs, rel)
     assert np.all(got[16:20] == 0)
+
+
+def test_verify_rows_sized_by_max_q_per_request():
+    """A context built for 4 draft tokens per request sizes the decode
+    partials for 4 rows (a quarter of the 16-row default) and computes the
+    same batch within the gates; a batch with more rows on average than that
+    is refused before any launch."""
+    spec = BASE.replace(batch=24, new_len_args=(1, 4), prefix_len_args=(1, 1500), seed=96)
+    prob, layout, values = _verify_problem(spec)
+    ctx4 = pka.Context(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
+                       layout.num_pages, spec.q_dtype, spec.kv_dtype, spec.softmax_scale,
+                       max_q_per_request=4)
+    full = prob.ctx.sizes("target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages)
+    four = ctx4.sizes("target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages)
+    assert four.workspace_bytes * 4 == full.workspace_bytes
+    prob.ctx = ctx4
+    prob.md = pka.Batch(ctx4, "target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages)
+    prob.metadata_step()
+    _check(prob, layout, values, "max_q_per_request=4")
+    many = BASE.replace(batch=8, new_len_args=(5, 6), prefix_len_args=(1, 300), seed=97)
+    prob5, layout5, _ = _verify_problem(many)
+    prob5.ctx = pka.Context(many.num_q_heads, many.num_kv_heads, many.head_dim, many.page_size,
+                            layout5.num_pages, many.q_dtype, many.kv_dtype, many.softmax_scale,
+                            max_q_per_request=4)
+    prob5.md = pka.Batch(prob5.ctx, "target_verify", layout5.batch, layout5.num_q_tokens, layout5.kv_pages)
+    with pytest.raises(pka.PkaError) as e:
+        prob5.attention_step(save=False, spec_mode="decode")
+    assert e.value.status == -2
