@@ -255,6 +255,27 @@ pka_status pka_forward_with_metadata(const pka_ctx* ctx, pka_forward_mode mode,
                                      void* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* pka_forward_with_metadata without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The decode path's split
+ * partials go to a file-scope device array of PKA_NOALLOC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends (its address
+ * is looked up on the first call on each device); nothing is allocated, and
+ * nothing in it needs clearing between calls.  A batch whose decode
+ * partials need more (pka_batch_sizes' workspace_bytes is an upper bound)
+ * is refused with PKA_ERR_WORKSPACE and nothing is launched.  All calls on
+ * one GPU share the array: calls that overlap in time on one GPU (other
+ * streams, concurrent graph replays) race on it.  Otherwise the same
+ * arguments, results and errors as pka_forward_with_metadata. */
+#define PKA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pka_status pka_forward_with_metadata_noalloc(const pka_ctx* ctx, pka_forward_mode mode,
+                                             pka_spec_attn_mode spec_mode, const int32_t* seq_lens,
+                                             const int32_t* extend_lens, const int32_t* page_table,
+                                             int32_t page_table_stride, int32_t page_table_cols,
+                                             pka_batch* md, const void* q, const void* k_new,
+                                             const void* v_new, int save_kv, void* k_pool,
+                                             void* v_pool, void* out, float* lse, void* stream);
+
 /* Synchronise `stream` and read the sticky device status word of a batch:
  * 0 = clean, else a bitwise OR of PKA_DEV_* flags. */
 pka_status pka_read_status(const pka_batch* md, int32_t* status, void* stream);

@@ -33,6 +33,8 @@ PATHS = {0: "none", 1: "decode", 2: "extend"}
 STATUS = {0: "PKA_OK", -1: "PKA_ERR_INVALID_ARG", -2: "PKA_ERR_UNSUPPORTED",
           -3: "PKA_ERR_WORKSPACE", -4: "PKA_ERR_HIP"}
 DEV_FLAGS = {1: "BAD_LENGTH", 2: "BAD_PAGE", 4: "TABLE_SHORT", 8: "CAPACITY"}
+# The scratch array of pka_forward_with_metadata_noalloc (PKA_NOALLOC_SCRATCH_BYTES in pka.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class PkaError(RuntimeError):
@@ -84,6 +86,9 @@ SIGNATURES = {
     "pka_forward_with_metadata": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, _VP, _VP, _VP, _I32,
                                                  _I32, ctypes.POINTER(BatchStruct), _VP, _VP, _VP,
                                                  ctypes.c_int, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "pka_forward_with_metadata_noalloc": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, _VP, _VP, _VP,
+                                                         _I32, _I32, ctypes.POINTER(BatchStruct), _VP, _VP,
+                                                         _VP, ctypes.c_int, _VP, _VP, _VP, _VP, _VP]),
     "pka_read_status": (ctypes.c_int, [ctypes.POINTER(BatchStruct), ctypes.POINTER(_I32), _VP]),
     "pka_describe": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, _I32, _I32, ctypes.c_int,
                                     ctypes.c_char_p, _SZ]),
@@ -335,3 +340,22 @@ def forward_with_metadata(ctx: Context, mode: str, md: Batch, seq_lens, extend_l
         _ptr(v_new), int(bool(save_kv_cache)), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), wp,
         wb, _stream(stream)))
 
+
+def forward_with_metadata_noalloc(ctx: Context, mode: str, md: Batch, seq_lens, extend_lens, page_table,
+                                  q, k_new, v_new, k_pool, v_pool, out, lse=None,
+                                  save_kv_cache: bool = True, spec_mode: str = "prefill", stream=None):
+    """forward_with_metadata without a workspace: the decode partials live in
+    the library's per-device scratch array (NOALLOC_SCRATCH_BYTES); nothing
+    is allocated by the call."""
+    if mode != "idle":
+        md._check_inputs(seq_lens, extend_lens, page_table)
+        _attn_common(ctx, md, q, k_pool, v_pool, out, lse)
+        if save_kv_cache:
+            _check_rows(ctx, k_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "k_new")
+            _check_rows(ctx, v_new, md.num_q_tokens, ctx.num_kv_heads, ctx.q_dtype, "v_new", value=True)
+    _check(lib().pka_forward_with_metadata_noalloc(
+        ctx.handle, MODES[mode], SPEC_MODES[spec_mode], _ptr(seq_lens), _ptr(extend_lens),
+        _ptr(page_table), 0 if page_table is None else page_table.stride(0),
+        0 if page_table is None else page_table.shape[1], ctypes.byref(md.s), _ptr(q), _ptr(k_new),
+        _ptr(v_new), int(bool(save_kv_cache)), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse),
+        _stream(stream)))

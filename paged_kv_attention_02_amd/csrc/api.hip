@@ -374,6 +374,36 @@ const char* dtype_name(pka_dtype t) { return t == PKA_F32 ? "f32" : t == PKA_BF1
 
 }  // namespace
 
+namespace pka {
+
+pka_status set_error(pka_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+pka_status forward_workspace_need(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
+                                  const pka_batch* md, int64_t* need) {
+    *need = 0;
+    if (mode < PKA_MODE_EXTEND || mode > PKA_MODE_DRAFT_EXTEND)
+        return fail(PKA_ERR_INVALID_ARG, "unknown forward mode %d", (int)mode);
+    if (spec_mode != PKA_SPEC_PREFILL && spec_mode != PKA_SPEC_DECODE)
+        return fail(PKA_ERR_INVALID_ARG, "unknown speculative attention mode %d", (int)spec_mode);
+    if (pka_select_path(mode, spec_mode) != PKA_PATH_DECODE) return PKA_OK;
+    pka_status s = check_batch(ctx, md);
+    if (s != PKA_OK || md->batch == 0) return s;
+    int32_t nwg = 0;
+    if ((s = batch_shares(ctx, md, &nwg)) != PKA_OK) return s;
+    *need = decode_ws_bytes(ctx, md->batch, nwg, decode_qslots(ctx, md->mode, md->num_q_tokens));
+    return PKA_OK;
+}
+
+}  // namespace pka
+
 extern "C" {
 
 pka_status pka_describe(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,

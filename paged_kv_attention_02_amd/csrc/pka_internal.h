@@ -188,6 +188,12 @@ struct AttnArgs {
 
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t s);
 
+// Record a failure for pka_last_error() and return s.
+pka_status set_error(pka_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Workspace bytes a pka_forward_with_metadata call on this batch uses (0 when
+// its path takes none); checks the mode arguments and the batch sizes.
+pka_status forward_workspace_need(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn_mode spec_mode,
+                                  const pka_batch* md, int64_t* need);
 // DK: key (and query) head width; DV: value (and output) head width.
 hipError_t launch_save_kv(pka_dtype src, pka_dtype kv, const SaveArgs& a, hipStream_t s);
 // wpb: waves per share (KV-head units of one share in a workgroup); a

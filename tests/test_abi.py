@@ -218,3 +218,26 @@ def test_decode_path_refuses_verify_batches_beyond_max_q():
     md = pka.BatchStruct(3, 4, 17, 40, fake, fake, fake, fake, fake, fake)  # target_verify, 17 > 4 x 4
     st = lib.pka_attn_decode(ctx.handle, ctypes.byref(md), fake, fake, fake, fake, None, fake, 1 << 30, None)
     assert st == -2 and b"at most 4 per request" in lib.pka_last_error()
+
+
+def test_noalloc_refuses_before_any_launch():
+    """The no-allocation entry point checks its arguments like the one-call
+    entry point, before it looks up its scratch array or enqueues anything."""
+    lib = pka.lib()
+    ctx = pka.Context(32, 8, 128, 16, 100)
+    fake = 1 << 20  # aligned, never dereferenced: validation fails first
+    f = lib.pka_forward_with_metadata_noalloc
+    md = pka.BatchStruct(0, 4, 40, 40, fake, fake, fake, fake, fake, fake)  # extend metadata
+    assert f(ctx.handle, 9, 0, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None) == -1
+    assert f(ctx.handle, 0, 5, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None) == -1
+    # IDLE needs no buffers and no scratch
+    assert f(ctx.handle, 2, 0, None, None, None, 0, 0, ctypes.byref(md), None, None, None, 1,
+             None, None, None, None, None) == 0
+    # metadata built for another mode
+    assert f(ctx.handle, 3, 0, fake, fake, fake, 3, 3, ctypes.byref(md), fake, fake, fake, 1,
+             fake, fake, fake, None, None) == -1
+    assert pka.NOALLOC_SCRATCH_BYTES == 64 << 20
+    text = open(os.path.join(ROOT, "include", "pka.h")).read()
+    assert "#define PKA_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
