@@ -344,39 +344,50 @@ def bench_verify_drafts(iters: int):
     return out
 
 
-def bench_graph_step(spec, iters: int):
-    """The headline step (one forward_with_metadata call with the cache
-    write) captured once per copy of pools and metadata in a HIP graph and
-    replayed alternately, against the same steps launched eagerly."""
+def bench_graph_step(spec, iters: int, per_graph: int = 8):
+    """The Llama-shaped step (one forward_with_metadata call with the cache
+    write) captured in HIP graphs and replayed, against the same steps
+    launched eagerly: one graph per copy of pools and metadata holding one
+    step, replayed alternately, and one graph holding `per_graph` steps
+    (alternating the copies, as one captured decode step holds the attention
+    of many layers).  Replays of a graph start ~9 us after the previous one
+    ends (kernel trace), so the per-step figure of the many-step graph shows
+    how that launch cost amortises."""
     import torch
     import workloads
     from tests.gpu_problem import GpuProblem
     layout = workloads.make_layout(spec)
     values = workloads.make_values(layout, device="cuda")
     probs = [GpuProblem(layout, values), GpuProblem(layout, values)]
-    graphs = []
-    for p in probs:
+
+    def capture(fn):
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            p.fused_step()
+            fn()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            p.fused_step()
-        graphs.append(g)
+            fn()
+        return g
+
+    graphs = [capture(lambda p=p: p.fused_step()) for p in probs]
+    multi = capture(lambda: [probs[i % 2].fused_step() for i in range(per_graph)])
     torch.cuda.synchronize()
     ms_graph = time_events(lambda i: graphs[i % 2].replay(), iters, warm=10)
+    ms_multi = time_events(lambda i: multi.replay(), max(2, iters // per_graph), warm=2) / per_graph
     ms_eager = time_events(lambda i: probs[i % 2].fused_step(), iters, warm=10)
     for p in probs:
         assert p.md.status() == 0, "device status flags set"
     kvb = kv_bytes(layout)
     out = {"workload": spec.name, "ms_per_step_graph": round(ms_graph, 4),
            "ms_per_step_eager": round(ms_eager, 4),
+           f"ms_per_step_graph_of_{per_graph}_steps": round(ms_multi, 4),
            "kv_read_GBps_graph": round(kvb / ms_graph / 1e6, 1),
-           "kv_read_GBps_eager": round(kvb / ms_eager / 1e6, 1)}
-    del graphs, probs
+           "kv_read_GBps_eager": round(kvb / ms_eager / 1e6, 1),
+           f"kv_read_GBps_graph_of_{per_graph}_steps": round(kvb / ms_multi / 1e6, 1)}
+    del graphs, multi, probs
     torch.cuda.empty_cache()
     return out
 
@@ -461,6 +472,9 @@ def bench_copy(iters: int, nbytes: int = 1 << 30):
             "ms": round(ms, 4), "GBps_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}
 
 
+# Untimed run of a step before its warm-up steps (seconds).
+SETTLE_S = 0.25
+
 # The workload the headline line is quoted on: the largest single-GPU decode
 # batch (Qwen3-235B-shaped, one layer on one GPU, 1.42 M cached tokens).
 HEADLINE = "qwen3_235b_decode"
@@ -488,6 +502,16 @@ def bench_decode_step(spec, steps: int, warmup: int, extras: bool) -> dict:
     torch.cuda.synchronize()
 
     def timed_steps(step):
+        # settle: the first ~50 ms of launches after the inputs are generated
+        # run up to 15% slower (the GPU leaving its idle state); run the step
+        # untimed for SETTLE_S, then the warm-up steps, then the timed ones
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < SETTLE_S:
+            step(i)
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads
-from tests.oracle_ref import LSE_ATOL, TOL, errors, oracle_full
+from tests.oracle_ref import LSE_ATOL, TOL, errors, oracle_full, oracle_requests
 
 pytestmark = pytest.mark.gpu
 
@@ -93,3 +93,69 @@ def test_graph_replay_matches_oracle():
     print(f"[parity] graph replay: max_abs={max_abs:.2e} rel={rel:.2e}", flush=True)
     assert max_abs <= TOL["bf16"][0] and rel <= TOL["bf16"][1]
     np.testing.assert_allclose(prob.lse_np(), ref_lse, rtol=0, atol=LSE_ATOL)
+
+
+def _capture_fused(prob, noalloc=False):
+    """Capture the one-call step (forward_with_metadata with the cache write)."""
+    import paged_kv_attention_02_amd as pka
+
+    def step():
+        if noalloc:
+            pka.forward_with_metadata_noalloc(prob.ctx, prob.mode, prob.md, prob.seq_lens, None,
+                                              prob.page_table, prob.values.q, prob.k_new, prob.v_new,
+                                              prob.k_pool, prob.v_pool, prob.out, prob.lse)
+        else:
+            prob.fused_step()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    return g, step
+
+
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_graph_replay_with_fewer_live_requests(noalloc):
+    """A step captured for 64 requests replayed with 64, 33 and 17 live ones.
+    Padding convention: a padded request has seq_len 1 and its page-table row
+    points at one reserved page no live request uses (the reserved page takes
+    the padded rows' cache writes; their outputs are unspecified).  Each
+    replay's live rows equal the same padded step run eagerly bit for bit, and
+    the oracle within the gates."""
+    spec = workloads.WORKLOADS["llama3_8b_decode"].replace(batch=64, seq_len_args=(30, 1500), seed=75)
+    layout = workloads.make_layout(spec)
+    values = workloads.make_values(layout, device="cuda")
+    prob = GpuProblem(layout, values)
+    g, step = _capture_fused(prob, noalloc)
+    reserved = int(layout.page_table[63, 0])  # a page of a request that is padding below
+    full_lens, full_table = prob.seq_lens.clone(), prob.page_table.clone()
+    for live in (64, 33, 17):
+        prob.seq_lens.copy_(full_lens)
+        prob.page_table.copy_(full_table)
+        if live < 64:
+            prob.seq_lens[live:] = 1
+            prob.page_table[live:, 0] = reserved
+        prob.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert prob.md.status() == 0
+        got, got_lse = prob.out[:live].clone(), prob.lse[:live].clone()
+        prob.out.fill_(float("nan"))
+        step()  # the same padded step, eagerly
+        torch.cuda.synchronize()
+        assert torch.equal(got, prob.out[:live]) and torch.equal(got_lse, prob.lse[:live]), live
+        ref = oracle_requests(layout, values, list(range(live)))
+        ref_out = np.concatenate([ref[b][1] for b in range(live)])
+        ref_lse = np.concatenate([ref[b][2] for b in range(live)])
+        out = got.float().cpu().numpy().astype(np.float64)
+        max_abs, rel = errors(out, ref_out)
+        print(f"[graph] 64-request graph, {live} live: bit-identical to eager; max_abs={max_abs:.2e} "
+              f"rel={rel:.2e}", flush=True)
+        assert max_abs <= TOL["bf16"][0] and rel <= TOL["bf16"][1]
+        np.testing.assert_allclose(got_lse.cpu().numpy(), ref_lse, rtol=0, atol=LSE_ATOL)
