@@ -1071,9 +1071,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a, MetaArgs 
         const int32_t* row = m.page_table + (int64_t)b * m.pt_stride;
         const int32_t chunk = (p1 - p0 + gridDim.y - 1) / gridDim.y;
         const int32_t i0 = p0 + blockIdx.y * chunk, i1 = min(p1, i0 + chunk);
-        for (int32_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
-            const int32_t pg = min(max(row[i - p0], 0), a.num_pages - 1);
-            if (i < m.max_kv_pages) m.kv_indices[i] = pg;
+        // four page ids per thread, all loaded before any is stored (a store
+        // may alias the next load, so the loop would otherwise make one
+        // round trip per id)
+        constexpr int PER = 4;
+        for (int32_t i = i0 + threadIdx.x; i < i1; i += PER * blockDim.x) {
+            int32_t pg[PER];
+            #pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int32_t j = i + k * blockDim.x;
+                pg[k] = j < i1 ? row[j - p0] : 0;
+            }
+            #pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int32_t j = i + k * blockDim.x;
+                if (j < i1 && j < m.max_kv_pages) m.kv_indices[j] = min(max(pg[k], 0), a.num_pages - 1);
+            }
         }
         if (blockIdx.y == 0 && threadIdx.x == 0) {
             const int32_t last = a.kv_last_page_len[b];  // position L - 1 is in page p1 - p0 - 1

@@ -16,8 +16,6 @@
 namespace pka {
 namespace {
 
-constexpr int SORT_MAX = 2048;  // extend items sorted in LDS (heaviest first)
-constexpr int RANK_MAX = 512;   // up to this many, by rank (no barriers) instead of bitonic
 constexpr int SCAN_THREADS = 256;  // small workgroups: cheap barriers, more of them share the gather
 
 // Inclusive block scan of NV int64 values per thread: a shuffle scan inside
@@ -51,8 +49,8 @@ __device__ inline void block_scan(int64_t (&x)[NV], int64_t* sh) {
 }
 
 __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
-    // scan scratch, then the sorted extend items (at most SORT_MAX)
-    __shared__ int64_t sh[SCAN_THREADS > SORT_MAX ? SCAN_THREADS : SORT_MAX];
+    // scan scratch
+    __shared__ int64_t sh[SCAN_THREADS];
     __shared__ int64_t carry[4];
     __shared__ int32_t s_status;
     // per-request prefixes kept in LDS when the gather is fused (B <= FUSE_MAX_B)
@@ -223,150 +221,109 @@ __global__ __launch_bounds__(SCAN_THREADS) void md_scan_kernel(MetaArgs a) {
         }
     }
     if (!a.is_decode) {
-        // Extend items (request, query tile), heaviest first: a tile's cost
-        // grows with the last key position it attends to.
+        // Extend items (request, query tile of tq tokens), request by
+        // request: the workgroups of one KV head run on one XCD in list order,
+        // so the ones resident together work on one or two requests and
+        // share their K/V pages in that XCD's L2 (a K/V head of a request is
+        // at most a few MB; several requests at once overflow the L2).  A
+        // tile's cost grows with the last key position it attends to, so
+        // each request's tiles go last to first (heaviest first) and the
+        // requests go longest first (ties: lower index first), which keeps
+        // the heaviest items at the front of the list.  Batches beyond
+        // FUSE_MAX_B requests keep request order.
         const int32_t tq = a.ext_tq;
         const int64_t cap = plan_ext_capacity(a.B, a.N, tq);
         int32_t* items = a.plan + plan_ext_items(a.B);
-        const bool fused = a.B <= FUSE_MAX_B;
         __shared__ int32_t s_count;
-        __shared__ int32_t sI[FUSE_MAX_B + 1];  // fused: each request's first item
-        __shared__ __align__(16) uint32_t keys[SORT_MAX];
+        __shared__ int32_t sI[FUSE_MAX_B + 1];  // first item of each request (request order)
+        __shared__ int32_t sR[FUSE_MAX_B];      // fused: rank of each request
+        __shared__ int32_t sS[FUSE_MAX_B + 1];  // fused: first item of each rank
         if (t == 0) s_count = 0;
         __syncthreads();
-        // sort key of item i = (request b, query tile ti): its weight, then
-        // the index (ties: lower index first); 0 is left for padding
-        auto key_of = [&](int32_t b, int32_t ti, int32_t i, int32_t L, int32_t n) {
-            const int32_t last = L - n + min((ti + 1) * tq, n);  // keys of the tile's last row
-            const uint32_t wgt = (uint32_t)min(last, (1 << 20) - 1);
-            return ((wgt << 11) | (uint32_t)(SORT_MAX - 1 - i)) + 1;
+        auto tiles_of = [&](int32_t b) {  // query tiles of request b (fused: from the LDS prefix)
+            return (sQ[b + 1] - sQ[b] + tq - 1) / tq;
         };
-        // fused: the request of item i, by binary search over sI
-        auto request_of = [&](int32_t i) {
-            int32_t lo = 0, hi = a.B - 1;  // largest b with sI[b] <= i
-            while (lo < hi) {
-                const int32_t mid = (lo + hi + 1) >> 1;
-                if (sI[mid] <= i) lo = mid; else hi = mid - 1;
-            }
-            return lo;
-        };
-        if (fused) {
-            // every request's first item (exclusive prefix of its tile
-            // count, from the LDS query prefix)
-            for (int32_t base = 0; base < a.B; base += SCAN_THREADS) {
-                const int32_t b = base + t;
-                int64_t x[1] = {b < a.B ? (sQ[b + 1] - sQ[b] + tq - 1) / tq : 0};
+        // exclusive prefix of v[0 .. n) into out[0 .. n], in chunks of the
+        // workgroup (s_count carries the running total)
+        auto prefix = [&](int32_t n, auto value, int32_t* out) {
+            for (int32_t base = 0; base < n; base += SCAN_THREADS) {
+                const int32_t j = base + t;
+                int64_t x[1] = {j < n ? (int64_t)value(j) : 0};
                 const int64_t own = x[0];
                 block_scan<1>(x, sh);
-                if (b < a.B) sI[b] = s_count + (int32_t)(x[0] - own);
+                if (j < n) out[j] = s_count + (int32_t)(x[0] - own);
                 __syncthreads();
                 if (t == SCAN_THREADS - 1) s_count += (int32_t)x[0];
                 __syncthreads();
             }
-            if (t == 0) sI[a.B] = s_count;
+            if (t == 0) out[n] = s_count;
             __syncthreads();
-        } else {
-            // large batches: serial over requests, tiles in parallel
-            for (int32_t b = 0; b < a.B; ++b) {
-                const int32_t q0 = a.qo_indptr[b], q1 = a.qo_indptr[b + 1];
-                const int32_t tiles = (q1 - q0 + tq - 1) / tq;
-                for (int32_t i = t; i < tiles; i += SCAN_THREADS) {
-                    const int32_t slot = s_count + i;
-                    if (slot < cap) {
-                        items[2 * slot] = b;
-                        items[2 * slot + 1] = i;
-                    }
-                }
-                __syncthreads();
-                if (t == 0) s_count += tiles;
-                __syncthreads();
-            }
-        }
-        int32_t count = s_count;
-        if (count > cap) { flags |= PKA_DEV_CAPACITY; count = (int32_t)cap; }
-        if (fused && count > SORT_MAX) {
-            // too many to sort in LDS: request order
-            for (int32_t i = t; i < count; i += SCAN_THREADS) {
-                const int32_t b = request_of(i);
-                items[2 * i] = b;
-                items[2 * i + 1] = i - sI[b];
-            }
-        } else if (fused && count <= RANK_MAX) {
-            // few items: each one's place is the number of heavier keys
-            const int32_t c4 = (count + 3) & ~3;
-            for (int32_t i = t; i < c4; i += SCAN_THREADS) {
-                uint32_t key = 0;  // padding counts as lightest
-                if (i < count) {
-                    const int32_t b = request_of(i);
-                    key = key_of(b, i - sI[b], i, sLen[b], sQ[b + 1] - sQ[b]);
-                }
-                keys[i] = key;
-            }
-            __syncthreads();
-            for (int32_t i = t; i < count; i += SCAN_THREADS) {
-                const uint32_t k = keys[i];
+        };
+        int32_t count;
+        if (a.B <= FUSE_MAX_B) {
+            // rank of request b: requests that are longer, or as long and
+            // earlier (the lengths are in LDS; every thread reads the same
+            // entry at a time)
+            for (int32_t b = t; b < a.B; b += SCAN_THREADS) {
+                const int32_t L = sLen[b];
                 int32_t r = 0;
-                for (int32_t j = 0; j < c4; j += 4) {
-                    const uint4 v = *(const uint4*)(keys + j);
-                    r += (v.x > k) + (v.y > k) + (v.z > k) + (v.w > k);
+                for (int32_t j = 0; j < a.B; ++j) {
+                    const int32_t Lj = sLen[j];
+                    r += (Lj > L) | ((Lj == L) & (j < b));
                 }
-                const int32_t b = request_of(i);
-                items[2 * r] = b;
-                items[2 * r + 1] = i - sI[b];
-            }
-        } else if (count <= SORT_MAX && count > 1) {
-            // bitonic sort in LDS (descending)
-            int n2 = 1;
-            while (n2 < count) n2 <<= 1;
-            for (int i = t; i < n2; i += SCAN_THREADS) {
-                uint32_t key = 0;  // padding sorts last
-                if (i < count) {
-                    if (fused) {
-                        const int32_t b = request_of(i);
-                        key = key_of(b, i - sI[b], i, sLen[b], sQ[b + 1] - sQ[b]);
-                    } else {
-                        const int32_t b = items[2 * i], ti = items[2 * i + 1];
-                        key = key_of(b, ti, i, F[b + 1] - F[b], a.qo_indptr[b + 1] - a.qo_indptr[b]);
-                    }
-                }
-                keys[i] = key;
+                sR[b] = r;
+                sS[r] = tiles_of(b);  // tile count by rank, scanned in place below
             }
             __syncthreads();
-            for (int k = 2; k <= n2; k <<= 1) {
-                for (int jj = k >> 1; jj > 0; jj >>= 1) {
-                    for (int i = t; i < n2; i += SCAN_THREADS) {
-                        const int ixj = i ^ jj;
-                        if (ixj > i) {
-                            const uint32_t x = keys[i], y = keys[ixj];
-                            const bool desc = (i & k) == 0;
-                            if (desc ? (x < y) : (x > y)) {
-                                keys[i] = y;
-                                keys[ixj] = x;
-                            }
-                        }
+            prefix(a.B, [&](int32_t r) { return sS[r]; }, sS);
+            if (t == 0) s_count = 0;
+            __syncthreads();
+            prefix(a.B, tiles_of, sI);
+            count = sI[a.B];
+            if (count > cap) { flags |= PKA_DEV_CAPACITY; count = (int32_t)cap; }
+            // item i of the request-order list: request b (largest b with
+            // sI[b] <= i), tile i - sI[b]; its place: the rank's first item
+            // plus its distance from the request's last tile
+            for (int32_t i = t; i < sI[a.B]; i += SCAN_THREADS) {
+                int32_t lo = 0, hi = a.B - 1;
+                while (lo < hi) {
+                    const int32_t mid = (lo + hi + 1) >> 1;
+                    if (sI[mid] <= i) lo = mid; else hi = mid - 1;
+                }
+                const int32_t b = lo, ti = i - sI[b];
+                const int32_t pos = sS[sR[b]] + (sI[b + 1] - sI[b] - 1 - ti);
+                if (pos < count) {
+                    items[2 * pos] = b;
+                    items[2 * pos + 1] = ti;
+                }
+            }
+        } else {
+            // large batches: request order, SCAN_THREADS requests at a time;
+            // the chunk's items are written by all threads in parallel
+            __shared__ int32_t cI[SCAN_THREADS + 1];
+            for (int32_t base = 0; base < a.B; base += SCAN_THREADS) {
+                const int32_t nb = min(SCAN_THREADS, a.B - base);
+                prefix(nb, [&](int32_t j) {
+                    const int32_t b = base + j;
+                    return (a.qo_indptr[b + 1] - a.qo_indptr[b] + tq - 1) / tq;
+                }, cI);
+                for (int32_t i = cI[0] + t; i < cI[nb]; i += SCAN_THREADS) {
+                    int32_t lo = 0, hi = nb - 1;
+                    while (lo < hi) {
+                        const int32_t mid = (lo + hi + 1) >> 1;
+                        if (cI[mid] <= i) lo = mid; else hi = mid - 1;
                     }
-                    __syncthreads();
+                    const int32_t ti = i - cI[lo];
+                    const int32_t pos = cI[lo] + (cI[lo + 1] - cI[lo] - 1 - ti);
+                    if (pos < cap) {
+                        items[2 * pos] = base + lo;
+                        items[2 * pos + 1] = ti;
+                    }
                 }
+                __syncthreads();  // cI is rewritten by the next chunk
             }
-            // the item list in sorted order (large batches stage the unsorted
-            // list through LDS first)
-            for (int i = t; i < count; i += SCAN_THREADS) {
-                const int32_t src = SORT_MAX - 1 - (int32_t)((keys[i] - 1) & (SORT_MAX - 1));
-                if (fused) {
-                    const int32_t b = request_of(src);
-                    items[2 * i] = b;
-                    items[2 * i + 1] = src - sI[b];
-                } else {
-                    sh[i] = ((int64_t)items[2 * src] << 32) | (uint32_t)items[2 * src + 1];
-                }
-            }
-            if (!fused) {
-                __syncthreads();
-                for (int i = t; i < count; i += SCAN_THREADS) {
-                    items[2 * i] = (int32_t)(sh[i] >> 32);
-                    items[2 * i + 1] = (int32_t)(sh[i] & 0xffffffff);
-                }
-            }
+            count = s_count;
+            if (count > cap) { flags |= PKA_DEV_CAPACITY; count = (int32_t)cap; }
         }
         if (t == 0) a.plan[PLAN_EXT_COUNT] = count;
     }
