@@ -212,19 +212,23 @@ __device__ inline void load_v(VTile<DK, DV, FP8>& T, int32_t slot, const uint8_t
 
 // S^T = K . Q^T for one tile, two 16-token row blocks, K from the wave's LDS
 // tile: lane (n, j) of row block sb reads chunk 4 s + j of token 16 sb + n.
-template <int DK, int DV, bool FP8>
-__device__ inline void tile_scores(const uint8_t* kst, const bf16x8_t* qop, f32x4_t (&st)[2], int j) {
+// qop(ks): the Q^T operand of k-step ks.
+template <int DK, int DV, bool FP8, typename QOp>
+__device__ inline void tile_scores(const uint8_t* kst, QOp qop, f32x4_t (&st)[2], int j) {
     using S = DecodeShape<DK, DV, FP8>;
     const int n = threadIdx.x & 15;
     auto kraw = [&](int sb, int s) -> u32x4_t {
         const int row = 16 * sb + n;
         return *(lds_u32x4_t*)(kst + row * S::KROW + 16 * S::kswz(row, 4 * s + j));
     };
+    // k-step outer: one Q^T operand per k-step serves both row blocks (each
+    // block's accumulation still runs over the k-steps in order)
+    st[0] = st[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < S::KSTEPS; ++ks) {
+        const bf16x8_t q = qop(ks);
         #pragma unroll
-        for (int ks = 0; ks < S::KSTEPS; ++ks) {
+        for (int sb = 0; sb < 2; ++sb) {
             u32x4_t kw;
             if constexpr (FP8) {
                 const u32x4_t raw = kraw(sb, ks / S::SPL);
@@ -235,7 +239,7 @@ __device__ inline void tile_scores(const uint8_t* kst, const bf16x8_t* qop, f32x
             } else {
                 kw = kraw(sb, ks);
             }
-            st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), qop[ks], st[sb], 0, 0, 0);
+            st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), q, st[sb], 0, 0, 0);
         }
     }
 }
@@ -820,16 +824,30 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     if constexpr (EARLY) prep_new_token(nx, nt);
     Rows crow = rows_of(cur.seg);  // query rows of cur's request
     Col col = column(cur, crow);
-    bf16x8_t qop[S::KSTEPS];
+    // The Q^T operand of the unit: held in registers from its first tile on
+    // (128-wide keys and less), or read from the LDS buffer at every tile
+    // (192-wide keys: six k-steps would take 24 more registers and push the
+    // kernel into spills).  Either way the reads of the buffer are done
+    // before the next unit's queries are loaded into it, which happens after
+    // the scores of the unit's last tile.
+    constexpr bool QLDS = DK > 128;
+    bf16x8_t qreg[QLDS ? 1 : S::KSTEPS];
+    auto q_lds = [&](int ks) {
+        const u32x4_t v = *(lds_u32x4_t*)(qbuf + 1024 * ks + 16 * lane);
+        return as_bf16x8(col.ok ? v : u32x4_t{0u, 0u, 0u, 0u});
+    };
+    auto qop = [&](int ks) {
+        if constexpr (QLDS) return q_lds(ks);
+        else return qreg[ks];
+    };
     auto take_q = [&]() {
-        #pragma unroll
-        for (int ks = 0; ks < S::KSTEPS; ++ks) {
-            const u32x4_t v = *(lds_u32x4_t*)(qbuf + 1024 * ks + 16 * lane);
-            qop[ks] = as_bf16x8(col.ok ? v : u32x4_t{0u, 0u, 0u, 0u});
+        if constexpr (!QLDS) {
+            #pragma unroll
+            for (int ks = 0; ks < S::KSTEPS; ++ks) qreg[ks] = q_lds(ks);
+            // the reads are done before a later direct load refills the buffer
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            asm volatile("" ::: "memory");
         }
-        // the reads are done before a later direct load refills the buffer
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        asm volatile("" ::: "memory");
     };
     f32x4_t O[S::CPL];
     #pragma unroll
