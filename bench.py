@@ -297,8 +297,10 @@ def bench_verify(spec, iters: int, warm: int = 10):
     request) through both paths the dispatch can take: the decode path
     (speculative attention mode decode: the split-K multi-query decode kernel
     + merge) and the extend path (mode prefill).  Two copies of pools and
-    metadata are used alternately.  GB/s counts each cached token's K and V
-    once."""
+    metadata are used alternately.  The context is created for the batch's
+    draft count (max_q_per_request = n, as a server configures its number of
+    speculative tokens), which sizes the partial workspace and the merge.
+    GB/s counts each cached token's K and V once."""
     import torch
     import workloads
     import paged_kv_attention_02_amd as pka
@@ -306,8 +308,9 @@ def bench_verify(spec, iters: int, warm: int = 10):
     layout = workloads.make_layout(spec)
     values = workloads.make_values(layout, device="cuda")
     probs = []
+    max_q = int(max(layout.extend_lens))
     for _ in range(2):
-        p = GpuProblem(layout, values)
+        p = GpuProblem(layout, values, max_q_per_request=max_q)
         p.mode = "target_verify"
         p.md = pka.Batch(p.ctx, "target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages)
         p.metadata_step()
@@ -316,7 +319,7 @@ def bench_verify(spec, iters: int, warm: int = 10):
     kvb = kv_bytes(layout)
     n = sorted(set(int(x) for x in layout.extend_lens))
     out = {"workload": spec.name, "kv_tokens": layout.total_tokens, "q_tokens": layout.num_q_tokens,
-           "draft_tokens_per_request": n[0] if len(n) == 1 else n}
+           "draft_tokens_per_request": n[0] if len(n) == 1 else n, "max_q_per_request": max_q}
     for path, mode in (("decode_path", "decode"), ("extend_path", "prefill")):
         call = lambda i, m=mode: probs[i % 2].attention_step(save=False, spec_mode=m, lse=False)
         ms = time_events(call, iters, warm=warm)

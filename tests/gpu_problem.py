@@ -21,7 +21,7 @@ def sentinel_pool_gpu(shape, kv_dtype: str, device="cuda"):
 
 class GpuProblem:
     def __init__(self, layout: workloads.Layout, values: workloads.Values = None, device="cuda",
-                 fill: bool = True, prefix_only: bool = False):
+                 fill: bool = True, prefix_only: bool = False, max_q_per_request: int = 0):
         spec = layout.spec
         self.layout, self.spec = layout, spec
         if values is None:
@@ -29,7 +29,8 @@ class GpuProblem:
         self.values = values
         self.ctx = pka.Context(spec.num_q_heads, spec.num_kv_heads, spec.head_dim, spec.page_size,
                                layout.num_pages, spec.q_dtype, spec.kv_dtype, spec.softmax_scale,
-                               values.k_scale, values.v_scale, v_head_dim=spec.value_dim)
+                               values.k_scale, values.v_scale, v_head_dim=spec.value_dim,
+                               max_q_per_request=max_q_per_request)
         self.k_pool = sentinel_pool_gpu(self.ctx.pool_shape(), spec.kv_dtype, device)
         self.v_pool = sentinel_pool_gpu(self.ctx.v_pool_shape(), spec.kv_dtype, device)
         i32 = dict(dtype=torch.int32, device=device)
