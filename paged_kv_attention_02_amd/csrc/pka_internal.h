@@ -33,7 +33,10 @@ constexpr int64_t FUSE_MAX_ITEMS = (int64_t)MD_SLOTS * 1024 * FUSE_PER_THREAD;
 // Tokens per decode tile (two MFMA row blocks of 16 tokens).
 constexpr int DEC_TILE = 32;
 // Smallest share of the flattened tile range given to one workgroup (tiles).
-constexpr int DEC_MIN_SHARE = 2;
+// A small batch leaves some workgroups idle rather than give every share a
+// tile or two: each share pays a start-up chain of dependent round trips
+// (lengths, page ids, first tile) and a partial for the merge.
+constexpr int DEC_MIN_SHARE = 4;
 // Decode shares: share w is tiles [share_start(w), share_start(w + 1)) of the
 // requests' tiles laid end to end, q tiles each and one more for the first r
 // shares.
