@@ -227,6 +227,36 @@ def test_full_size_batches_are_bit_identical(name):
         np.testing.assert_allclose(prob.lse_np(), want_lse, rtol=0, atol=LSE_ATOL)
 
 
+def test_l4_log_batch_through_one_call():
+    """The batch shaped after the pages' L4 server-log line ("sglang-101
+    s4.2", section "What we measured on an L4": 33 running requests, ~20k
+    cached tokens; page size 1, 32/8 heads): the one-call step with the cache
+    write leaves what the two calls leave, bit for bit, and every request and
+    head is within the gates of the oracle."""
+    spec = workloads.EXTRA["l4_log_decode"]
+    layout = workloads.make_layout(spec)
+    assert layout.batch == 33
+    values = workloads.make_values(layout, device="cuda")
+    ref = GpuProblem(layout, values, prefix_only=True)
+    ref.step()
+    prob = GpuProblem(layout, values, prefix_only=True)
+    _scrub(prob)
+    prob.fused_step()
+    torch.cuda.synchronize()
+    assert prob.md.status() == 0
+    for k in MD_ARRAYS:
+        assert torch.equal(_md_arrays(prob)[k], _md_arrays(ref)[k]), k
+    assert torch.equal(prob.out, ref.out)
+    assert torch.equal(prob.lse, ref.lse)
+    assert torch.equal(prob.k_pool.view(torch.int16), ref.k_pool.view(torch.int16))
+    assert torch.equal(prob.v_pool.view(torch.int16), ref.v_pool.view(torch.int16))
+    want, want_lse = oracle_full(layout, values)
+    max_abs, rel = errors(prob.out_np(), want)
+    print(f"[parity] l4_log_decode one call: max_abs={max_abs:.3e} rel_rms={rel:.3e}", flush=True)
+    assert max_abs <= TOL["bf16"][0] and rel <= TOL["bf16"][1]
+    np.testing.assert_allclose(prob.lse_np(), want_lse, rtol=0, atol=LSE_ATOL)
+
+
 def test_graph_replays_of_the_one_call_step():
     spec = CASES["llama_b9_p16"]
     layout = workloads.make_layout(spec)
