@@ -1173,61 +1173,47 @@ __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
 }
 
 // MD: the decode kernel built the metadata in-kernel; the merge writes what
-// it left out: kv_indices (the gridDim.y workgroups of request b take equal
-// slices of its pages, clamped into the pool as the decode kernel read them)
-// and the request's new-token slot in out_cache_loc.  A workgroup loads its
-// first page ids before the merge and stores them after it, so their round
-// trip overlaps the merge's loads.
+// it left out: kv_indices and the request's new-token slot in out_cache_loc.
+// The grid has MERGE_GATHER_WGS more workgroups per request (grid y beyond
+// the merging ones) that only copy equal slices of the request's page ids
+// from the page table, clamped into the pool as the decode kernel read them,
+// so the copy runs beside the merge instead of inside its workgroups.
+constexpr int MERGE_GATHER_WGS = 16;
 template <int D, bool OUT_BF16, bool MD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a, MetaArgs m) {
     const int32_t b = blockIdx.x;
-    constexpr int PER = 4;  // page ids per thread and round
-    int32_t pg[PER];
-    int32_t p0 = 0, i1 = 0, ifirst = 0, last = 0;
-    bool gather = false;
-    const int32_t* row = nullptr;
-    // ids from i on, four per thread; every load is issued (indices past the
-    // slice read the request's last id, which is not stored), since a load
-    // under a lane condition would be waited for on its own
-    auto fetch = [&](int32_t i, int32_t (&v)[PER]) {
-        #pragma unroll
-        for (int k = 0; k < PER; ++k) v[k] = row[min(i + k * (int32_t)blockDim.x, last) - p0];
-    };
-    if constexpr (MD) {
-        p0 = a.kv_indptr[b];
-        const int32_t p1 = a.kv_indptr[b + 1];
-        row = m.page_table + (int64_t)b * m.pt_stride;
-        const int32_t chunk = (p1 - p0 + gridDim.y - 1) / gridDim.y;
-        const int32_t i0 = p0 + blockIdx.y * chunk;
-        i1 = min(p1, i0 + chunk);
-        last = p1 - 1;
-        ifirst = i0 + threadIdx.x;
-        gather = i1 > i0;  // uniform over the workgroup
-        if (gather) fetch(ifirst, pg);
+    const int32_t ym = (a.Hq + 3) / 4;  // merging workgroups per request
+    if (!MD || (int32_t)blockIdx.y < ym) {
+        if (blockIdx.z < a.qslots) merge_column<D, OUT_BF16>(a, b);
+        if constexpr (MD) {
+            if (blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+                const int32_t p0 = a.kv_indptr[b], pl = a.kv_indptr[b + 1] - p0 - 1;  // page of position L - 1
+                const int32_t last = a.kv_last_page_len[b];
+                const int32_t pg = min(max(m.page_table[(int64_t)b * m.pt_stride + pl], 0), a.num_pages - 1);
+                m.out_cache_loc[b] = (pg << a.page_shift) | (last - 1);
+            }
+        }
+        return;
     }
-    merge_column<D, OUT_BF16>(a, b);
     if constexpr (MD) {
-        auto put = [&](int32_t i, const int32_t (&v)[PER]) {
+        if (blockIdx.z != 0) return;
+        const int32_t p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
+        const int32_t* row = m.page_table + (int64_t)b * m.pt_stride;
+        const int32_t chunk = (p1 - p0 + MERGE_GATHER_WGS - 1) / MERGE_GATHER_WGS;
+        const int32_t i0 = p0 + (blockIdx.y - ym) * chunk, i1 = min(p1, i0 + chunk);
+        // four ids per thread and round, all loaded before any is stored (a
+        // store may alias the next load); every load is issued, indices past
+        // the slice reading the request's last id, which is not stored
+        constexpr int PER = 4;
+        for (int32_t i = i0 + threadIdx.x; i < i1; i += PER * blockDim.x) {
+            int32_t v[PER];
+            #pragma unroll
+            for (int k = 0; k < PER; ++k) v[k] = row[min(i + k * (int32_t)blockDim.x, p1 - 1) - p0];
             #pragma unroll
             for (int k = 0; k < PER; ++k) {
                 const int32_t j = i + k * blockDim.x;
                 if (j < i1 && j < m.max_kv_pages) m.kv_indices[j] = min(max(v[k], 0), a.num_pages - 1);
             }
-        };
-        if (gather) {
-            put(ifirst, pg);
-            // larger slices: further rounds, each loaded whole before it is
-            // stored (a store may alias the next load)
-            for (int32_t i = ifirst + PER * blockDim.x; i < i1; i += PER * blockDim.x) {
-                int32_t v[PER];
-                fetch(i, v);
-                put(i, v);
-            }
-        }
-        if (blockIdx.y == 0 && threadIdx.x == 0) {
-            const int32_t lastlen = a.kv_last_page_len[b];  // position L - 1 is in page p1 - p0 - 1
-            const int32_t pgl = min(max(row[a.kv_indptr[b + 1] - p0 - 1], 0), a.num_pages - 1);
-            m.out_cache_loc[b] = (pgl << a.page_shift) | (lastlen - 1);
         }
     }
 }
@@ -1249,7 +1235,7 @@ size_t decode_md_lds_bytes(int waves, int32_t B) {
 // the metadata; the merge then writes kv_indices and out_cache_loc).
 template <int DV>
 hipError_t launch_merge(pka_dtype q, const AttnArgs& a, const MetaArgs* md, hipStream_t s) {
-    const dim3 mgrid(a.B, (a.Hq + 3) / 4, a.qslots);
+    const dim3 mgrid(a.B, (a.Hq + 3) / 4 + (md ? MERGE_GATHER_WGS : 0), a.qslots);
     const MetaArgs none{};
     if (md && q == PKA_BF16)
         hipLaunchKernelGGL((decode_merge_kernel<DV, true, true>), mgrid, dim3(256), 0, s, a, *md);
