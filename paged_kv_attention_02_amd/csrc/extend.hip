@@ -385,9 +385,19 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                                                        0, 0, 0);
     };
 
-    // raw scores of the current and the next tile (the two sets swap roles
-    // from one iteration to the next)
-    f32x16_t SA[SB], SBn[SB];
+    // Where the next tile's scores are computed.  Equal widths: inside the
+    // P.V block, interleaved with the exponentials (two score sets that swap
+    // roles from one iteration to the next).  Wider keys (192/128): after
+    // the block, into the registers this tile's scores held; the score
+    // phase is then long enough on its own (24 MFMAs) and one score set
+    // fewer leaves registers to the block.
+    constexpr bool SPLITQK = DK > DV;
+    f32x16_t SA[SB], SBn[SPLITQK ? 1 : SB];
+    auto second = [&]() -> f32x16_t (&)[SB] {
+        if constexpr (SPLITQK) return SA;
+        else return SBn;
+    };
+    f32x16_t (&SB2)[SB] = second();
 
     // prologue: K(0), V(0), K(1) resident, S(0) computed
     int32_t pgK = 0, pgV = 0;        // BIGPAGE: pages of tiles t+2 (K) and t+1 (V)
@@ -538,7 +548,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
                                                         __builtin_bit_cast(bf16x2_t, ones), lsum, false);
             }
-            if constexpr (NEXT) {
+            if constexpr (NEXT && !SPLITQK) {
                 #pragma unroll
                 for (int qq = 0; qq < QPK; ++qq) qk_mfma(knext, pk * QPK + qq, Sn);
             }
@@ -557,6 +567,10 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 O[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), pop, O[c], 0, 0, 0);
             }
         }
+        if constexpr (NEXT && SPLITQK) {
+            #pragma unroll
+            for (int q = 0; q < KSTEPS * SB; ++q) qk_mfma(knext, q, Sn);
+        }
         // fp8: the next tiles go into the stages this iteration did not read;
         // the next iteration's barrier publishes them
         if constexpr (FP8) {
@@ -569,14 +583,14 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     using T_ = std::integral_constant<bool, true>;
     int32_t t = 0;
     for (; t + 2 < ntiles; t += 2) {
-        iteration(F_{}, T_{}, t, SA, SBn);
-        iteration(T_{}, T_{}, t + 1, SBn, SA);
+        iteration(F_{}, T_{}, t, SA, SB2);
+        iteration(T_{}, T_{}, t + 1, SB2, SA);
     }
     if (t + 1 < ntiles) {
-        iteration(F_{}, T_{}, t, SA, SBn);
-        iteration(T_{}, F_{}, t + 1, SBn, SA);
+        iteration(F_{}, T_{}, t, SA, SB2);
+        iteration(T_{}, F_{}, t + 1, SB2, SA);
     } else {
-        iteration(F_{}, F_{}, t, SA, SBn);
+        iteration(F_{}, F_{}, t, SA, SB2);
     }
 
     // finish: the two lanes of a column hold halves of the sums
