@@ -1080,21 +1080,33 @@ __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
     const int lane = threadIdx.x & 63;
     const int32_t h = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (h >= a.Hq) return;
+    // The partition, the request's tile range and its query rows, read
+    // together (one round trip; the wait below keeps the compiler from
+    // issuing them one branch at a time).
     const int32_t* plan = a.plan;
-    const int64_t shq = plan[PLAN_SHARE], shr = plan[PLAN_SHARE_REM];
     const int32_t* T = plan + plan_tile_prefix(a.B);
-    const int64_t t0 = T[b], t1 = T[b + 1];
+    const uint32_t shq = (uint32_t)load_uniform(plan, PLAN_SHARE);
+    const uint32_t shr = (uint32_t)load_uniform(plan, PLAN_SHARE_REM);
+    const int32_t t0 = load_uniform(T, b), t1 = load_uniform(T, b + 1);
+    const int32_t qa = load_uniform(a.qo_indptr, b), qb = load_uniform(a.qo_indptr, b + 1);
+    asm volatile("" ::"s"(shq), "s"(shr), "s"(t0), "s"(t1), "s"(qa), "s"(qb));
     if (t1 <= t0) return;
-    const int64_t w0 = share_of(t0, shq, shr), w1 = share_of(t1 - 1, shq, shr);
+    // share_of in 32 bits: tile indices and both partition words fit, and
+    // shr * (shq + 1) <= total tiles (shq >= DEC_MIN_SHARE)
+    auto share32 = [&](uint32_t t) -> int32_t {
+        const uint32_t big = shr * (shq + 1);
+        return (int32_t)(t < big ? t / (shq + 1) : shr + (t - big) / shq);
+    };
+    const int32_t w0 = share32((uint32_t)t0), w1 = share32((uint32_t)(t1 - 1));
     if (w0 == w1) return;  // written directly by its only workgroup
-    const int32_t np = (int32_t)(w1 - w0 + 1);
+    const int32_t np = w1 - w0 + 1;
     // query rows of the request (one without multi-query partials)
     int32_t q0, nq;
     if (a.qslots > 1) {
-        q0 = a.qo_indptr[b];
-        nq = min(a.qo_indptr[b + 1] - q0, a.qslots);
+        q0 = qa;
+        nq = min(qb - qa, a.qslots);
     } else {
-        q0 = min(max(a.qo_indptr[b + 1] - 1, 0), a.N - 1);
+        q0 = min(max(qb - 1, 0), a.N - 1);
         nq = 1;
     }
     const int64_t lstride = (int64_t)a.qslots * a.Hq;  // per partial
@@ -1102,8 +1114,8 @@ __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
     const int32_t qi = blockIdx.z;
     if (qi >= nq) return;
     {
-        const float* lse_col = a.ws_lse + ((b + w0) * a.qslots + qi) * a.Hq + h;
-        const float* o_col = a.ws_o + (((b + w0) * a.qslots + qi) * a.Hq + h) * D;
+        const float* lse_col = a.ws_lse + ((int64_t)(b + w0) * a.qslots + qi) * a.Hq + h;
+        const float* o_col = a.ws_o + (((int64_t)(b + w0) * a.qslots + qi) * a.Hq + h) * D;
 
         float M = -INFINITY;
         float den = 0.f, acc[EPL];
