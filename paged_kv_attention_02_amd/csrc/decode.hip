@@ -636,17 +636,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
                                         : __builtin_amdgcn_readfirstlane(sT[i]);
         else return load_uniform(T, i);
     };
-    // MD: the page id at page k of request sg from the page table, clamped
-    // into the pool
     const int32_t P = 1 << a.page_shift;
-    auto table_page = [&](int32_t sg, int32_t k) {
-        int32_t pg = m.page_table[(int64_t)sg * m.pt_stride + k];
-        if (pg < 0 || pg >= a.num_pages) {
-            pflags = 1;
-            pg = min(max(pg, 0), a.num_pages - 1);
-        }
-        return pg;
-    };
 
     // one pool slot, all KV heads
     const int64_t krow = (int64_t)a.Hkv * DK * S::ESZ, vrow = (int64_t)a.Hkv * DV * S::ESZ;
@@ -702,7 +692,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             if (hi <= lo) continue;
             if constexpr (MQ) {
                 const int32_t nb = load_uniform(a.qo_indptr, sg + 1) - load_uniform(a.qo_indptr, sg);
-                if (nb > a.qslots && lo == 0 && lane == 0 && unit == 0)
+                // (every lane: a lane condition inside this loop would make
+                // the compiler keep the whole iterator in vector registers)
+                if (nb > a.qslots && lo == 0 && unit == 0)
                     atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_LENGTH);
                 // no query rows, or none in this wave's passes
                 if (16 * ps >= min(nb, a.qslots) * nh) continue;
@@ -731,14 +723,33 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             open_piece(cur.seg + 1, nx);
         }
     };
-    // pool slot of tile token `tok`; positions past the piece repeat its last
-    // token (loaded, never counted).  MD: the page id comes from the page
-    // table.
-    auto slot_for = [&](const It& it) {
+    // Pool slot of tile token `tok`; positions past the piece repeat its last
+    // token (loaded, never counted).  In two halves: page_id loads the page
+    // id (MD: from the page table; else from kv_indices, the index clamped
+    // into it), and slot_from clamps it into the pool (MD: flagging an id
+    // outside it) and adds the offset in the page.  The id of the tile after
+    // next is loaded a step ahead and used only after the next step's wait:
+    // loads complete in order, so a use right after the load would wait for
+    // the tile loads issued before it as well.
+    auto page_id = [&](const It& it) -> int32_t {
         const int32_t pos = it.t0 + tok;
         const int32_t pc = pos < it.hi ? pos : it.hi - 1;
-        if constexpr (MD) return (table_page(it.seg, pc >> a.page_shift) << a.page_shift) | (pc & (P - 1));
-        else return slot_of(a, it.pb, pc);
+        if constexpr (MD) {
+            return m.page_table[(int64_t)it.seg * m.pt_stride + (pc >> a.page_shift)];
+        } else {
+            int64_t idx = (int64_t)it.pb + (pc >> a.page_shift);
+            idx = idx < a.kv_cap ? idx : a.kv_cap - 1;
+            return a.kv_indices[idx];
+        }
+    };
+    auto slot_from = [&](const It& it, int32_t pg) {
+        const int32_t pos = it.t0 + tok;
+        const int32_t pc = pos < it.hi ? pos : it.hi - 1;
+        if (pg < 0 || pg >= a.num_pages) {
+            if constexpr (MD) pflags = 1;
+            pg = min(max(pg, 0), a.num_pages - 1);
+        }
+        return (pg << a.page_shift) | (pc & (P - 1));
     };
     // this lane's column of a unit: query token qi, head h
     struct Col {
@@ -814,13 +825,13 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     if (nt.on) store_new_token<DK, DV, FP8>(a, nt.w, nt.slot, g, lane);
     VTile<DK, DV, FP8> A, Bt;
     {
-        const int32_t s0 = slot_for(cur);
+        const int32_t s0 = slot_from(cur, page_id(cur));
         load_k<DK, DV, FP8>(kst, s0, kbase, krow);
         load_v(A, s0, vbase, vrow, n, j);
     }
     fetch_q(cur);
     advance(cur, nx);
-    int32_t s_nx = nx.seg < a.B ? slot_for(nx) : 0;
+    int32_t id_nx = nx.seg < a.B ? page_id(nx) : 0;  // tile nx's page id, turned into its slot in the step
     if constexpr (EARLY) prep_new_token(nx, nt);
     Rows crow = rows_of(cur.seg);  // query rows of cur's request
     Col col = column(cur, crow);
@@ -916,6 +927,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             else __builtin_amdgcn_s_setprio(0);
         }
         if (nx.seg < a.B) {
+            const int32_t s_nx = slot_from(nx, id_nx);  // its id landed before this step's wait
             const bool opens = nx.t0 == nx.lo;  // nx is the first tile of its unit
             if constexpr (EARLY) {
                 if (nt.on) store_new_token<DK, DV, FP8>(a, nt.w, nt.slot, g, lane);
@@ -929,7 +941,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             if (opens) fetch_q(nx);
         }
         advance(nx, nn);
-        const int32_t s_nn = nn.seg < a.B ? slot_for(nn) : 0;
+        const int32_t id_nn = nn.seg < a.B ? page_id(nn) : 0;
         if constexpr (EARLY) prep_new_token(nn, nt);
         tile_update<DK, DV, FP8, MQ>(X, st, O, m2, lsum, col.kend - cur.t0, a.scale_log2, j);
         if (cur.t0 + DEC_TILE >= cur.hi) {  // last tile of its unit
@@ -944,7 +956,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         }
         cur = nx;
         nx = nn;
-        s_nx = s_nn;
+        id_nx = id_nn;
         return true;
     };
     for (;;) {
