@@ -109,19 +109,32 @@ int32_t decode_qslots(const pka_ctx* ctx, pka_forward_mode m, int32_t num_q_toke
     return std::max(1, std::min<int32_t>(ctx->max_q, num_q_tokens));
 }
 
-// Waves per head group on the decode path.  A verify batch whose query
-// columns (tokens x heads of a group) need several 16-column passes gives
-// them to up to DEC_MAX_CSPLIT waves of one workgroup that read the same
-// tiles side by side, instead of one wave reading them once per pass.  The
-// split follows the average tokens per request; a request with fewer
-// leaves the surplus waves idle over its tiles.  bf16 / fp8 caches only.
-int32_t decode_csplit(const pka_ctx* ctx, const pka_batch* md) {
+// 16-column passes a verify batch's query columns (tokens x heads of a
+// group) need on the decode path, from the average tokens per request; 1
+// for a decode batch or an fp32 cache.
+int32_t decode_passes(const pka_ctx* ctx, const pka_batch* md) {
     if (ctx->cfg.kv_dtype == PKA_F32 || md->batch <= 0) return 1;
     const int32_t qslots = decode_qslots(ctx, md->mode, md->num_q_tokens);
     if (qslots <= 1) return 1;
     const int32_t nq = std::min<int32_t>(qslots, (md->num_q_tokens + md->batch - 1) / md->batch);
-    const int32_t passes = (nq * std::min<int32_t>(ctx->G, 16) + 15) / 16;
-    return std::max<int32_t>(1, std::min<int32_t>(passes, pka::DEC_MAX_CSPLIT));
+    return std::max<int32_t>(1, (nq * std::min<int32_t>(ctx->G, 16) + 15) / 16);
+}
+
+// Column blocks of 16 per decode wave: with several passes each wave takes
+// two adjacent blocks, so one tile stream serves 32 columns (keys of at most
+// 128; the 192-wide kernel has no registers left for a second block).
+int32_t decode_cb(const pka_ctx* ctx, const pka_batch* md) {
+    return ctx->dk <= 128 && decode_passes(ctx, md) >= 2 ? 2 : 1;
+}
+
+// Waves per head group on the decode path.  Passes beyond a wave's column
+// blocks go to up to DEC_MAX_CSPLIT waves of one workgroup that read the
+// same tiles side by side, instead of one wave reading them once per pass.
+// The split follows the average tokens per request; a request with fewer
+// leaves the surplus waves idle over its tiles.
+int32_t decode_csplit(const pka_ctx* ctx, const pka_batch* md) {
+    const int32_t cb = decode_cb(ctx, md);
+    return std::min<int32_t>((decode_passes(ctx, md) + cb - 1) / cb, pka::DEC_MAX_CSPLIT);
 }
 
 // Launch shape of a decode call with column split cs: waves per share in a
@@ -199,6 +212,7 @@ pka::AttnArgs attn_args(const pka_ctx* ctx, const pka_batch* md, const void* q, 
     a.pool_slots = (int64_t)c.num_pages * c.page_size;
     a.spw = 1;
     a.csplit = 1;
+    a.cb = 1;
     const float k_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f;
     a.scale_log2 = c.scale * 1.4426950408889634f * k_scale;
     a.v_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f;
@@ -245,6 +259,7 @@ pka_status decode_args(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
     int wpb = 1, sp = 1;
     a.csplit = decode_csplit(ctx, md);  // 1 unless several query rows per request
+    a.cb = decode_cb(ctx, md);
     decode_shape(ctx, a.csplit, spw, &wpb, &sp);
     a.nwg = nwg;
     a.spw = sp;
@@ -429,7 +444,7 @@ pka_status pka_describe(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn
         int32_t nwg = 0, base_spw = 1;
         pka_status s = batch_shares(ctx, &md, &nwg, &base_spw);
         if (s != PKA_OK) return s;
-        const int32_t cs = decode_csplit(ctx, &md);
+        const int32_t cs = decode_csplit(ctx, &md), cb = decode_cb(ctx, &md);
         int wpb = 1, spw = 1;
         decode_shape(ctx, cs, base_spw, &wpb, &spw);
         const int32_t qslots = decode_qslots(ctx, mode, num_q_tokens);
@@ -438,11 +453,12 @@ pka_status pka_describe(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn
         snprintf(tmp, sizeof tmp,
                  "path decode: %s<Dk %d, Dv %d, %s cache%s%s>, page size %d, %d query heads per KV head "
                  "(%d head group(s) of <= 16), %d shares (one resident round), %d wave(s) per share, "
-                 "%d share(s) per workgroup, %d workgroups, column split %d, %d partial row(s) per share; "
+                 "%d share(s) per workgroup, %d workgroups, %d column block(s) of 16 per wave, column split %d, "
+                 "%d partial row(s) per share; "
                  "then decode_merge_kernel<Dv %d>%s",
                  kern, ctx->dk, ctx->dv, dtype_name(c.kv_dtype), qslots > 1 ? ", several query rows" : "",
                  md_in ? ", metadata built in-kernel" : "", c.page_size, ctx->G, ctx->qgroups, nwg, wpb, spw,
-                 (nwg + spw - 1) / spw, cs, qslots, ctx->dv,
+                 (nwg + spw - 1) / spw, cb, cs, qslots, ctx->dv,
                  with_metadata && !md_in ? "; metadata by md_scan_kernel first" : "");
         d = tmp;
     } else {

@@ -140,8 +140,6 @@ struct DecodeShape {
     static constexpr int KCPR = KROW / 16;      // 16-byte chunks per K row
     static constexpr int KDMA = KCPR / 2;       // direct-to-LDS loads per lane and tile
     static constexpr int KTILE = DEC_TILE * KROW;  // bytes of the LDS K tile
-    // LDS per wave: the K tile and one Q^T operand (1 KB per k-step)
-    static constexpr int WAVE_LDS = KTILE + KSTEPS * 1024;
     static_assert(KCPR == 4 || KCPR == 8 || KCPR == 12 || KCPR == 16 || KCPR == 24, "K row width");
     // Chunk swizzle of the LDS K tile: the K operand reads 16 rows at one
     // logical chunk, and those 16 rows must hit 16 different 16-byte bank
@@ -153,6 +151,13 @@ struct DecodeShape {
              : c ^ ((row >> 2) & 3);
     }
 };
+
+// LDS bytes of one decode wave: the K tile and the queries of cb column
+// blocks (1 KB per k-step each).
+template <int DK, int DV, bool FP8>
+__host__ __device__ constexpr int decode_wave_lds(int cb) {
+    return DecodeShape<DK, DV, FP8>::KTILE + cb * DecodeShape<DK, DV, FP8>::KSTEPS * 1024;
+}
 
 typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
 
@@ -212,9 +217,10 @@ __device__ inline void load_v(VTile<DK, DV, FP8>& T, int32_t slot, const uint8_t
 
 // S^T = K . Q^T for one tile, two 16-token row blocks, K from the wave's LDS
 // tile: lane (n, j) of row block sb reads chunk 4 s + j of token 16 sb + n.
-// qop(ks): the Q^T operand of k-step ks.
-template <int DK, int DV, bool FP8, typename QOp>
-__device__ inline void tile_scores(const uint8_t* kst, QOp qop, f32x4_t (&st)[2], int j) {
+// qop(k, ks): the Q^T operand of k-step ks for column block k (CB blocks of
+// 16 columns share every K operand read).
+template <int DK, int DV, bool FP8, int CB, typename QOp>
+__device__ inline void tile_scores(const uint8_t* kst, QOp qop, f32x4_t (&st)[CB][2], int j) {
     using S = DecodeShape<DK, DV, FP8>;
     const int n = threadIdx.x & 15;
     auto kraw = [&](int sb, int s) -> u32x4_t {
@@ -223,10 +229,13 @@ __device__ inline void tile_scores(const uint8_t* kst, QOp qop, f32x4_t (&st)[2]
     };
     // k-step outer: one Q^T operand per k-step serves both row blocks (each
     // block's accumulation still runs over the k-steps in order)
-    st[0] = st[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+    for (int k = 0; k < CB; ++k) st[k][0] = st[k][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     #pragma unroll
     for (int ks = 0; ks < S::KSTEPS; ++ks) {
-        const bf16x8_t q = qop(ks);
+        bf16x8_t q[CB];
+        #pragma unroll
+        for (int k = 0; k < CB; ++k) q[k] = qop(k, ks);
         #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             u32x4_t kw;
@@ -239,7 +248,9 @@ __device__ inline void tile_scores(const uint8_t* kst, QOp qop, f32x4_t (&st)[2]
             } else {
                 kw = kraw(sb, ks);
             }
-            st[sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), q, st[sb], 0, 0, 0);
+            #pragma unroll
+            for (int k = 0; k < CB; ++k)
+                st[k][sb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kw), q[k], st[k][sb], 0, 0, 0);
         }
     }
 }
@@ -511,10 +522,12 @@ typedef __attribute__((address_space(3))) const int32_t lds_i32_t;
 // waits in the tile stream (stores count in vmcnt like loads).  The
 // partition and the page ids are those the metadata kernel would produce,
 // so the outputs are bit-identical to running it first.
-template <int DK, int DV, bool FP8, bool MQ, bool MD>
+template <int DK, int DV, bool FP8, bool MQ, bool MD, int CB = 1>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m) {
     static_assert(!(MQ && MD), "metadata is built in-kernel for one query per request only");
+    static_assert(CB == 1 || MQ, "several column blocks per wave only for several query rows");
     using S = DecodeShape<DK, DV, FP8>;
+    constexpr int WLDS = decode_wave_lds<DK, DV, FP8>(CB);  // this wave's LDS bytes
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, j = lane >> 4;
     // a workgroup holds a.spw shares of wpb waves (one KV-head unit each)
@@ -534,9 +547,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     // this wave's LDS: the K tile, then the queries of the next unit; after
     // the waves' regions, one progress word per wave
     extern __shared__ __attribute__((aligned(1024))) uint8_t dec_lds[];
-    uint8_t* const kst = dec_lds + wv * S::WAVE_LDS;
-    uint8_t* const qbuf = kst + S::KTILE;
-    int32_t* const prog = (int32_t*)(dec_lds + waves * S::WAVE_LDS);
+    uint8_t* const kst = dec_lds + wv * WLDS;
+    uint8_t* const qbuf = kst + S::KTILE;  // column block k's queries at qbuf + k * KSTEPS KB
+    int32_t* const prog = (int32_t*)(dec_lds + waves * WLDS);
     // Waves wv and wv ^ 4 of an 8-wave workgroup share a SIMD, and the one
     // with the higher priority gets the larger part of the memory pipeline
     // (equal priorities favour the older wave, ~8% on the Llama-shaped
@@ -549,7 +562,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     int32_t nst = 0;  // tiles computed so far
     if (pair) __hip_atomic_store(prog + wv, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     // MD: the metadata area, 8-byte aligned after the progress words
-    uint8_t* const md_lds = dec_lds + ((waves * (S::WAVE_LDS + 4) + 7) & ~7);
+    uint8_t* const md_lds = dec_lds + ((waves * (WLDS + 4) + 7) & ~7);
     // MD: prefixes in registers (at most 64 requests) or in LDS
     const bool md_reg = MD && a.B <= 64;
     int64_t W_md = 0;
@@ -697,12 +710,12 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
                 if (nb > a.qslots && lo == 0 && unit == 0)
                     atomicOr((int32_t*)a.plan + PLAN_STATUS, PKA_DEV_BAD_LENGTH);
                 // no query rows, or none in this wave's passes
-                if (16 * ps >= min(nb, a.qslots) * nh) continue;
+                if (16 * CB * ps >= min(nb, a.qslots) * nh) continue;
             }
             it.seg = sg;
             it.lo = lo;
             it.hi = hi;
-            it.c0 = 16 * ps;
+            it.c0 = 16 * CB * ps;
             it.pb = MD ? 0 : load_uniform(a.kv_indptr, sg);  // MD reads the page table instead
             it.t0 = lo;
             return;
@@ -716,8 +729,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         if (cur.seg >= a.B) return;
         nx.t0 = cur.t0 + DEC_TILE;
         if (nx.t0 < cur.hi) return;
-        if (MQ && cur.c0 + 16 * a.csplit < rows_of(cur.seg).nq * nh) {
-            nx.c0 = cur.c0 + 16 * a.csplit;
+        if (MQ && cur.c0 + 16 * CB * a.csplit < rows_of(cur.seg).nq * nh) {
+            nx.c0 = cur.c0 + 16 * CB * a.csplit;
             nx.t0 = cur.lo;
         } else {
             open_piece(cur.seg + 1, nx);
@@ -756,9 +769,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         bool ok;
         int32_t qi, h, qr, kend;  // keys of the column within the piece: positions < kend
     };
-    auto column = [&](const It& u, const Rows& r) {
+    auto column = [&](const It& u, const Rows& r, int k) {
         Col c;
-        const int32_t cc = u.c0 + n;
+        const int32_t cc = u.c0 + 16 * k + n;
         c.ok = MQ ? cc < r.nq * nh : n < nh;
         c.qi = MQ ? (c.ok ? cc / nh : 0) : 0;
         c.h = h0 + (MQ ? cc % nh : n);
@@ -772,13 +785,17 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     // and into registers once that tile has landed; lanes without a column
     // load nothing and take zeros.
     auto fetch_q = [&](const It& u) {
-        const Col c = column(u, rows_of(u.seg));
-        if (c.ok) {
-            const __bf16* qrow = (const __bf16*)a.q + ((int64_t)c.qr * a.Hq + c.h) * DK;
-            #pragma unroll
-            for (int ks = 0; ks < S::KSTEPS; ++ks) {
-                const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
-                lds_dma16(qrow + d0, qbuf + 1024 * ks);
+        const Rows r = rows_of(u.seg);
+        #pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            const Col c = column(u, r, k);
+            if (c.ok) {
+                const __bf16* qrow = (const __bf16*)a.q + ((int64_t)c.qr * a.Hq + c.h) * DK;
+                #pragma unroll
+                for (int ks = 0; ks < S::KSTEPS; ++ks) {
+                    const int d0 = (ks / S::SPL) * 4 * S::KE + j * S::KE + (ks % S::SPL) * 8;
+                    lds_dma16(qrow + d0, qbuf + 1024 * (k * S::KSTEPS + ks));
+                }
             }
         }
     };
@@ -834,47 +851,60 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     int32_t id_nx = nx.seg < a.B ? page_id(nx) : 0;  // tile nx's page id, turned into its slot in the step
     if constexpr (EARLY) prep_new_token(nx, nt);
     Rows crow = rows_of(cur.seg);  // query rows of cur's request
-    Col col = column(cur, crow);
+    Col col[CB];
+    #pragma unroll
+    for (int k = 0; k < CB; ++k) col[k] = column(cur, crow, k);
     // The Q^T operand of the unit: held in registers from its first tile on
     // (128-wide keys and less), or read from the LDS buffer at every tile
     // (192-wide keys: six k-steps would take 24 more registers and push the
     // kernel into spills).  Either way the reads of the buffer are done
     // before the next unit's queries are loaded into it, which happens after
-    // the scores of the unit's last tile.
-    constexpr bool QLDS = DK > 128;
+    // the scores of the unit's last tile.  Two column blocks per wave read
+    // both from LDS (two register sets would spill).
+    constexpr bool QLDS = DK > 128 || CB > 1;
     bf16x8_t qreg[QLDS ? 1 : S::KSTEPS];
-    auto q_lds = [&](int ks) {
-        const u32x4_t v = *(lds_u32x4_t*)(qbuf + 1024 * ks + 16 * lane);
-        return as_bf16x8(col.ok ? v : u32x4_t{0u, 0u, 0u, 0u});
+    auto q_lds = [&](int k, int ks) {
+        const u32x4_t v = *(lds_u32x4_t*)(qbuf + 1024 * (k * S::KSTEPS + ks) + 16 * lane);
+        return as_bf16x8(col[k].ok ? v : u32x4_t{0u, 0u, 0u, 0u});
     };
-    auto qop = [&](int ks) {
-        if constexpr (QLDS) return q_lds(ks);
+    auto qop = [&](int k, int ks) {
+        if constexpr (QLDS) return q_lds(k, ks);
         else return qreg[ks];
     };
     auto take_q = [&]() {
         if constexpr (!QLDS) {
             #pragma unroll
-            for (int ks = 0; ks < S::KSTEPS; ++ks) qreg[ks] = q_lds(ks);
+            for (int ks = 0; ks < S::KSTEPS; ++ks) qreg[ks] = q_lds(0, ks);
             // the reads are done before a later direct load refills the buffer
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
             asm volatile("" ::: "memory");
         }
     };
-    f32x4_t O[S::CPL];
-    #pragma unroll
-    for (int cc = 0; cc < S::CPL; ++cc) O[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m2 = -INFINITY, lsum = 0.f;
+    f32x4_t O[CB][S::CPL];
+    float m2[CB], lsum[CB];
+    auto reset = [&]() {
+        #pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            #pragma unroll
+            for (int cc = 0; cc < S::CPL; ++cc) O[k][cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            m2[k] = -INFINITY;
+            lsum[k] = 0.f;
+        }
+    };
+    reset();
 
-    // finish a unit: denominator over the four lane groups of each column; a
-    // column with no key in this piece leaves weight 0 (lse -inf, o 0)
-    auto finish = [&](const It& u) {
-        const float ltot = wave_sum_xor_16_32(lsum);
+    // finish a unit's column block k: denominator over the four lane groups
+    // of each column; a column with no key in this piece leaves weight 0
+    // (lse -inf, o 0)
+    auto finish_block = [&](const It& u, int k) {
+        const Col& c = col[k];
+        const float ltot = wave_sum_xor_16_32(lsum[k]);
         const float inv = MQ && !(ltot > 0.f) ? 0.f : 1.0f / ltot;
-        const float lse_nat = MQ && !(ltot > 0.f) ? -INFINITY : (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
-        if (!col.ok) return;
+        const float lse_nat = MQ && !(ltot > 0.f) ? -INFINITY : (m2[k] + __builtin_amdgcn_logf(ltot)) * LN2;
+        if (!c.ok) return;
         if (u.lo == 0 && u.hi == crow.L) {
-            __bf16* orow = (__bf16*)a.out + ((int64_t)col.qr * a.Hq + col.h) * DV;
-            emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+            __bf16* orow = (__bf16*)a.out + ((int64_t)c.qr * a.Hq + c.h) * DV;
+            emit_rows<DV>(O[k], inv * a.v_scale, j, [&](const float* v, int d0) {
                 #pragma unroll
                 for (int i = 0; i < 4 * S::CPL; i += 8) {
                     const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
@@ -882,18 +912,22 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
                     *(u32x4_t*)(orow + d0 + i) = pk;
                 }
             });
-            if (a.lse && j == 0) a.lse[(int64_t)col.qr * a.Hq + col.h] = lse_nat;
+            if (a.lse && j == 0) a.lse[(int64_t)c.qr * a.Hq + c.h] = lse_nat;
         } else {
             // partial slot of (request, workgroup, query token)
-            const int64_t ps = ((int64_t)u.seg + w) * a.qslots + col.qi;
-            float* prow = a.ws_o + (ps * a.Hq + col.h) * DV;
-            emit_rows<DV>(O, inv * a.v_scale, j, [&](const float* v, int d0) {
+            const int64_t ps = ((int64_t)u.seg + w) * a.qslots + c.qi;
+            float* prow = a.ws_o + (ps * a.Hq + c.h) * DV;
+            emit_rows<DV>(O[k], inv * a.v_scale, j, [&](const float* v, int d0) {
                 #pragma unroll
                 for (int i = 0; i < 4 * S::CPL; i += 4)
                     *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
             });
-            if (j == 0) a.ws_lse[ps * a.Hq + col.h] = lse_nat;
+            if (j == 0) a.ws_lse[ps * a.Hq + c.h] = lse_nat;
         }
+    };
+    auto finish = [&](const It& u) {
+        #pragma unroll
+        for (int k = 0; k < CB; ++k) finish_block(u, k);
     };
 
     // One step: wait for tile `cur` (K in LDS, V in X); its scores; then,
@@ -917,8 +951,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
             __hip_atomic_store(prog + wv, nst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             other = __hip_atomic_load(prog + (wv ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        f32x4_t st[2];
-        tile_scores<DK, DV, FP8>(kst, qop, st, j);
+        f32x4_t st[CB][2];
+        tile_scores<DK, DV, FP8, CB>(kst, qop, st, j);
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the K reads are done ...
         asm volatile("" ::: "memory");       // ... before the direct loads refill the tile
         if (pair) {
@@ -943,16 +977,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         advance(nx, nn);
         const int32_t id_nn = nn.seg < a.B ? page_id(nn) : 0;
         if constexpr (EARLY) prep_new_token(nn, nt);
-        tile_update<DK, DV, FP8, MQ>(X, st, O, m2, lsum, col.kend - cur.t0, a.scale_log2, j);
+        #pragma unroll
+        for (int k = 0; k < CB; ++k)
+            tile_update<DK, DV, FP8, MQ>(X, st[k], O[k], m2[k], lsum[k], col[k].kend - cur.t0, a.scale_log2, j);
         if (cur.t0 + DEC_TILE >= cur.hi) {  // last tile of its unit
             finish(cur);
             if (nx.seg >= a.B) return false;
             if (nx.seg != cur.seg) crow = rows_of(nx.seg);
-            col = column(nx, crow);
             #pragma unroll
-            for (int cc = 0; cc < S::CPL; ++cc) O[cc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            m2 = -INFINITY;
-            lsum = 0.f;
+            for (int k = 0; k < CB; ++k) col[k] = column(nx, crow, k);
+            reset();
         }
         cur = nx;
         nx = nn;
@@ -1246,8 +1280,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(AttnArgs a, MetaArgs 
 // progress word each; with in-kernel metadata, the 8-byte aligned metadata
 // area of a batch of B requests after them.
 template <int DK, int DV, bool FP8>
-size_t decode_lds_bytes(int waves) {
-    return (size_t)waves * (DecodeShape<DK, DV, FP8>::WAVE_LDS + 4);
+size_t decode_lds_bytes(int waves, int cb = 1) {
+    return (size_t)waves * (decode_wave_lds<DK, DV, FP8>(cb) + 4);
 }
 template <int DK, int DV, bool FP8>
 size_t decode_md_lds_bytes(int waves, int32_t B) {
@@ -1279,14 +1313,19 @@ hipError_t launch_decode_d(pka_dtype q, pka_dtype kv, const AttnArgs& a, int wpb
     const dim3 grid((a.nwg + a.spw - 1) / a.spw, units / wpb);
     const dim3 block(64 * waves);
     const bool mq = a.qslots > 1;
+    // two column blocks per wave: several query rows, keys of at most 128
+    constexpr bool CB2 = DK <= 128;
+    const bool cb2 = CB2 && mq && a.cb == 2;
     const MetaArgs none{};
     if (kv == PKA_BF16) {
-        const size_t lds = decode_lds_bytes<DK, DV, false>(waves);
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true, false>), grid, block, lds, s, a, none);
+        const size_t lds = decode_lds_bytes<DK, DV, false>(waves, cb2 ? 2 : 1);
+        if (cb2) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true, false, CB2 ? 2 : 1>), grid, block, lds, s, a, none);
+        else if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, true, false>), grid, block, lds, s, a, none);
         else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, false, false, false>), grid, block, lds, s, a, none);
     } else if (kv == PKA_FP8_E4M3FN) {
-        const size_t lds = decode_lds_bytes<DK, DV, true>(waves);
-        if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true, false>), grid, block, lds, s, a, none);
+        const size_t lds = decode_lds_bytes<DK, DV, true>(waves, cb2 ? 2 : 1);
+        if (cb2) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true, false, CB2 ? 2 : 1>), grid, block, lds, s, a, none);
+        else if (mq) hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, true, false>), grid, block, lds, s, a, none);
         else hipLaunchKernelGGL((decode_mfma_kernel<DK, DV, true, false, false>), grid, block, lds, s, a, none);
     } else {
         if (mq) hipLaunchKernelGGL((decode_f32_kernel<DK, DV, true>), grid, block, 0, s, a);

@@ -169,6 +169,7 @@ struct AttnArgs {
     int32_t G;
     int32_t qgroups;  // ceil(G / 16): head groups per KV head
     int32_t csplit;   // decode waves per head group (MQ: they take its column passes in turn)
+    int32_t cb;       // decode column blocks of 16 per wave and pass (MQ: 1 or 2)
     int32_t page_shift;
     int32_t num_pages;
     int32_t nwg;       // decode shares (the partition's workgroup count)

@@ -72,15 +72,28 @@ def test_verify_on_decode_path(name, spec, mode):
 
 
 @pytest.mark.parametrize("name,spec", [
-    # 8 tokens x 4 heads = 32 columns: two waves per KV head take the passes
+    # 4 tokens x 4 heads = 16 columns: one 16-column block per wave
+    ("llama_n4_g4", BASE.replace(batch=64, new_len_args=(4, 4), prefix_len_args=(0, 600), seed=90)),
+    # 8 tokens x 4 heads = 32 columns: both blocks of one wave
     ("llama_n8_g4", BASE.replace(batch=64, new_len_args=(8, 8), prefix_len_args=(0, 600), seed=91)),
-    # 4 tokens x 16 heads = 64 columns: four waves per KV head, fp8 cache
+    # 4 tokens x 16 heads = 64 columns: two waves of two blocks per KV head, fp8 cache
     ("fp8_n4_g16", BASE.replace(batch=9, num_q_heads=64, num_kv_heads=4, page_size=64, kv_dtype="fp8",
                                 new_len_args=(4, 4), prefix_len_args=(0, 2000), seed=92)),
+    # 8 tokens x 8 heads = 64 columns: two waves of two blocks per KV head, bf16 cache
+    ("bf16_n8_g8", BASE.replace(batch=12, num_q_heads=64, num_kv_heads=8, page_size=16,
+                                new_len_args=(8, 8), prefix_len_args=(0, 1500), seed=93)),
+    # 16 tokens x 16 heads = 256 columns: four waves per KV head, each taking
+    # two 32-column passes over its tiles
+    ("bf16_n16_g16", BASE.replace(batch=5, num_q_heads=32, num_kv_heads=2, page_size=1,
+                                  new_len_args=(16, 16), prefix_len_args=(0, 1200), seed=94)),
+    # 64-wide heads, 8 tokens x 4 heads = 32 columns
+    ("bf16_d64_n8_g4", BASE.replace(batch=10, num_q_heads=16, num_kv_heads=4, head_dim=64, page_size=32,
+                                    new_len_args=(8, 8), prefix_len_args=(0, 900), seed=95)),
 ])
 def test_verify_column_passes_in_parallel_waves(name, spec):
-    """Uniform draft lengths whose columns need several 16-column passes:
-    the passes go to parallel waves of one workgroup."""
+    """Uniform draft lengths whose columns need one or several 16-column
+    blocks: a wave takes up to two adjacent blocks over one tile stream, and
+    further passes go to parallel waves of one workgroup."""
     prob, layout, values = _verify_problem(spec)
     _check(prob, layout, values, name)
 
