@@ -507,8 +507,10 @@ __device__ inline void md_write_batch(const MetaArgs& m, const MdWave& r, int64_
 typedef __attribute__((address_space(3))) const int32_t lds_i32_t;
 
 // MQ: several query tokens per request (speculative verify on the decode
-// path).  Columns are then (query token i, head h) pairs of the request, 16
-// per pass of the wave over its share; token i of a request with n query
+// path).  Columns are then (query token i, head h) pairs of the request, in
+// blocks of 16; a pass of the wave over its share takes CB adjacent blocks
+// (CB = 2: one K operand read and one set of V registers serve both, their
+// queries read from LDS at every tile); token i of a request with n query
 // tokens sits at position L - n + i and sees keys 0 .. L - n + i.  Partials
 // of token i go to slot (b + w) * qslots + i.
 //
@@ -536,9 +538,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     const int wpb = waves / a.spw;
     const int unit = blockIdx.y * wpb + wv % wpb;
     // unit = (KV head g, group of up to 16 of its query heads, column split
-    // ps): with MQ the csplit waves of one head group take its 16-column
-    // passes in turn (pass k goes to wave k % csplit), side by side in one
-    // workgroup, so they read the same tiles at the same time
+    // ps): with MQ the csplit waves of one head group take its passes of
+    // 16 * CB columns in turn (pass k goes to wave k % csplit), side by side
+    // in one workgroup, so they read the same tiles at the same time
     const int ps = unit % a.csplit, uh = unit / a.csplit;
     const int g = uh / a.qgroups;
     const int h0 = g * a.G + (uh % a.qgroups) * 16;
@@ -658,7 +660,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
     const int tok = lane & 31;  // tile token whose slot this lane looks up
 
     // The wave's work is one stream of 32-position tiles.  A unit is one
-    // 16-column pass over one piece (the part of a request inside this
+    // pass of 16 * CB columns over one piece (the part of a request inside this
     // wave's tile share); units follow each other in request order, and
     // the loads of a unit's first tile and its queries go out while the
     // previous unit's last tile is computed, so a request boundary costs no
