@@ -325,6 +325,7 @@ def bench_verify(spec, iters: int, warm: int = 10):
         ms = time_events(call, iters, warm=warm)
         out[path] = {"ms": round(ms, 4), "kv_read_GBps": round(kvb / ms / 1e6, 1),
                      "frac_hbm_peak": round(kvb / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    out["extend_path"]["variant"] = probs[0].ctx.describe("target_verify", layout.batch, layout.num_q_tokens)
     out["metadata_ms"] = round(time_events(lambda i: probs[i % 2].metadata_step(), iters, warm=warm), 4)
     for p in probs:
         assert p.md.status() == 0, "device status flags set"
@@ -344,6 +345,13 @@ def bench_verify_drafts(iters: int):
                         prefix_len_args=(512 - n_draft, 4096 - n_draft))
         out[f"n{n_draft}"] = bench_verify(vs, iters)
         log(f"verify, {n_draft} draft tokens: {out[f'n{n_draft}']}")
+    # a small batch (4 requests of 8,192 tokens, 8 drafts): too few extend
+    # items to fill the chip, so the extend path cuts their key ranges
+    vs = workloads.EXTRA["llama3_8b_verify"]
+    vs = vs.replace(name=vs.name.replace("_b64", "_b4").replace("_n4", "_n8"), batch=4, new_len_args=(8, 8),
+                    prefix_len_args=(8184, 8184))
+    out["small_b4_n8"] = bench_verify(vs, iters)
+    log(f"verify, 4 requests x 8 draft tokens: {out['small_b4_n8']}")
     return out
 
 

@@ -161,7 +161,12 @@ void pka_destroy(pka_ctx* ctx);
  * kernel's occupancy; the most the library allows, 2048 shares, if no
  * device can be queried) and up to min(16, max_q_per_request, num_q_tokens)
  * query rows per request for verify batches; it also covers any smaller
- * batch of the same mode on the same device. */
+ * batch of the same mode on the same device.  For an extend-like batch of
+ * bf16 queries with at most 16 rows per request on average, it also covers
+ * the extend path's key-range partials (pka_attn_extend): an fp32 row and
+ * an lse per (query row, query head, chunk), with C = min(8, 1024 /
+ * (batch * num_kv_heads)) chunks when C >= 3 (no split, and none of these
+ * bytes, otherwise). */
 pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t batch,
                            int32_t num_q_tokens, int64_t max_kv_pages, pka_sizes* out);
 
@@ -208,8 +213,13 @@ pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* forward_extend: each new token attends causally to its request's prefix and
- * to the new tokens up to itself.  Same buffers as decode (the workspace is
- * not used).  bf16 and fp8 e4m3fn caches run on MFMA (fp8 tiles are widened
+ * to the new tokens up to itself.  Same buffers as decode.  A batch of few
+ * rows per request has about one work item per request and KV head; when
+ * those are too few to fill the chip (the C >= 3 of pka_batch_sizes) and
+ * the workspace holds that many partials, each item's key range is cut into
+ * C chunks computed by workgroups of their own and merged by a second
+ * kernel (the same attention up to rounding); with a smaller workspace, or
+ * none, the batch runs unsplit.  bf16 and fp8 e4m3fn caches run on MFMA (fp8 tiles are widened
  * to bf16 exactly on their way into LDS; k_scale and v_scale are applied to
  * the scores and the output), fp32 on the vector ALUs.  bf16 queries cover
  * up to 128 query heads per KV head (checked by pka_create). */
@@ -257,7 +267,8 @@ pka_status pka_forward_with_metadata(const pka_ctx* ctx, pka_forward_mode mode,
 
 /* pka_forward_with_metadata without a workspace argument, for callers that
  * cannot allocate device memory (code under HIP graph capture, tight
- * serving loops, harnesses that forbid hipMalloc).  The decode path's split
+ * serving loops, harnesses that forbid hipMalloc).  The extend path runs
+ * without its key-range split here.  The decode path's split
  * partials go to a file-scope device array of PKA_NOALLOC_SCRATCH_BYTES that
  * every GPU the library runs on holds until the process ends (its address
  * is looked up on the first call on each device); nothing is allocated, and

@@ -163,6 +163,30 @@ pka_status batch_shares(const pka_ctx* ctx, const pka_batch* md, int32_t* nwg, i
     return s;
 }
 
+// Key-range chunks per extend item.  A batch of few query rows per request
+// (at most 16 on average: speculative verify, short continuations) has about
+// one item per request and KV head; when those are too few to fill the chip,
+// a long request's item would stream its keys alone while most workgroup
+// slots idle.  Its key range is then cut into chunks whose partials a merge
+// kernel combines: enough chunks for about EXT_SPLIT_WGS workgroups (two
+// rounds of two resident extend workgroups on each of 256 CUs), at most
+// EXT_MAX_SPLIT, and none below three (two chunks of a batch that nearly
+// fills the chip cost more in partials than they balance).  A function of
+// the batch sizes only, so the workspace and the launch agree.  bf16
+// queries (the MFMA kernel) only.
+constexpr int64_t EXT_SPLIT_WGS = 1024;
+int32_t ext_split(const pka_ctx* ctx, int32_t batch, int32_t num_q_tokens) {
+    if (ctx->cfg.q_dtype != PKA_BF16 || batch <= 0 || num_q_tokens <= 0) return 1;
+    if ((int64_t)num_q_tokens > 16LL * batch) return 1;
+    const int64_t c = EXT_SPLIT_WGS / ((int64_t)batch * ctx->cfg.num_kv_heads);
+    return c < 3 ? 1 : (int32_t)std::min<int64_t>(c, pka::EXT_MAX_SPLIT);
+}
+// Workspace of a split extend call: fp32 partial rows + lse per (query row,
+// head, chunk).
+int64_t ext_ws_bytes(const pka_ctx* ctx, int32_t num_q_tokens, int32_t C) {
+    return C > 1 ? (int64_t)num_q_tokens * ctx->cfg.num_q_heads * C * (ctx->dv + 1) * 4 : 0;
+}
+
 int64_t decode_ws_bytes(const pka_ctx* ctx, int32_t B, int32_t nwg, int32_t qslots) {
     return ((int64_t)B + nwg) * qslots * ctx->cfg.num_q_heads * (ctx->dv + 1) * 4;
 }
@@ -213,6 +237,7 @@ pka::AttnArgs attn_args(const pka_ctx* ctx, const pka_batch* md, const void* q, 
     a.spw = 1;
     a.csplit = 1;
     a.cb = 1;
+    a.ext_split = 1;
     const float k_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.k_scale : 1.0f;
     a.scale_log2 = c.scale * 1.4426950408889634f * k_scale;
     a.v_scale = c.kv_dtype == PKA_FP8_E4M3FN ? c.v_scale : 1.0f;
@@ -469,12 +494,18 @@ pka_status pka_describe(const pka_ctx* ctx, pka_forward_mode mode, pka_spec_attn
             const bool big = c.page_size >= 64;
             const int64_t row = (int64_t)c.num_kv_heads * std::max(ctx->dk, ctx->dv) * (int64_t)elem_bytes(c.kv_dtype);
             const bool wide = !big && (int64_t)c.num_pages * c.page_size * row > (int64_t)UINT32_MAX;
+            const int32_t C = ext_split(ctx, batch, num_q_tokens);
+            char split[160] = "";
+            if (C > 1)
+                snprintf(split, sizeof split,
+                         ", key range cut into %d chunks per item (with a workspace of pka_batch_sizes' size), "
+                         "then extend_split_merge_kernel<Dv %d>", C, ctx->dv);
             snprintf(tmp, sizeof tmp,
                      "path extend: extend_mfma_kernel<Dk %d, Dv %d, scale %s 0, %s, %s cache>, %d query tokens "
-                     "x %d heads per workgroup item, 64-key tiles",
+                     "x %d heads per workgroup item, 64-key tiles%s",
                      ctx->dk, ctx->dv, c.scale > 0.f ? ">" : "<=",
                      big ? "one page per key tile" : (wide ? "per-row slots, 64-bit addresses" : "per-row slots"),
-                     dtype_name(c.kv_dtype), ctx->ext_tq, ctx->G);
+                     dtype_name(c.kv_dtype), ctx->ext_tq, ctx->G, split);
         }
         d = tmp;
         if (with_metadata) d = "md_scan_kernel, then " + d;
@@ -574,17 +605,21 @@ pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t ba
     out->qo_indptr = (int64_t)batch + 1;
     out->out_cache_loc = std::max<int32_t>(num_q_tokens, 1);
     out->plan = pka::plan_elems(batch, num_q_tokens, ctx->ext_tq);
-    // split partials: only the decode path uses the workspace (a verify batch
-    // may be routed to it by the speculative-attention dispatch).  One
-    // resident round of the device's decode launch (without a column split:
-    // the most shares any batch of this mode can use), else the library's
-    // bound when no device answers.
+    // split partials.  Decode path (a verify batch may be routed to it by
+    // the speculative-attention dispatch): one resident round of the
+    // device's decode launch (without a column split: the most shares any
+    // batch of this mode can use), else the library's bound when no device
+    // answers.  Extend path: the key-range chunks of a batch of few rows per
+    // request.
     out->workspace_bytes = 0;
     if (mode != PKA_MODE_EXTEND && mode != PKA_MODE_IDLE) {
         int32_t nwg = 0;
         if (decode_wgs(ctx, &nwg) != PKA_OK) nwg = pka::DEC_MAX_WG;
         out->workspace_bytes = decode_ws_bytes(ctx, batch, nwg, decode_qslots(ctx, mode, num_q_tokens));
     }
+    if (mode != PKA_MODE_DECODE && mode != PKA_MODE_IDLE)
+        out->workspace_bytes = std::max<int64_t>(
+            out->workspace_bytes, ext_ws_bytes(ctx, num_q_tokens, ext_split(ctx, batch, num_q_tokens)));
     return PKA_OK;
 }
 
@@ -639,13 +674,22 @@ pka_status pka_attn_decode(const pka_ctx* ctx, const pka_batch* md, const void* 
 
 pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* q,
                            const void* k_pool, const void* v_pool, void* out, float* lse,
-                           void* /*workspace*/, size_t /*workspace_bytes*/, void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream) {
     pka_status s = check_attn(ctx, md, q, k_pool, v_pool, out);
     if (s != PKA_OK) return s;
     if (md->mode == PKA_MODE_IDLE || md->batch == 0 || md->num_q_tokens == 0) return PKA_OK;
     if (!is_extend_like(md->mode))
         return fail(PKA_ERR_INVALID_ARG, "metadata was built for a decode batch; extend needs extend metadata");
     pka::AttnArgs a = attn_args(ctx, md, q, k_pool, v_pool, out, lse);
+    // a batch of few rows per request splits its key ranges when the
+    // workspace holds the partials (else it runs unsplit)
+    const int32_t C = ext_split(ctx, md->batch, md->num_q_tokens);
+    if (C > 1 && workspace && aligned16(workspace) &&
+        (int64_t)workspace_bytes >= ext_ws_bytes(ctx, md->num_q_tokens, C)) {
+        a.ext_split = C;
+        a.ws_o = (float*)workspace;
+        a.ws_lse = a.ws_o + (int64_t)md->num_q_tokens * ctx->cfg.num_q_heads * C * ctx->dv;
+    }
     hipError_t e = pka::launch_extend(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
                                       (hipStream_t)stream);
     return e == hipSuccess ? PKA_OK : hip_fail(e, "extend launch");

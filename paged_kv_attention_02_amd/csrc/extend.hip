@@ -33,6 +33,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -181,11 +182,14 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     // the items of one KV head (same K/V pages) share one XCD's L2.
     const int32_t* plan = a.plan;
     // XCD x receives grid/8 workgroups, plus one when x < grid % 8.
-    const int32_t cap = gridDim.x / a.Hkv;  // item slots per KV head
+    // With a key-range split (a.ext_split = C > 1) each item has C
+    // consecutive workgroups, one per chunk of its key tiles.
+    const int32_t C = a.ext_split;
+    const int32_t cap = gridDim.x / (a.Hkv * C);  // item slots per KV head
     const int32_t xcd = blockIdx.x % EXT_XCDS;
     const int32_t base = gridDim.x / EXT_XCDS, extra = gridDim.x % EXT_XCDS;
     const int32_t w = xcd * base + min(xcd, extra) + blockIdx.x / EXT_XCDS;
-    const int32_t g = w / cap, item = w % cap;
+    const int32_t g = w / (cap * C), item = (w % (cap * C)) / C, chunk = w % C;
     if (item >= plan[PLAN_EXT_COUNT]) return;
     const int32_t TQ = plan[PLAN_EXT_TQ];
     const int32_t* items = plan + plan_ext_items(a.B);
@@ -221,7 +225,31 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     }
 
     const int32_t kend = pb + tok_hi;  // keys 0 .. kend-1
-    const int32_t ntiles = (kend + BN - 1) / BN;
+    // This workgroup's key tiles: all of the item's, or with a split, chunk
+    // `chunk` of them.  A chunk may start only at a tile whose first key is
+    // at or below the item's first query position, so every column has a
+    // visible key in every chunk; the last non-empty chunk runs to the end.
+    int32_t t_lo = 0, ntiles = (kend + BN - 1) / BN;
+    if (C > 1) {
+        const int32_t nstart = min(ntiles, qpos_min / BN + 1);  // tiles a chunk may start at
+        const int32_t per = (nstart + C - 1) / C;
+        t_lo = chunk * per;
+        if (t_lo >= nstart) {
+            // empty chunk: a zero-weight partial (lse -inf, o 0)
+            if (col_ok) {
+                const int64_t pi = ((int64_t)(q0 + ctok) * a.Hq + head) * C + chunk;
+                #pragma unroll
+                for (int c = 0; c < VC; ++c)
+                    #pragma unroll
+                    for (int r = 0; r < 16; r += 4)
+                        *(f32x4_t*)(a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (hh == 0) a.ws_lse[pi] = -INFINITY;
+            }
+            return;
+        }
+        ntiles = ((chunk + 1) * per < nstart ? (chunk + 1) * per : ntiles) - t_lo;
+    }
+    const int32_t kb0 = t_lo * BN;  // key position of this workgroup's first tile
     constexpr int ESZ = FP8 ? 1 : 2;  // cache bytes per element
     const int32_t krow = a.Hkv * DK * ESZ, vrow = a.Hkv * DV * ESZ;  // bytes of one pool slot
     const uint8_t* kbase = (const uint8_t*)a.k_pool + (int64_t)g * DK * ESZ;
@@ -407,22 +435,22 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     int32_t rawK[MK::NR], kpK[MK::NR], slotK[MK::NR];
     int32_t rawV[MV::NR], kpV[MV::NR], slotV[MV::NR];
     if constexpr (BIGPAGE) {
-        const int32_t p0 = page_of_tile(0);
-        dma_big(K_{}, p0, 0, sK0);
-        dma_big(V_{}, p0, 0, sV0);
+        const int32_t p0 = page_of_tile(kb0);
+        dma_big(K_{}, p0, kb0, sK0);
+        dma_big(V_{}, p0, kb0, sV0);
         if constexpr (FP8) {
             f8_finish(K_{}, sK0);
             f8_finish(V_{}, sV0);
         }
         if (ntiles > 1) {
-            const int32_t p1 = page_of_tile(BN);
-            dma_big(K_{}, p1, BN, sK1);
+            const int32_t p1 = page_of_tile(kb0 + BN);
+            dma_big(K_{}, p1, kb0 + BN, sK1);
             if constexpr (FP8) f8_finish(K_{}, sK1);
             pgV = p1;
         }
-        if (ntiles > 2) pgK = page_of_tile(2 * BN);
+        if (ntiles > 2) pgK = page_of_tile(kb0 + 2 * BN);
     } else if constexpr (SAME) {
-        lookup(K_{}, 0, rawK, kpK);
+        lookup(K_{}, kb0, rawK, kpK);
         form_slots(K_{}, rawK, kpK, slotK);
         dma_small(K_{}, slotK, sK0);
         dma_small(V_{}, slotK, sV0);
@@ -430,18 +458,18 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
             f8_finish(K_{}, sK0);
             f8_finish(V_{}, sV0);
         }
-        lookup(K_{}, BN, rawK, kpK);
+        lookup(K_{}, kb0 + BN, rawK, kpK);
         form_slots(K_{}, rawK, kpK, slotV);
         if (ntiles > 1) {
             dma_small(K_{}, slotV, sK1);
             if constexpr (FP8) f8_finish(K_{}, sK1);
         }
-        lookup(K_{}, 2 * BN, rawK, kpK);
+        lookup(K_{}, kb0 + 2 * BN, rawK, kpK);
     } else {
-        lookup(K_{}, 0, rawK, kpK);
+        lookup(K_{}, kb0, rawK, kpK);
         form_slots(K_{}, rawK, kpK, slotK);
         dma_small(K_{}, slotK, sK0);
-        lookup(V_{}, 0, rawV, kpV);
+        lookup(V_{}, kb0, rawV, kpV);
         form_slots(V_{}, rawV, kpV, slotV);
         dma_small(V_{}, slotV, sV0);
         if constexpr (FP8) {
@@ -449,13 +477,13 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
             f8_finish(V_{}, sV0);
         }
         if (ntiles > 1) {
-            lookup(K_{}, BN, rawK, kpK);
+            lookup(K_{}, kb0 + BN, rawK, kpK);
             form_slots(K_{}, rawK, kpK, slotK);
             dma_small(K_{}, slotK, sK1);
             if constexpr (FP8) f8_finish(K_{}, sK1);
         }
-        lookup(V_{}, BN, rawV, kpV);
-        lookup(K_{}, 2 * BN, rawK, kpK);
+        lookup(V_{}, kb0 + BN, rawV, kpV);
+        lookup(K_{}, kb0 + 2 * BN, rawK, kpK);
     }
     if constexpr (!FP8) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the direct loads landed
     __syncthreads();
@@ -469,7 +497,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         const uint8_t* knext = ODD ? sK0 : sK1; // K(t+1)
         uint8_t* kdst = ODD ? sK1 : sK0;        // K(t+2)
         uint8_t* vdst = ODD ? sV0 : sV1;        // V(t+1)
-        const int32_t kt0 = t * BN;
+        const int32_t kt0 = kb0 + t * BN;
 
         // bf16: K(t+1), V(t) and the lookups have landed (fp8 tiles were
         // written to LDS at the end of the previous iteration)
@@ -597,6 +625,19 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const float ltot = sum_halves(lsum);
     if (!col_ok) return;
     const float inv = a.v_scale / ltot;  // v_scale: fp8 V dequantisation (1 otherwise)
+    if (C > 1) {
+        // a chunk's partial: normalised fp32 output and natural-log lse,
+        // slot (row, head, chunk), for the split merge
+        const int64_t pi = ((int64_t)(q0 + ctok) * a.Hq + head) * C + chunk;
+        #pragma unroll
+        for (int c = 0; c < VC; ++c)
+            #pragma unroll
+            for (int r = 0; r < 16; r += 4)
+                *(f32x4_t*)(a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) =
+                    f32x4_t{O[c][r] * inv, O[c][r + 1] * inv, O[c][r + 2] * inv, O[c][r + 3] * inv};
+        if (hh == 0) a.ws_lse[pi] = (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
+        return;
+    }
     __bf16* orow = (__bf16*)a.out + ((int64_t)(q0 + ctok) * a.Hq + head) * DV;
     #pragma unroll
     for (int c = 0; c < VC; ++c)
@@ -674,6 +715,47 @@ int extend_max_group(pka_dtype q, int /*page_size*/) {
 }
 
 namespace {
+// Merge of a key-range split: each (query row, head) of the batch has C
+// partials (normalised output, natural-log lse; a chunk with no key leaves
+// lse -inf); out = sum_c e^(lse_c - M) o_c / sum_c e^(lse_c - M), lse = M +
+// ln(sum_c e^(lse_c - M)).  One wave per (row, head), lanes over the value
+// dims; chunk 0 always holds keys, so M is finite.
+template <int DV>
+__global__ __launch_bounds__(256) void extend_split_merge_kernel(AttnArgs a) {
+    constexpr int EPL = DV / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t pair = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int32_t rows = min(a.qo_indptr[a.B], a.N);  // the batch's query rows
+    if (pair >= (int64_t)rows * a.Hq) return;
+    const int32_t C = a.ext_split;
+    const float lv = lane < C ? a.ws_lse[pair * C + lane] : -INFINITY;
+    float v[EXT_MAX_SPLIT][EPL];
+    #pragma unroll
+    for (int c = 0; c < EXT_MAX_SPLIT; ++c)
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            v[c][e] = c < C ? a.ws_o[(pair * C + c) * DV + e * 64 + lane] : 0.f;
+    float M = lv;
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float wk = lane < C ? expf(lv - M) : 0.f;
+    float den = wk, acc[EPL];
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    #pragma unroll
+    for (int c = 0; c < EXT_MAX_SPLIT; ++c) {
+        const float wt = __shfl(wk, c);
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += wt * v[c][e];
+    }
+    #pragma unroll
+    for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+    const float inv = 1.0f / den;
+    #pragma unroll
+    for (int e = 0; e < EPL; ++e) ((__bf16*)a.out)[pair * DV + e * 64 + lane] = (__bf16)(acc[e] * inv);
+    if (a.lse && lane == 0) a.lse[pair] = M + logf(den);
+}
+
 // One launch of the MFMA kernel for a (widths, scale sign, page path, cache
 // dtype) combination; the fp8 path moves tiles through registers and has no
 // 64-bit gather variant.
@@ -712,8 +794,10 @@ hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnAr
         else return hipErrorInvalidValue;
         return hipGetLastError();
     }
-    if (items * a.Hkv * 64 * EXT_WAVES > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(items * a.Hkv));
+    const int C = a.ext_split;
+    if (C < 1 || C > EXT_MAX_SPLIT) return hipErrorInvalidValue;
+    if (items * a.Hkv * C * 64 * EXT_WAVES > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)(items * a.Hkv * C));
     const bool pos = a.scale_log2 > 0.f;
     const bool big = P >= BN;
     // pages under 64 tokens gather rows by slot: 32-bit offsets while every
@@ -725,6 +809,12 @@ hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnAr
     else if (DK == 64 && DV == 64) launch_ext_d<64, 64>(a, pos, big, wide, f8, grid, s);
     else if (DK == 192 && DV == 128) launch_ext_d<192, 128>(a, pos, big, wide, f8, grid, s);
     else return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || C == 1) return e;
+    const int64_t pairs = (int64_t)a.N * a.Hq;  // waves: one per (query row, head)
+    const dim3 mgrid((unsigned)((pairs + 3) / 4));
+    if (DV == 128) hipLaunchKernelGGL((extend_split_merge_kernel<128>), mgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((extend_split_merge_kernel<64>), mgrid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -54,6 +54,8 @@ constexpr int DEC_MAX_WG = 2048;
 constexpr int DEC_MAX_Q = 16;
 // Most waves that share one head group's column passes (speculative verify).
 constexpr int DEC_MAX_CSPLIT = 4;
+// Most key-range chunks per extend item (batches of few query rows per request).
+constexpr int EXT_MAX_SPLIT = 8;
 
 // plan offsets that depend on the batch size: the token prefix F[b] = sum of
 // L over requests before b, the tile prefix T[b] = sum of ceil(L / DEC_TILE)
@@ -170,6 +172,7 @@ struct AttnArgs {
     int32_t qgroups;  // ceil(G / 16): head groups per KV head
     int32_t csplit;   // decode waves per head group (MQ: they take its column passes in turn)
     int32_t cb;       // decode column blocks of 16 per wave and pass (MQ: 1 or 2)
+    int32_t ext_split;  // extend: key-range chunks per item (1: none; partials in ws_o / ws_lse)
     int32_t page_shift;
     int32_t num_pages;
     int32_t nwg;       // decode shares (the partition's workgroup count)

@@ -241,3 +241,20 @@ def test_noalloc_refuses_before_any_launch():
     assert pka.NOALLOC_SCRATCH_BYTES == 64 << 20
     text = open(os.path.join(ROOT, "include", "pka.h")).read()
     assert "#define PKA_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+
+
+def test_extend_workspace_covers_the_key_range_split():
+    """pka_batch_sizes reports the extend split's partials (fp32 row + lse per
+    query row, head and chunk) for batches of at most 16 rows per request on
+    average, and none for longer extend batches; describe names the split."""
+    ctx = pka.Context(32, 8, 128, 16, 1000)
+    # chunks: about 1024 workgroups over the batch's items (one per request
+    # and KV head), 3 .. 8, else none
+    for batch, n, chunks in [(64, 256, 1), (42, 168, 3), (32, 128, 4), (12, 60, 8), (1, 4, 8), (100, 400, 1)]:
+        need = n * 32 * chunks * (128 + 1) * 4 if chunks > 1 else 0
+        assert ctx.sizes("extend", batch, n, 9000).workspace_bytes == need, (batch, n)
+        assert ctx.sizes("target_verify", batch, n, 9000).workspace_bytes >= need
+        assert ("%d chunks per item" % chunks in ctx.describe("target_verify", batch, n)) == (chunks > 1)
+    assert ctx.sizes("extend", 4, 100, 40).workspace_bytes == 0  # 25 rows per request: no split
+    assert "chunks per item" not in ctx.describe("extend", 4, 100)
+    assert "chunks per item" not in pka.Context(4, 2, 64, 1, 100, "f32", "f32").describe("extend", 8, 16)
