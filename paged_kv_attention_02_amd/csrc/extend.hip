@@ -559,12 +559,13 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
             for (int c = 0; c < VC; ++c) O[c] *= alpha;
         }
 
-        // The compiler's interleaving strategy 0 for MFMA-heavy regions
-        // orders this block's MFMAs, operand reads and vector work: about
-        // +2% over a bf16 cache at equal widths (A/B on one box); it cost 3%
-        // over an fp8 cache (whose tile conversions share the block's
-        // iteration) and 4.5% at 192/128 (next scores after the block).
-        if constexpr (!SPLITQK && !FP8) __builtin_amdgcn_iglp_opt(0);
+        // The compiler's interleaving strategies for MFMA-heavy regions
+        // order this block's MFMAs, operand reads and vector work: strategy
+        // 0 over a bf16 cache and 3 over an fp8 cache (whose tile
+        // conversions share the iteration) each gain 2-3% at equal widths
+        // (A/B in one process; 0 cost 3% over fp8); at 192/128 (next scores
+        // after the block) every strategy tried cost 2-6%.
+        if constexpr (!SPLITQK) __builtin_amdgcn_iglp_opt(FP8 ? 3 : 0);
         // interleaved block: probabilities of S(t) (bf16; the normaliser sums
         // the same rounded values), O^T += V^T . P^T over tile t, and the
         // scores of tile t+1.  A column has a valid key in every tile up to
