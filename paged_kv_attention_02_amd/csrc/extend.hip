@@ -562,10 +562,11 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         // The compiler's interleaving strategies for MFMA-heavy regions
         // order this block's MFMAs, operand reads and vector work: strategy
         // 0 over a bf16 cache and 3 over an fp8 cache (whose tile
-        // conversions share the iteration) each gain 2-3% at equal widths
-        // (A/B in one process; 0 cost 3% over fp8); at 192/128 (next scores
-        // after the block) every strategy tried cost 2-6%.
+        // conversions share the iteration) each gain 2-3% at equal widths,
+        // and 3 gains 1-3% at 192/128 over a bf16 cache (A/B in one process;
+        // 0 cost 3% over fp8 and 2-5% at 192/128).
         if constexpr (!SPLITQK) __builtin_amdgcn_iglp_opt(FP8 ? 3 : 0);
+        else if constexpr (!FP8) __builtin_amdgcn_iglp_opt(3);
         // interleaved block: probabilities of S(t) (bf16; the normaliser sums
         // the same rounded values), O^T += V^T . P^T over tile t, and the
         // scores of tile t+1.  A column has a valid key in every tile up to
