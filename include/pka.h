@@ -156,8 +156,9 @@ void pka_destroy(pka_ctx* ctx);
 
 /* Sizes for a batch of `batch` requests, `num_q_tokens` new tokens and at
  * most `max_kv_pages` pages in total (sum of ceil(L_b / page_size)).  The
- * decode workspace holds fp32 partial rows for one resident round of the
- * decode launch on the current device (its compute units times the
+ * decode workspace holds partial rows in the output's type (bf16 rows for
+ * bf16 queries, fp32 for fp32), each with an fp32 log-sum-exp, for one
+ * resident round of the decode launch on the current device (its compute units times the
  * kernel's occupancy; the most the library allows, 2048 shares, if no
  * device can be queried) and up to min(16, max_q_per_request, num_q_tokens)
  * query rows per request for verify batches; it also covers any smaller

@@ -187,8 +187,12 @@ int64_t ext_ws_bytes(const pka_ctx* ctx, int32_t num_q_tokens, int32_t C) {
     return C > 1 ? (int64_t)num_q_tokens * ctx->cfg.num_q_heads * C * (ctx->dv + 1) * 4 : 0;
 }
 
+// Workspace of a decode call: a partial row in the output's type (bf16 or
+// fp32, that of the queries) and an fp32 lse per (request or share, query
+// slot, head).
 int64_t decode_ws_bytes(const pka_ctx* ctx, int32_t B, int32_t nwg, int32_t qslots) {
-    return ((int64_t)B + nwg) * qslots * ctx->cfg.num_q_heads * (ctx->dv + 1) * 4;
+    const int64_t row = (int64_t)ctx->dv * elem_bytes(ctx->cfg.q_dtype) + 4;
+    return ((int64_t)B + nwg) * qslots * ctx->cfg.num_q_heads * row;
 }
 
 pka_status check_batch(const pka_ctx* ctx, const pka_batch* md) {
@@ -289,8 +293,9 @@ pka_status decode_args(const pka_ctx* ctx, const pka_batch* md, const void* q, c
     a.nwg = nwg;
     a.spw = sp;
     a.qslots = qslots;
-    a.ws_o = (float*)workspace;
-    a.ws_lse = a.ws_o + ((int64_t)md->batch + nwg) * qslots * ctx->cfg.num_q_heads * ctx->dv;
+    a.ws_o = workspace;
+    a.ws_lse = (float*)((uint8_t*)workspace + ((int64_t)md->batch + nwg) * qslots * ctx->cfg.num_q_heads *
+                                                  ctx->dv * (int64_t)elem_bytes(ctx->cfg.q_dtype));
     if (write_new) {
         const pka_config& c = ctx->cfg;
         a.k_new = k_new;
@@ -687,8 +692,8 @@ pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* 
     if (C > 1 && workspace && aligned16(workspace) &&
         (int64_t)workspace_bytes >= ext_ws_bytes(ctx, md->num_q_tokens, C)) {
         a.ext_split = C;
-        a.ws_o = (float*)workspace;
-        a.ws_lse = a.ws_o + (int64_t)md->num_q_tokens * ctx->cfg.num_q_heads * C * ctx->dv;
+        a.ws_o = workspace;
+        a.ws_lse = (float*)workspace + (int64_t)md->num_q_tokens * ctx->cfg.num_q_heads * C * ctx->dv;
     }
     hipError_t e = pka::launch_extend(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
                                       (hipStream_t)stream);

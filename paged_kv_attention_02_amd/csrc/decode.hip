@@ -904,27 +904,24 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(AttnArgs a, MetaArgs m
         const float inv = MQ && !(ltot > 0.f) ? 0.f : 1.0f / ltot;
         const float lse_nat = MQ && !(ltot > 0.f) ? -INFINITY : (m2[k] + __builtin_amdgcn_logf(ltot)) * LN2;
         if (!c.ok) return;
-        if (u.lo == 0 && u.hi == crow.L) {
-            __bf16* orow = (__bf16*)a.out + ((int64_t)c.qr * a.Hq + c.h) * DV;
-            emit_rows<DV>(O[k], inv * a.v_scale, j, [&](const float* v, int d0) {
-                #pragma unroll
-                for (int i = 0; i < 4 * S::CPL; i += 8) {
-                    const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
-                                        pack_bf16(v[i + 4], v[i + 5]), pack_bf16(v[i + 6], v[i + 7])};
-                    *(u32x4_t*)(orow + d0 + i) = pk;
-                }
-            });
-            if (a.lse && j == 0) a.lse[(int64_t)c.qr * a.Hq + c.h] = lse_nat;
-        } else {
-            // partial slot of (request, workgroup, query token)
-            const int64_t ps = ((int64_t)u.seg + w) * a.qslots + c.qi;
-            float* prow = a.ws_o + (ps * a.Hq + c.h) * DV;
-            emit_rows<DV>(O[k], inv * a.v_scale, j, [&](const float* v, int d0) {
-                #pragma unroll
-                for (int i = 0; i < 4 * S::CPL; i += 4)
-                    *(f32x4_t*)(prow + d0 + i) = f32x4_t{v[i], v[i + 1], v[i + 2], v[i + 3]};
-            });
-            if (j == 0) a.ws_lse[ps * a.Hq + c.h] = lse_nat;
+        // the output row when the piece is the whole request, else the
+        // partial row of (request, workgroup, query token); both bf16 (the
+        // merge weighs the partials in fp32), the lse in fp32
+        const bool whole = u.lo == 0 && u.hi == crow.L;
+        const int64_t ps = ((int64_t)u.seg + w) * a.qslots + c.qi;
+        __bf16* const orow = whole ? (__bf16*)a.out + ((int64_t)c.qr * a.Hq + c.h) * DV
+                                   : (__bf16*)a.ws_o + (ps * a.Hq + c.h) * DV;
+        emit_rows<DV>(O[k], inv * a.v_scale, j, [&](const float* v, int d0) {
+            #pragma unroll
+            for (int i = 0; i < 4 * S::CPL; i += 8) {
+                const u32x4_t pk = {pack_bf16(v[i], v[i + 1]), pack_bf16(v[i + 2], v[i + 3]),
+                                    pack_bf16(v[i + 4], v[i + 5]), pack_bf16(v[i + 6], v[i + 7])};
+                *(u32x4_t*)(orow + d0 + i) = pk;
+            }
+        });
+        if (j == 0) {
+            if (!whole) a.ws_lse[ps * a.Hq + c.h] = lse_nat;
+            else if (a.lse) a.lse[(int64_t)c.qr * a.Hq + c.h] = lse_nat;
         }
     };
     auto finish = [&](const It& u) {
@@ -1107,7 +1104,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
                     const int64_t ps = ((int64_t)b + w) * a.qslots + qi;
                     #pragma unroll
                     for (int e = 0; e < EPV; ++e)
-                        a.ws_o[(ps * a.Hq + h) * DV + e * 64 + lane] = o[cc][e] * inv;
+                        ((float*)a.ws_o)[(ps * a.Hq + h) * DV + e * 64 + lane] = o[cc][e] * inv;
                     if (lane == 0) a.ws_lse[ps * a.Hq + h] = lse_nat;
                 }
             }
@@ -1121,10 +1118,34 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(AttnArgs a) {
 // row; grid z = query rows): lanes first take one partial each (max and
 // normaliser by wave reductions), then lanes take head dims and sweep the
 // partials with several loads in flight.  D: the value (output) width.
+// Dims of a row that lane `lane` reads and writes in the merge: EPL
+// consecutive ones (lane * EPL + e) for bf16 rows, so a lane moves them in
+// one access; e * 64 + lane for fp32 rows.
+template <int EPL, bool BF>
+__device__ inline int merge_dim(int lane, int e) { return BF ? lane * EPL + e : e * 64 + lane; }
+// This lane's EPL values of one partial row, as fp32.
+template <int EPL, bool BF>
+__device__ inline void load_partial(const void* row, int lane, float (&v)[EPL]) {
+    if constexpr (BF && EPL == 2) {
+        const uint32_t w = ((const uint32_t*)row)[lane];
+        v[0] = __uint_as_float(w << 16);
+        v[1] = __uint_as_float(w & 0xffff0000u);
+    } else if constexpr (BF) {
+        static_assert(EPL == 1, "bf16 rows of 64 or 128 values");
+        v[0] = __uint_as_float((uint32_t)((const uint16_t*)row)[lane] << 16);
+    } else {
+        #pragma unroll
+        for (int e = 0; e < EPL; ++e) v[e] = ((const float*)row)[merge_dim<EPL, false>(lane, e)];
+    }
+}
+
 template <int D, bool OUT_BF16>
 __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
+    static_assert(D == 64 || D == 128, "value width");
     constexpr int EPL = D / 64;
     constexpr int UNROLL = 8;
+    // partial rows in the output's type
+    using PT = typename std::conditional<OUT_BF16, __bf16, float>::type;
     const int lane = threadIdx.x & 63;
     const int32_t h = blockIdx.y * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (h >= a.Hq) return;
@@ -1163,7 +1184,7 @@ __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
     if (qi >= nq) return;
     {
         const float* lse_col = a.ws_lse + ((int64_t)(b + w0) * a.qslots + qi) * a.Hq + h;
-        const float* o_col = a.ws_o + (((int64_t)(b + w0) * a.qslots + qi) * a.Hq + h) * D;
+        const PT* o_col = (const PT*)a.ws_o + (((int64_t)(b + w0) * a.qslots + qi) * a.Hq + h) * D;
 
         float M = -INFINITY;
         float den = 0.f, acc[EPL];
@@ -1175,11 +1196,8 @@ __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
             const float lv = lane < np ? lse_col[(int64_t)lane * lstride] : -INFINITY;
             float v[UNROLL][EPL];
             #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int32_t kk = min(u, np - 1);
-                #pragma unroll
-                for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)kk * ostride + e * 64 + lane];
-            }
+            for (int u = 0; u < UNROLL; ++u)
+                load_partial<EPL, OUT_BF16>(o_col + (int64_t)min(u, np - 1) * ostride, lane, v[u]);
             M = lv;
             #pragma unroll
             for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -1206,8 +1224,7 @@ __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
                     for (int u = 0; u < UNROLL; ++u) {
                         const int32_t kk = min(i + u, cnt - 1);
                         wt[u] = i + u < cnt ? __shfl(wk, kk) : 0.f;
-                        #pragma unroll
-                        for (int e = 0; e < EPL; ++e) v[u][e] = o_col[(int64_t)(k0 + kk) * ostride + e * 64 + lane];
+                        load_partial<EPL, OUT_BF16>(o_col + (int64_t)(k0 + kk) * ostride, lane, v[u]);
                     }
                     #pragma unroll
                     for (int u = 0; u < UNROLL; ++u)
@@ -1220,13 +1237,18 @@ __device__ inline void merge_column(const AttnArgs& a, int32_t b) {
         for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
         const float inv = 1.0f / den;
         const int32_t qr = q0 + qi;
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int64_t o = ((int64_t)qr * a.Hq + h) * D + e * 64 + lane;
-            if constexpr (OUT_BF16)
-                ((__bf16*)a.out)[o] = (__bf16)(acc[e] * inv);
-            else
-                ((float*)a.out)[o] = acc[e] * inv;
+        const int64_t orow = ((int64_t)qr * a.Hq + h) * D;
+        if constexpr (OUT_BF16 && EPL == 2) {
+            ((uint32_t*)((__bf16*)a.out + orow))[lane] = pack_bf16(acc[0] * inv, acc[1] * inv);
+        } else {
+            #pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+                const int64_t o = orow + merge_dim<EPL, OUT_BF16>(lane, e);
+                if constexpr (OUT_BF16)
+                    ((__bf16*)a.out)[o] = (__bf16)(acc[e] * inv);
+                else
+                    ((float*)a.out)[o] = acc[e] * inv;
+            }
         }
         if (a.lse && lane == 0) a.lse[(int64_t)qr * a.Hq + h] = M + logf(den);
     }

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 for (int c = 0; c < VC; ++c)
                     #pragma unroll
                     for (int r = 0; r < 16; r += 4)
-                        *(f32x4_t*)(a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        *(f32x4_t*)((float*)a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 if (hh == 0) a.ws_lse[pi] = -INFINITY;
             }
             return;
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 lds_dma16(src + (int64_t)slot[j] * rb + off[j], dst + (TT::LOADS * wave + j) * 1024);
         } else {
             // the pool from this head on fits in 32-bit offsets (checked at launch)
-            const auto rs = raw_buffer(src, (uint32_t)min(a.pool_slots * (int64_t)rb, (int64_t)UINT32_MAX));
+            const int64_t pool_bytes = a.pool_slots * (int64_t)rb;
+            const auto rs = raw_buffer(src, pool_bytes < (int64_t)UINT32_MAX ? (uint32_t)pool_bytes : UINT32_MAX);
             #pragma unroll
             for (int j = 0; j < M::NR; ++j)
                 lds_dma16_buf(rs, (uint32_t)slot[j] * (uint32_t)rb + off[j], dst + (TT::LOADS * wave + j) * 1024);
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         for (int c = 0; c < VC; ++c)
             #pragma unroll
             for (int r = 0; r < 16; r += 4)
-                *(f32x4_t*)(a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) =
+                *(f32x4_t*)((float*)a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) =
                     f32x4_t{O[c][r] * inv, O[c][r + 1] * inv, O[c][r + 2] * inv, O[c][r + 3] * inv};
         if (hh == 0) a.ws_lse[pi] = (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
         return;
@@ -742,7 +743,7 @@ __global__ __launch_bounds__(256) void extend_split_merge_kernel(AttnArgs a) {
     for (int c = 0; c < EXT_MAX_SPLIT; ++c)
         #pragma unroll
         for (int e = 0; e < EPL; ++e)
-            v[c][e] = c < C ? a.ws_o[(pair * C + c) * DV + e * 64 + lane] : 0.f;
+            v[c][e] = c < C ? ((const float*)a.ws_o)[(pair * C + c) * DV + e * 64 + lane] : 0.f;
     float M = lv;
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));

@@ -156,8 +156,11 @@ struct AttnArgs {
     const void* v_pool;
     void* out;
     float* lse;
-    float* ws_o;    // split partials [(B + nwg) * qslots, Hq, value width] fp32
-    float* ws_lse;  // [(B + nwg), Hq]
+    // decode split partials [(B + nwg) * qslots, Hq, value width] in the
+    // output's type (bf16 rows with bf16 queries, fp32 with fp32); extend
+    // key-range partials [N, Hq, chunks, value width] fp32
+    void* ws_o;
+    float* ws_lse;  // their log-sum-exps (natural log), one per row
     const int32_t* kv_indptr;
     const int32_t* kv_indices;
     const int32_t* kv_last_page_len;

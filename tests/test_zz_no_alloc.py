@@ -117,10 +117,12 @@ def test_noalloc_matches_workspace_entry_point(name):
 
 
 def test_noalloc_refuses_batches_beyond_the_scratch():
-    """16 query rows per request over 64-head groups need more partial rows
-    than the array holds: refused, nothing launched (outputs untouched)."""
-    spec = workloads.Spec("v", "extend", 64, 64, 4, 128, 16, "bf16", "bf16", seed=209,
-                          new_len_args=(16, 16), prefix_len_args=(1, 300))
+    """16 query rows per request of 96 requests over 32-head groups need more
+    partial rows than the array holds (the requests' own slots alone take
+    96 x 16 x 128 bf16 rows and lse, 51 MB, and every share adds 16 x 128):
+    refused, nothing launched (outputs untouched)."""
+    spec = workloads.Spec("v", "extend", 96, 128, 4, 128, 16, "bf16", "bf16", seed=209,
+                          new_len_args=(16, 16), prefix_len_args=(600, 1200))
     prob, layout, values = _problem(spec, "target_verify")
     need = prob.ctx.sizes("target_verify", layout.batch, layout.num_q_tokens, layout.kv_pages).workspace_bytes
     assert need > pka.NOALLOC_SCRATCH_BYTES
