@@ -565,7 +565,12 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         // 0 over a bf16 cache and 3 over an fp8 cache (whose tile
         // conversions share the iteration) each gain 2-3% at equal widths,
         // and 3 gains 1-3% at 192/128 over a bf16 cache (A/B in one process;
-        // 0 cost 3% over fp8 and 2-5% at 192/128).
+        // 0 cost 3% over fp8 and 2-5% at 192/128).  Over a bf16 cache the
+        // wave also raises its issue priority for the block, so that of the
+        // two waves sharing a SIMD the one feeding the matrix core issues
+        // first while the other runs its softmax prologue (+1-2%; over fp8,
+        // whose conversions follow the block, no gain).
+        if constexpr (!FP8) __builtin_amdgcn_s_setprio(1);
         if constexpr (!SPLITQK) __builtin_amdgcn_iglp_opt(FP8 ? 3 : 0);
         else if constexpr (!FP8) __builtin_amdgcn_iglp_opt(3);
         // interleaved block: probabilities of S(t) (bf16; the normaliser sums
@@ -608,6 +613,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
             #pragma unroll
             for (int q = 0; q < KSTEPS * SB; ++q) qk_mfma(knext, q, Sn);
         }
+        if constexpr (!FP8) __builtin_amdgcn_s_setprio(0);
         // fp8: the next tiles go into the stages this iteration did not read;
         // the next iteration's barrier publishes them
         if constexpr (FP8) {
