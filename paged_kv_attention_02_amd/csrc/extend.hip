@@ -429,7 +429,12 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     f32x16_t (&SB2)[SB] = second();
 
     // prologue: K(0), V(0), K(1) resident, S(0) computed
-    int32_t pgK = 0, pgV = 0;        // BIGPAGE: pages of tiles t+2 (K) and t+1 (V)
+    // BIGPAGE: page ids by tile parity.  At the top of iteration t, pgp[t & 1]
+    // holds the page of tile t+2 (its K goes out now) and pgp[~t & 1] that of
+    // tile t+1 (its V goes out now); that slot then takes tile t+3's id, which
+    // is first used an iteration later, so the lookup is never waited for
+    // where it is issued.
+    int32_t pgp[2] = {0, 0};
     // small pages.  Equal widths: V(t+1) reuses the slots K(t+1) was loaded
     // with.  Otherwise V's rows have lookups of their own, also an iteration
     // ahead (rawV holds the page ids of V(t+1) at the top of iteration t).
@@ -447,9 +452,9 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
             const int32_t p1 = page_of_tile(kb0 + BN);
             dma_big(K_{}, p1, kb0 + BN, sK1);
             if constexpr (FP8) f8_finish(K_{}, sK1);
-            pgV = p1;
+            pgp[1] = p1;
         }
-        if (ntiles > 2) pgK = page_of_tile(kb0 + 2 * BN);
+        if (ntiles > 2) pgp[0] = page_of_tile(kb0 + 2 * BN);
     } else if constexpr (SAME) {
         lookup(K_{}, kb0, rawK, kpK);
         form_slots(K_{}, rawK, kpK, slotK);
@@ -505,10 +510,10 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
         if constexpr (!FP8) __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();  // ... for every wave; iteration t-1 is done
         if constexpr (BIGPAGE) {
-            if (t + 2 < ntiles) dma_big(K_{}, pgK, kt0 + 2 * BN, kdst);
-            if (NEXT) dma_big(V_{}, pgV, kt0 + BN, vdst);
-            pgV = pgK;
-            if (t + 3 < ntiles) pgK = page_of_tile(kt0 + 3 * BN);
+            constexpr int PI = ODD ? 1 : 0;  // t & 1
+            if (t + 2 < ntiles) dma_big(K_{}, pgp[PI], kt0 + 2 * BN, kdst);
+            if (NEXT) dma_big(V_{}, pgp[1 - PI], kt0 + BN, vdst);
+            if (t + 3 < ntiles) pgp[1 - PI] = page_of_tile(kt0 + 3 * BN);
         } else if constexpr (SAME) {
             if (NEXT) dma_small(V_{}, slotV, vdst);
             if (t + 2 < ntiles) {
