@@ -6,8 +6,9 @@
 // flash decoding: the batch's 32-token tiles, laid end to end, are cut into
 // shares equal to within a tile, one or more per workgroup; each wave serves
 // one KV head (16 query heads of its group at most) over one share with an
-// online softmax, and a share that covers only part of a request leaves an
-// fp32 partial (output and log-sum-exp) that a merge kernel combines.
+// online softmax, and a share that covers only part of a request leaves a
+// partial (its normalised output row in the output's type and an fp32
+// log-sum-exp) that a merge kernel combines in fp32.
 //
 // gfx950 mapping of the MFMA variant (bf16 or fp8 e4m3fn cache):
 //   S^T[token, head]  = K[token, :] . Q^T        v_mfma_f32_16x16x32_bf16
