@@ -164,8 +164,8 @@ void pka_destroy(pka_ctx* ctx);
  * query rows per request for verify batches; it also covers any smaller
  * batch of the same mode on the same device.  For an extend-like batch of
  * bf16 queries with at most 16 rows per request on average, it also covers
- * the extend path's key-range partials (pka_attn_extend): an fp32 row and
- * an lse per (query row, query head, chunk), with C = min(8, 1024 /
+ * the extend path's key-range partials (pka_attn_extend): a bf16 row and
+ * an fp32 lse per (query row, query head, chunk), with C = min(8, 1024 /
  * (batch * num_kv_heads)) chunks when C >= 3 (no split, and none of these
  * bytes, otherwise). */
 pka_status pka_batch_sizes(const pka_ctx* ctx, pka_forward_mode mode, int32_t batch,

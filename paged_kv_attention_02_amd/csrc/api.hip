@@ -181,10 +181,10 @@ int32_t ext_split(const pka_ctx* ctx, int32_t batch, int32_t num_q_tokens) {
     const int64_t c = EXT_SPLIT_WGS / ((int64_t)batch * ctx->cfg.num_kv_heads);
     return c < 3 ? 1 : (int32_t)std::min<int64_t>(c, pka::EXT_MAX_SPLIT);
 }
-// Workspace of a split extend call: fp32 partial rows + lse per (query row,
-// head, chunk).
+// Workspace of a split extend call: a bf16 partial row and an fp32 lse per
+// (query row, head, chunk).
 int64_t ext_ws_bytes(const pka_ctx* ctx, int32_t num_q_tokens, int32_t C) {
-    return C > 1 ? (int64_t)num_q_tokens * ctx->cfg.num_q_heads * C * (ctx->dv + 1) * 4 : 0;
+    return C > 1 ? (int64_t)num_q_tokens * ctx->cfg.num_q_heads * C * ((int64_t)ctx->dv * 2 + 4) : 0;
 }
 
 // Workspace of a decode call: a partial row in the output's type (bf16 or
@@ -693,7 +693,7 @@ pka_status pka_attn_extend(const pka_ctx* ctx, const pka_batch* md, const void* 
         (int64_t)workspace_bytes >= ext_ws_bytes(ctx, md->num_q_tokens, C)) {
         a.ext_split = C;
         a.ws_o = workspace;
-        a.ws_lse = (float*)workspace + (int64_t)md->num_q_tokens * ctx->cfg.num_q_heads * C * ctx->dv;
+        a.ws_lse = (float*)((uint8_t*)workspace + (int64_t)md->num_q_tokens * ctx->cfg.num_q_heads * C * ctx->dv * 2);
     }
     hipError_t e = pka::launch_extend(ctx->cfg.q_dtype, ctx->cfg.kv_dtype, ctx->dk, ctx->dv, a,
                                       (hipStream_t)stream);

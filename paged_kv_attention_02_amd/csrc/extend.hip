@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
                 for (int c = 0; c < VC; ++c)
                     #pragma unroll
                     for (int r = 0; r < 16; r += 4)
-                        *(f32x4_t*)((float*)a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                        *(u32x2_t*)((__bf16*)a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) = u32x2_t{0u, 0u};
                 if (hh == 0) a.ws_lse[pi] = -INFINITY;
             }
             return;
@@ -646,15 +646,16 @@ __global__ __launch_bounds__(64 * EXT_WAVES) __attribute__((amdgpu_waves_per_eu(
     if (!col_ok) return;
     const float inv = a.v_scale / ltot;  // v_scale: fp8 V dequantisation (1 otherwise)
     if (C > 1) {
-        // a chunk's partial: normalised fp32 output and natural-log lse,
-        // slot (row, head, chunk), for the split merge
+        // a chunk's partial: normalised output row (bf16; the merge weighs
+        // the chunks in fp32) and natural-log lse, slot (row, head, chunk)
         const int64_t pi = ((int64_t)(q0 + ctok) * a.Hq + head) * C + chunk;
+        __bf16* const prow = (__bf16*)a.ws_o + pi * DV;
         #pragma unroll
         for (int c = 0; c < VC; ++c)
             #pragma unroll
             for (int r = 0; r < 16; r += 4)
-                *(f32x4_t*)((float*)a.ws_o + pi * DV + 32 * c + acc_row(r, hh)) =
-                    f32x4_t{O[c][r] * inv, O[c][r + 1] * inv, O[c][r + 2] * inv, O[c][r + 3] * inv};
+                *(u32x2_t*)(prow + 32 * c + acc_row(r, hh)) =
+                    u32x2_t{pack_bf16(O[c][r] * inv, O[c][r + 1] * inv), pack_bf16(O[c][r + 2] * inv, O[c][r + 3] * inv)};
         if (hh == 0) a.ws_lse[pi] = (m2 + __builtin_amdgcn_logf(ltot)) * LN2;
         return;
     }
@@ -736,13 +737,15 @@ int extend_max_group(pka_dtype q, int /*page_size*/) {
 
 namespace {
 // Merge of a key-range split: each (query row, head) of the batch has C
-// partials (normalised output, natural-log lse; a chunk with no key leaves
-// lse -inf); out = sum_c e^(lse_c - M) o_c / sum_c e^(lse_c - M), lse = M +
-// ln(sum_c e^(lse_c - M)).  One wave per (row, head), lanes over the value
-// dims; chunk 0 always holds keys, so M is finite.
+// partials (normalised bf16 output row, natural-log lse; a chunk with no key
+// leaves lse -inf and a zero row); out = sum_c e^(lse_c - M) o_c / sum_c
+// e^(lse_c - M), lse = M + ln(sum_c e^(lse_c - M)), in fp32.  One wave per
+// (row, head); lane l holds the EPL consecutive value dims from EPL * l (one
+// access per row); chunk 0 always holds keys, so M is finite.
 template <int DV>
 __global__ __launch_bounds__(256) void extend_split_merge_kernel(AttnArgs a) {
     constexpr int EPL = DV / 64;
+    static_assert(EPL == 1 || EPL == 2, "value rows of 64 or 128 dims");
     const int lane = threadIdx.x & 63;
     const int64_t pair = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int32_t rows = min(a.qo_indptr[a.B], a.N);  // the batch's query rows
@@ -751,10 +754,16 @@ __global__ __launch_bounds__(256) void extend_split_merge_kernel(AttnArgs a) {
     const float lv = lane < C ? a.ws_lse[pair * C + lane] : -INFINITY;
     float v[EXT_MAX_SPLIT][EPL];
     #pragma unroll
-    for (int c = 0; c < EXT_MAX_SPLIT; ++c)
-        #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-            v[c][e] = c < C ? ((const float*)a.ws_o)[(pair * C + c) * DV + e * 64 + lane] : 0.f;
+    for (int c = 0; c < EXT_MAX_SPLIT; ++c) {
+        const __bf16* prow = (const __bf16*)a.ws_o + (pair * C + min(c, C - 1)) * DV;
+        if constexpr (EPL == 2) {
+            const uint32_t w = ((const uint32_t*)prow)[lane];
+            v[c][0] = __uint_as_float(w << 16);
+            v[c][1] = __uint_as_float(w & 0xffff0000u);
+        } else {
+            v[c][0] = __uint_as_float((uint32_t)((const uint16_t*)prow)[lane] << 16);
+        }
+    }
     float M = lv;
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -771,8 +780,10 @@ __global__ __launch_bounds__(256) void extend_split_merge_kernel(AttnArgs a) {
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
     const float inv = 1.0f / den;
-    #pragma unroll
-    for (int e = 0; e < EPL; ++e) ((__bf16*)a.out)[pair * DV + e * 64 + lane] = (__bf16)(acc[e] * inv);
+    if constexpr (EPL == 2)
+        ((uint32_t*)((__bf16*)a.out + pair * DV))[lane] = pack_bf16(acc[0] * inv, acc[1] * inv);
+    else
+        ((__bf16*)a.out)[pair * DV + lane] = (__bf16)(acc[0] * inv);
     if (a.lse && lane == 0) a.lse[pair] = M + logf(den);
 }
 

@@ -158,7 +158,7 @@ struct AttnArgs {
     float* lse;
     // decode split partials [(B + nwg) * qslots, Hq, value width] in the
     // output's type (bf16 rows with bf16 queries, fp32 with fp32); extend
-    // key-range partials [N, Hq, chunks, value width] fp32
+    // key-range partials [N, Hq, chunks, value width] bf16
     void* ws_o;
     float* ws_lse;  // their log-sum-exps (natural log), one per row
     const int32_t* kv_indptr;

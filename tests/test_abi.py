@@ -244,14 +244,14 @@ def test_noalloc_refuses_before_any_launch():
 
 
 def test_extend_workspace_covers_the_key_range_split():
-    """pka_batch_sizes reports the extend split's partials (fp32 row + lse per
+    """pka_batch_sizes reports the extend split's partials (bf16 row + fp32 lse per
     query row, head and chunk) for batches of at most 16 rows per request on
     average, and none for longer extend batches; describe names the split."""
     ctx = pka.Context(32, 8, 128, 16, 1000)
     # chunks: about 1024 workgroups over the batch's items (one per request
     # and KV head), 3 .. 8, else none
     for batch, n, chunks in [(64, 256, 1), (42, 168, 3), (32, 128, 4), (12, 60, 8), (1, 4, 8), (100, 400, 1)]:
-        need = n * 32 * chunks * (128 + 1) * 4 if chunks > 1 else 0
+        need = n * 32 * chunks * (128 * 2 + 4) if chunks > 1 else 0
         assert ctx.sizes("extend", batch, n, 9000).workspace_bytes == need, (batch, n)
         assert ctx.sizes("target_verify", batch, n, 9000).workspace_bytes >= need
         assert ("%d chunks per item" % chunks in ctx.describe("target_verify", batch, n)) == (chunks > 1)

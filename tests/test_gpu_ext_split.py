@@ -110,7 +110,7 @@ def test_split_edges():
 
 def test_split_and_unsplit_agree():
     """The same batch with and without the split: the same attention, up to
-    rounding (the chunks' partials are merged in fp32)."""
+    rounding (the chunks' bf16 partial rows are merged in fp32)."""
     prob, layout, values = _problem(BASE.replace(seed=311), "target_verify")
     prob.attention_step(save=True, spec_mode="prefill")
     torch.cuda.synchronize()
