@@ -165,10 +165,13 @@ typedef __attribute__((address_space(3))) const u32x4_t lds_u32x4_t;
 // Direct HBM -> LDS load of 16 bytes per lane: lane i's bytes land at
 // lds_dst + 16 * i (lds_dst is wave-uniform; the compiler moves it to M0).
 // The load counts in vmcnt like any other; the kernel still waits for it
-// with an explicit vmcnt(0) before the data is read.
+// with an explicit vmcnt(0) before the data is read.  STREAM: the
+// non-temporal policy, for cache rows that are read once per call.
+template <bool STREAM = false>
 __device__ inline void lds_dma16(const void* src, const uint8_t* lds_dst) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)lds_dst, 16, 0,
+                                     STREAM ? 2 /* nt */ : 0);
 }
 
 // V of one 32-token tile in registers: k-slot q of lane group j holds tile
@@ -181,7 +184,8 @@ struct VTile {
 
 // The loads of one tile.  `slot` is the pool slot of tile token (lane & 31);
 // lanes exchange slots with cross-lane moves.  The cache is read once per
-// call, so the V loads carry the non-temporal hint.
+// call, so the K direct loads and the V loads carry the non-temporal policy
+// (the split partials, written between the reads, then stay cached).
 //
 // K goes to the wave's LDS tile `kst`: a wave instruction moves 1 KB of the
 // tile, lane i the 16-byte chunk f = 64 q + i of the tile's rows laid end to
@@ -201,7 +205,7 @@ __device__ inline void load_k(uint8_t* kst, int32_t slot, const uint8_t* kbase, 
     for (int q = 0; q < S::KDMA; ++q) {
         const int f = 64 * q + lane;
         const int row = f / S::KCPR, pc = f % S::KCPR;
-        lds_dma16(kbase + ks[q] * krow + 16 * S::kswz(row, pc), kst + 1024 * q);
+        lds_dma16<true>(kbase + ks[q] * krow + 16 * S::kswz(row, pc), kst + 1024 * q);
     }
 }
 template <int DK, int DV, bool FP8>
