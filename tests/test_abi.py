@@ -179,6 +179,23 @@ def test_forward_with_metadata_refuses_before_any_launch():
     assert b"extend_lens" in lib.pka_last_error() or lib.pka_last_error()
 
 
+def test_decode_workspace_holds_partials_in_the_output_type():
+    """Decode partial rows are stored in the output's type with an fp32 lse:
+    Dv bf16 values + 4 bytes per (request or share, head) for bf16 queries
+    (bf16 or fp8 cache), Dv fp32 values + 4 bytes for fp32.  Without a device
+    the partition is sized for the most shares the library allows (2048)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("sizes depend on the visible device's share count")
+    rows = lambda batch: (batch + 2048) * 32
+    assert pka.Context(32, 8, 128, 16, 100).sizes("decode", 8, 8, 80).workspace_bytes == rows(8) * (128 * 2 + 4)
+    assert pka.Context(32, 8, 128, 16, 100, "bf16", "fp8").sizes(
+        "decode", 8, 8, 80).workspace_bytes == rows(8) * (128 * 2 + 4)
+    assert pka.Context(32, 8, 128, 16, 100, "f32", "f32").sizes(
+        "decode", 8, 8, 80).workspace_bytes == rows(8) * (128 * 4 + 4)
+    assert pka.Context(32, 8, 64, 16, 100).sizes("decode", 5, 5, 80).workspace_bytes == rows(5) * (64 * 2 + 4)
+
+
 def test_verify_workspace_follows_max_q_per_request():
     """The decode path's partial rows per request: min(16, max_q_per_request,
     num_q_tokens) for verify batches (0 means 16), one for decode batches."""
