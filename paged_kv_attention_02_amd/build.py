@@ -30,8 +30,16 @@ HIPCC_FLAGS = [
 ]
 
 
+# Sources compiled on their own with extra flags, then linked in: the extend
+# kernels for 192-wide keys take the max-ILP scheduling strategy (faster at
+# those widths, slower for others, so not for the whole library).
+EXTRA_FLAGS = {
+    "extend_dk192.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    return sorted(f for f in glob.glob(os.path.join(CSRC, "*.hip")) if os.path.basename(f) not in EXTRA_FLAGS)
 
 
 def hipcc() -> str:
@@ -43,15 +51,31 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile every HIP source into libpka.so (always recompiles)."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", tmp]
+    objs = []
+    try:
+        for name, extra in EXTRA_FLAGS.items():
+            obj = "%s.%s.o" % (tmp, name)
+            flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+            _run([hipcc(), *flags, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, name), "-o", obj],
+                 verbose)
+            objs.append(obj)
+        # objects first: the driver marks every source after them as HIP
+        _run([hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *objs, *sources(), "-o", tmp], verbose)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libpka.so")
-    os.replace(tmp, LIB)
-    return LIB
 
 
 if __name__ == "__main__":
