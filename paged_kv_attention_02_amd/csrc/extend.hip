@@ -814,15 +814,17 @@ void launch_ext_d(const AttnArgs& a, bool pos, bool big, bool wide, bool f8, dim
 }
 }  // namespace
 
-// The MFMA kernels for 192-wide keys and 128-wide values are instantiated in
-// a translation unit of their own (extend_dk192.hip, which includes this
-// file), so that the build can compile them with the compiler's max-ILP
-// scheduling strategy: +1-6% at these widths, where the kernel is short of
-// registers, while the same strategy costs the fp8 variants at 128/128 2-4%.
-void launch_extend_dk192(const AttnArgs& a, bool pos, bool big, bool wide, bool f8, dim3 grid, hipStream_t s);
+// The MFMA kernels for 192-wide keys and 128-wide values over a bf16 cache
+// are instantiated in a translation unit of their own (extend_dk192.hip,
+// which includes this file), so that the build can compile them with the
+// compiler's max-ILP scheduling strategy: +1-5% at page size 128 and 13-15%
+// at page size 16, where the kernel is short of registers, while the same
+// strategy costs the fp8 variants 1-4% (so those stay here).
+void launch_extend_dk192(const AttnArgs& a, bool pos, bool big, bool wide, dim3 grid, hipStream_t s);
 #ifdef PKA_EXTEND_DK192_TU
-void launch_extend_dk192(const AttnArgs& a, bool pos, bool big, bool wide, bool f8, dim3 grid, hipStream_t s) {
-    launch_ext_d<192, 128>(a, pos, big, wide, f8, grid, s);
+void launch_extend_dk192(const AttnArgs& a, bool pos, bool big, bool wide, dim3 grid, hipStream_t s) {
+    if (pos) launch_ext_p<192, 128, true, false>(a, big, wide, grid, s);
+    else launch_ext_p<192, 128, false, false>(a, big, wide, grid, s);
 }
 #else
 hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnArgs& a, hipStream_t s) {
@@ -851,7 +853,12 @@ hipError_t launch_extend(pka_dtype q, pka_dtype kv, int DK, int DV, const AttnAr
     const bool f8 = kv == PKA_FP8_E4M3FN;
     if (DK == 128 && DV == 128) launch_ext_d<128, 128>(a, pos, big, wide, f8, grid, s);
     else if (DK == 64 && DV == 64) launch_ext_d<64, 64>(a, pos, big, wide, f8, grid, s);
-    else if (DK == 192 && DV == 128) launch_extend_dk192(a, pos, big, wide, f8, grid, s);
+    else if (DK == 192 && DV == 128 && f8) {
+        if (pos) launch_ext_p<192, 128, true, true>(a, big, wide, grid, s);
+        else launch_ext_p<192, 128, false, true>(a, big, wide, grid, s);
+    } else if (DK == 192 && DV == 128) {
+        launch_extend_dk192(a, pos, big, wide, grid, s);
+    }
     else return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || C == 1) return e;
